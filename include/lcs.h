@@ -1,0 +1,203 @@
+/*
+ * lcs.h - C ABI of the verify / select / sparse-draft attention path of
+ * verification-guided self-speculative decoding, for AMD MI355X (gfx950).
+ *
+ * The three calls follow the problem as the pages state it:
+ *  - Vegas page ("The pith", "Core claim", Figure 6 caption "Collect-2-Query"):
+ *    verification computes full attention for the k+1 verifier tokens over the
+ *    whole KV cache and exposes the pre-softmax logits of two rows, the first
+ *    draft token and the bonus token;  -> lcs_verify_attn
+ *  - the same pages, plus the Sparse Glimpse page ("Core claim": sink, recent
+ *    and top-ranked historical tokens per head) and the SSV page (NSA block
+ *    selection, "What carries the argument"): the two rows are summed over
+ *    heads and the top-k prefix positions (or blocks) are kept;  -> lcs_select_topk
+ *  - drafting attends only to the selected entries (Vegas "The pith"), and the
+ *    SSV page's grouped verifier rows load each shared block once
+ *    ("overlap-aware grouped-query execution", section 4.2 exact merged
+ *    schedule, per-row causal masks at absolute positions).  -> lcs_sparse_draft_attn
+ *
+ * Conventions common to every call
+ *  - Every pointer argument is DEVICE memory owned by the caller, except the
+ *    lcs_paged_kv struct itself (host memory, read during the call only).
+ *    The library never allocates or frees device memory and keeps no state
+ *    between calls beyond its loaded code objects.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  Outputs are valid once the stream has reached the call.
+ *  - All shape and argument checks run on the host before anything is
+ *    launched.  On failure the call returns a non-OK status, launches nothing
+ *    and lcs_last_error() describes the problem.  LCS_E_HIP reports a launch
+ *    failure from the HIP runtime.
+ *  - Contents of device arrays (index lists, block tables, lengths) are not
+ *    validated on the host.  Kernels skip, rather than read, any position or
+ *    page id that falls outside the cache; such entries simply do not take
+ *    part in the result.
+ *  - Calls are thread-safe as long as concurrent calls use distinct
+ *    workspaces and outputs.
+ *  - bf16 inputs, fp32 accumulation, fp32 outputs.
+ *
+ * Paged KV layout (the pages name vLLM's PagedAttention but fix no layout):
+ * K and V are separate bf16 arrays [num_pages][Hkv][page_size][d]; logical
+ * position p of sequence b lives in page block_table[b][p / page_size] at slot
+ * p % page_size.  A (page, head) run is page_size*d contiguous elements and a
+ * (token, head) row is d contiguous elements.  Query head h uses KV head
+ * h / (Hq / Hkv).
+ */
+#ifndef LCS_H
+#define LCS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LCS_OK = 0,
+  LCS_E_ARG = 1,          /* null pointer, negative size, bad enum, bad row index   */
+  LCS_E_SHAPE = 2,        /* inconsistent sizes (Hq % Hkv, cap too small, ...)       */
+  LCS_E_WORKSPACE = 3,    /* workspace smaller than the *_workspace_bytes query      */
+  LCS_E_UNSUPPORTED = 4,  /* valid but not implemented (d not 64/128, n_q > 64, ...) */
+  LCS_E_HIP = 5           /* the HIP runtime refused a launch                        */
+} lcs_status;
+
+typedef enum {
+  LCS_SET_SHARED = 0,      /* Vegas: one set per sequence, used by every KV head     */
+  LCS_SET_PER_KV_HEAD = 1, /* Sparse Glimpse: one set per (sequence, KV head)        */
+  LCS_SET_BLOCK = 2        /* SSV / NSA: block ids, one block = one page              */
+} lcs_set_mode;
+
+typedef struct {
+  const void* k;              /* device bf16 [num_pages][Hkv][page_size][d]            */
+  const void* v;              /* device bf16 [num_pages][Hkv][page_size][d]            */
+  const int32_t* block_table; /* device int32 [B][max_pages]                           */
+  int32_t num_pages;          /* >= 1; num_pages*Hkv*page_size < 2^31                  */
+  int32_t page_size;          /* power of two, 1..1024                                  */
+  int32_t max_pages;          /* row length of block_table                              */
+  int32_t Hkv;                /* KV heads, >= 1                                         */
+  int32_t d;                  /* head dim: 64 or 128                                    */
+} lcs_paged_kv;
+
+/* ---------------------------------------------------------------------------
+ * Dense verify attention with Collect-2-Query logits.
+ *
+ * Vegas page, "The pith" / "Core claim" and Figure 6: full attention for the
+ * n_q = k+1 verifier queries (draft chain plus bonus token) over the whole
+ * cache; only the pre-softmax logits of rows collect_row0 and collect_row1
+ * (the first draft token and the bonus token: 0 and n_q-1) are written.
+ *
+ *  q            bf16 [B][n_q][Hq][d].  Row i of sequence b sits at cache
+ *               position prefix_len[b] + i; the cache must already hold the
+ *               K/V of all n_q verifier tokens.
+ *  prefix_len   device int32 [B]; values above max_prefix_len are clamped.
+ *  max_prefix_len  host bound on prefix_len, sizes the launch.
+ *  tree_mask    device uint64 [B][n_q] or NULL.  NULL: row i sees verifier
+ *               slots j <= i (a chain).  Otherwise row i sees slot j iff bit j
+ *               of tree_mask[b][i] is set.  Every row sees the whole prefix.
+ *  scale        softmax scale (1/sqrt(d) in the pages' models).
+ *  out          fp32 [B][n_q][Hq][d]: softmax(scale q K^T) V.
+ *  logits       fp32 [B][Hq][2][logits_ld]: scale*q.k of the two collected rows
+ *               for columns p < prefix_len[b]; other columns are untouched.
+ *               logits_ld >= max_prefix_len.
+ *  lse          fp32 [B][n_q][Hq] natural-log sum-exp of the scaled logits, or NULL.
+ *  workspace    device scratch of at least lcs_verify_workspace_bytes(...) bytes
+ *               (no initialisation needed; contents are clobbered).
+ * Limits: n_q in [1, 64]; Hq % Hkv == 0; Hq/Hkv <= 64; d in {64, 128}.
+ * ------------------------------------------------------------------------- */
+size_t lcs_verify_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq,
+                                  const lcs_paged_kv* kv, int32_t max_prefix_len);
+
+lcs_status lcs_verify_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q,
+                           int32_t Hq, const int32_t* prefix_len, int32_t max_prefix_len,
+                           const uint64_t* tree_mask, float scale, int32_t collect_row0,
+                           int32_t collect_row1, float* out, float* logits, int64_t logits_ld,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Verification-guided top-k selection.
+ *
+ * Vegas page, "Core claim" / "What carries the argument": the two collected
+ * logit rows are combined across query heads and the top-k prefix positions
+ * are kept.  Sparse Glimpse page, "Core claim": sink + recent + top-ranked
+ * history, per head.  SSV page: hardware-aligned blocks.
+ *
+ * Score of prefix position p for a set:  sigma_p = sum over the set's query
+ * heads h, ascending, of (logits[b][h][0][p] + logits[b][h][1][p]), summed in
+ * that fixed fp32 order (acc = acc + (row0 + row1)); -0 counts as +0.
+ *   SHARED:       one set per sequence over all Hq heads.
+ *   PER_KV_HEAD:  one set per (sequence, KV head g) over heads g*G .. g*G+G-1.
+ *   BLOCK:        per (sequence, KV head) like PER_KV_HEAD; a block c of
+ *                 block_size positions scores max(sigma_p) over its p < L.
+ * Rule (L = prefix_len[b]; items are positions, or blocks in BLOCK mode):
+ *   if L items <= n_sink + top_k + n_recent: keep every item;
+ *   else keep the sink window, the recent window, and the top_k items of the
+ *   pool between them by (score descending, index ascending).
+ *   In BLOCK mode the sink window is every block holding a position < n_sink
+ *   and the recent window every block meeting [L - n_recent, L).
+ * Output: indices [B][n_sets][cap] int32, ascending; counts [B][n_sets].
+ * Entries past counts are untouched.  cap >= min(max items, window sizes + top_k).
+ * The result is bit-identical to the same rule run on the CPU over the same
+ * logits with the same fp32 summation order.
+ *
+ *  logits       fp32 [B][Hq][2][logits_ld] as written by lcs_verify_attn.
+ *  block_size   BLOCK mode only: power of two in [4, 4096]; ignored otherwise.
+ *  workspace    at least lcs_select_workspace_bytes(...) bytes, no initialisation.
+ * Limits: max_prefix_len < 2^24.
+ * ------------------------------------------------------------------------- */
+size_t lcs_select_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, lcs_set_mode mode,
+                                  int32_t max_prefix_len, int32_t block_size);
+
+lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, int32_t Hq,
+                           int32_t Hkv, const int32_t* prefix_len, int32_t max_prefix_len,
+                           lcs_set_mode mode, int32_t top_k, int32_t n_sink, int32_t n_recent,
+                           int32_t block_size, int32_t* indices, int32_t* counts, int32_t cap,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Sparse draft attention over the selected entries plus the recent tail.
+ *
+ * Vegas page, "The pith": drafting attends only to the selected prefix
+ * positions.  SSV page, section 4.2 and Figure 5/6 text: verifier rows with
+ * different block sets share block loads (merged schedule, per-row selection
+ * unchanged) and each row keeps its own causal boundary.
+ *
+ *  q            bf16 [B][n_q][Hq][d]; n_q = 1 for a single-token draft step,
+ *               several rows for grouped (tree) verification in BLOCK mode.
+ *  mode, indices, counts, cap:
+ *    SHARED       indices [B][1][cap] ascending token positions, counts [B][1]
+ *    PER_KV_HEAD  indices [B][Hkv][cap], counts [B][Hkv]
+ *    BLOCK        indices [B][n_q][Hkv][cap] ascending block ids (block = page,
+ *                 page_size % 32 == 0), counts [B][n_q][Hkv]; a block covers
+ *                 positions [c*page_size, (c+1)*page_size) below tail_begin[b].
+ *    Listed positions must be < tail_begin[b] and distinct.
+ *  tail_begin, tail_len  device int32 [B]: every row also sees the tail slots
+ *               tail_begin[b] + j, j < tail_len[b] (the tokens written since the
+ *               selection, the current one included), filtered by tail_mask.
+ *  max_tail_len host bound on tail_len, sizes the launch.
+ *  tail_mask    device uint64 [B][n_q] or NULL: row i sees tail slot j iff bit j
+ *               is set (needs tail_len <= 64); NULL = every row sees the whole tail.
+ *  out, lse     as for lcs_verify_attn.  A row that sees nothing gets out = 0
+ *               and lse = -inf.
+ * Limits: n_q in [1, 64]; d in {64, 128}.
+ * ------------------------------------------------------------------------- */
+size_t lcs_sparse_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq, const lcs_paged_kv* kv,
+                                  lcs_set_mode mode, int32_t cap, int32_t max_tail_len);
+
+lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q,
+                                 int32_t Hq, lcs_set_mode mode, const int32_t* indices,
+                                 const int32_t* counts, int32_t cap, const int32_t* tail_begin,
+                                 const int32_t* tail_len, int32_t max_tail_len,
+                                 const uint64_t* tail_mask, float scale, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* lcs_last_error(void);
+
+/* Library version string ("lcs <major>.<minor> gfx950"). */
+const char* lcs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCS_H */

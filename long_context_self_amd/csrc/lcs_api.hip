@@ -1,0 +1,261 @@
+// Host side of the C ABI declared in include/lcs.h: argument validation, workspace
+// sizing and kernel launch.  Every check runs before anything touches the device,
+// so an invalid call returns a status without a launch (and without a GPU).
+#include "../../include/lcs.h"
+#include "lcs_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lcs_status fail(lcs_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool is_pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+lcs_status check_kv(const lcs_paged_kv* kv) {
+  if (kv == nullptr) return fail(LCS_E_ARG, "kv is NULL");
+  if (kv->k == nullptr || kv->v == nullptr || kv->block_table == nullptr)
+    return fail(LCS_E_ARG, "kv->k, kv->v and kv->block_table must be non-NULL");
+  if (kv->d != 64 && kv->d != 128) return fail(LCS_E_UNSUPPORTED, "head dim %d not in {64, 128}", kv->d);
+  if (!is_pow2(kv->page_size) || kv->page_size > 1024)
+    return fail(LCS_E_UNSUPPORTED, "page_size %d is not a power of two in [1, 1024]", kv->page_size);
+  if (kv->num_pages < 1 || kv->max_pages < 1 || kv->Hkv < 1)
+    return fail(LCS_E_SHAPE, "num_pages (%d), max_pages (%d) and Hkv (%d) must be >= 1",
+                kv->num_pages, kv->max_pages, kv->Hkv);
+  if ((long long)kv->num_pages * kv->Hkv * kv->page_size >= (1ll << 31))
+    return fail(LCS_E_UNSUPPORTED, "num_pages*Hkv*page_size must stay below 2^31 rows");
+  if (!aligned(kv->k, 16) || !aligned(kv->v, 16)) return fail(LCS_E_ARG, "kv->k and kv->v must be 16-byte aligned");
+  return LCS_OK;
+}
+
+lcs_status check_heads(int32_t Hq, int32_t Hkv) {
+  if (Hq < 1) return fail(LCS_E_SHAPE, "Hq must be >= 1");
+  if (Hq % Hkv != 0) return fail(LCS_E_SHAPE, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
+  return LCS_OK;
+}
+
+lcs_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return LCS_OK;
+  return fail(LCS_E_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lcs_last_error(void) { return g_err; }
+
+const char* lcs_version(void) { return "lcs 0.1 gfx950"; }
+
+size_t lcs_verify_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq, const lcs_paged_kv* kv,
+                                  int32_t max_prefix_len) {
+  if (kv == nullptr || kv->Hkv < 1 || Hq < 1 || n_q < 1 || B < 0 || max_prefix_len < 0) return 0;
+  if (Hq % kv->Hkv != 0 || (kv->d != 64 && kv->d != 128)) return 0;
+  return lcs::attn_plan(lcs::MODE_DENSE, B, n_q, Hq, kv->Hkv, kv->d, kv->page_size, max_prefix_len, 0, 0)
+      .total_bytes;
+}
+
+lcs_status lcs_verify_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q, int32_t Hq,
+                           const int32_t* prefix_len, int32_t max_prefix_len, const uint64_t* tree_mask,
+                           float scale, int32_t collect_row0, int32_t collect_row1, float* out,
+                           float* logits, int64_t logits_ld, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  lcs_status st = check_kv(kv);
+  if (st != LCS_OK) return st;
+  if ((st = check_heads(Hq, kv->Hkv)) != LCS_OK) return st;
+  if (B < 0) return fail(LCS_E_SHAPE, "B must be >= 0");
+  if (n_q < 1) return fail(LCS_E_SHAPE, "n_q must be >= 1");
+  if (n_q > 64) return fail(LCS_E_UNSUPPORTED, "n_q %d > 64 verifier rows", n_q);
+  if (max_prefix_len < 0) return fail(LCS_E_SHAPE, "max_prefix_len must be >= 0");
+  if (collect_row0 < 0 || collect_row0 >= n_q || collect_row1 < 0 || collect_row1 >= n_q)
+    return fail(LCS_E_ARG, "collect rows (%d, %d) outside [0, %d)", collect_row0, collect_row1, n_q);
+  if (B == 0) return LCS_OK;   // empty batch: nothing is read or written, pointers may be NULL
+  if (q == nullptr || prefix_len == nullptr || out == nullptr)
+    return fail(LCS_E_ARG, "q, prefix_len and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(LCS_E_ARG, "q and out must be 16-byte aligned");
+  if (!isfinite(scale)) return fail(LCS_E_ARG, "scale must be finite");
+  if (logits != nullptr && logits_ld < max_prefix_len)
+    return fail(LCS_E_SHAPE, "logits_ld %lld < max_prefix_len %d", (long long)logits_ld, max_prefix_len);
+  if ((long long)max_prefix_len + n_q > (long long)kv->max_pages * kv->page_size)
+    return fail(LCS_E_SHAPE, "max_prefix_len + n_q exceeds max_pages * page_size");
+  const lcs::AttnPlan plan = lcs::attn_plan(lcs::MODE_DENSE, B, n_q, Hq, kv->Hkv, kv->d, kv->page_size,
+                                            max_prefix_len, 0, 0);
+  if (workspace_bytes < plan.total_bytes || (plan.part_bytes > 0 && workspace == nullptr))
+    return fail(LCS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, plan.total_bytes);
+  lcs::AttnArgs a{};
+  a.k = static_cast<const uint16_t*>(kv->k);
+  a.v = static_cast<const uint16_t*>(kv->v);
+  a.bt = kv->block_table;
+  a.num_pages = kv->num_pages;
+  a.lg_page = ilog2(kv->page_size);
+  a.max_pages = kv->max_pages;
+  a.Hkv = kv->Hkv;
+  a.q = static_cast<const uint16_t*>(q);
+  a.B = B;
+  a.n_q = n_q;
+  a.Hq = Hq;
+  a.G = Hq / kv->Hkv;
+  a.mode = lcs::MODE_DENSE;
+  a.prefix_len = prefix_len;
+  a.max_prefix_len = max_prefix_len;
+  a.rowmask = tree_mask;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.c0 = collect_row0;
+  a.c1 = collect_row1;
+  a.logits = logits;
+  a.logits_ld = logits_ld;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(lcs::attn_launch(plan, a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t lcs_select_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, lcs_set_mode mode,
+                                  int32_t max_prefix_len, int32_t block_size) {
+  if (B < 0 || Hkv < 1 || Hq < 1 || max_prefix_len < 0) return 0;
+  if (mode == LCS_SET_BLOCK && (!is_pow2(block_size) || block_size < 4 || block_size > 4096)) return 0;
+  return lcs::select_plan(B, Hq, Hkv, (int32_t)mode, max_prefix_len, block_size).total_bytes;
+}
+
+lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, int32_t Hq, int32_t Hkv,
+                           const int32_t* prefix_len, int32_t max_prefix_len, lcs_set_mode mode,
+                           int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t block_size,
+                           int32_t* indices, int32_t* counts, int32_t cap, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (Hkv < 1) return fail(LCS_E_SHAPE, "Hkv must be >= 1");
+  lcs_status st = check_heads(Hq, Hkv);
+  if (st != LCS_OK) return st;
+  if (mode != LCS_SET_SHARED && mode != LCS_SET_PER_KV_HEAD && mode != LCS_SET_BLOCK)
+    return fail(LCS_E_ARG, "unknown set mode %d", (int)mode);
+  if (B < 0) return fail(LCS_E_SHAPE, "B must be >= 0");
+  if (B == 0) return LCS_OK;   // empty batch: nothing is read or written, pointers may be NULL
+  if (logits == nullptr || prefix_len == nullptr || indices == nullptr || counts == nullptr)
+    return fail(LCS_E_ARG, "logits, prefix_len, indices and counts must be non-NULL");
+  if (top_k < 0 || n_sink < 0 || n_recent < 0) return fail(LCS_E_ARG, "top_k, n_sink, n_recent must be >= 0");
+  if (max_prefix_len < 0) return fail(LCS_E_SHAPE, "max_prefix_len must be >= 0");
+  if (max_prefix_len >= (1 << 24)) return fail(LCS_E_UNSUPPORTED, "max_prefix_len must be < 2^24");
+  if (logits_ld < max_prefix_len) return fail(LCS_E_SHAPE, "logits_ld %lld < max_prefix_len %d",
+                                              (long long)logits_ld, max_prefix_len);
+  long long items = max_prefix_len, need;
+  if (mode == LCS_SET_BLOCK) {
+    if (!is_pow2(block_size) || block_size < 4 || block_size > 4096)
+      return fail(LCS_E_UNSUPPORTED, "block_size %d is not a power of two in [4, 4096]", block_size);
+    items = (max_prefix_len + block_size - 1) / block_size;
+    need = (n_sink + block_size - 1) / block_size + (long long)top_k + (n_recent + block_size - 1) / block_size + 1;
+  } else {
+    need = (long long)n_sink + top_k + n_recent;
+  }
+  if (need > items) need = items;
+  if (cap < need) return fail(LCS_E_SHAPE, "cap %d < %lld entries the selection can produce", cap, need);
+  const lcs::SelPlan plan = lcs::select_plan(B, Hq, Hkv, (int32_t)mode, max_prefix_len, block_size);
+  if (workspace == nullptr || workspace_bytes < plan.total_bytes)
+    return fail(LCS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, plan.total_bytes);
+  lcs::SelArgs a{};
+  a.logits = logits;
+  a.ld = logits_ld;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.mode = (int32_t)mode;
+  a.prefix_len = prefix_len;
+  a.max_len = max_prefix_len;
+  a.top_k = top_k;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.lg_bs = (mode == LCS_SET_BLOCK) ? ilog2(block_size) : 0;
+  a.vec4 = (aligned(logits, 16) && logits_ld % 4 == 0) ? 1 : 0;
+  a.indices = indices;
+  a.counts = counts;
+  a.cap = cap;
+  return hip_status(lcs::select_launch(plan, a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t lcs_sparse_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq, const lcs_paged_kv* kv,
+                                  lcs_set_mode mode, int32_t cap, int32_t max_tail_len) {
+  if (kv == nullptr || kv->Hkv < 1 || Hq < 1 || n_q < 1 || B < 0 || cap < 0 || max_tail_len < 0) return 0;
+  if (Hq % kv->Hkv != 0 || (kv->d != 64 && kv->d != 128)) return 0;
+  const int32_t m = (mode == LCS_SET_BLOCK) ? lcs::MODE_BLOCK
+                    : (mode == LCS_SET_SHARED) ? lcs::MODE_LIST_SHARED : lcs::MODE_LIST_PER_HEAD;
+  return lcs::attn_plan(m, B, n_q, Hq, kv->Hkv, kv->d, kv->page_size, 0, cap, max_tail_len).total_bytes;
+}
+
+lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q, int32_t Hq,
+                                 lcs_set_mode mode, const int32_t* indices, const int32_t* counts,
+                                 int32_t cap, const int32_t* tail_begin, const int32_t* tail_len,
+                                 int32_t max_tail_len, const uint64_t* tail_mask, float scale, float* out,
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  lcs_status st = check_kv(kv);
+  if (st != LCS_OK) return st;
+  if ((st = check_heads(Hq, kv->Hkv)) != LCS_OK) return st;
+  if (mode != LCS_SET_SHARED && mode != LCS_SET_PER_KV_HEAD && mode != LCS_SET_BLOCK)
+    return fail(LCS_E_ARG, "unknown set mode %d", (int)mode);
+  if (B < 0) return fail(LCS_E_SHAPE, "B must be >= 0");
+  if (n_q < 1) return fail(LCS_E_SHAPE, "n_q must be >= 1");
+  if (n_q > 64) return fail(LCS_E_UNSUPPORTED, "n_q %d > 64 rows", n_q);
+  if (cap < 0 || max_tail_len < 0) return fail(LCS_E_SHAPE, "cap and max_tail_len must be >= 0");
+  if (B == 0) return LCS_OK;   // empty batch: nothing is read or written, pointers may be NULL
+  if (q == nullptr || out == nullptr || tail_begin == nullptr || tail_len == nullptr)
+    return fail(LCS_E_ARG, "q, out, tail_begin and tail_len must be non-NULL");
+  if (cap > 0 && (indices == nullptr || counts == nullptr))
+    return fail(LCS_E_ARG, "indices and counts must be non-NULL when cap > 0");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(LCS_E_ARG, "q and out must be 16-byte aligned");
+  if (!isfinite(scale)) return fail(LCS_E_ARG, "scale must be finite");
+  if (tail_mask != nullptr && max_tail_len > 64)
+    return fail(LCS_E_UNSUPPORTED, "a tail mask covers at most 64 tail slots (max_tail_len %d)", max_tail_len);
+  if (mode == LCS_SET_BLOCK && kv->page_size % lcs::kStepTokens != 0)
+    return fail(LCS_E_UNSUPPORTED, "block mode needs page_size %% %d == 0 (page_size %d)", lcs::kStepTokens,
+                kv->page_size);
+  const int32_t m = (mode == LCS_SET_BLOCK) ? lcs::MODE_BLOCK
+                    : (mode == LCS_SET_SHARED) ? lcs::MODE_LIST_SHARED : lcs::MODE_LIST_PER_HEAD;
+  const lcs::AttnPlan plan = lcs::attn_plan(m, B, n_q, Hq, kv->Hkv, kv->d, kv->page_size, 0, cap, max_tail_len);
+  if (workspace_bytes < plan.total_bytes ||
+      ((plan.part_bytes > 0 || m == lcs::MODE_BLOCK) && workspace == nullptr))
+    return fail(LCS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, plan.total_bytes);
+  lcs::AttnArgs a{};
+  a.k = static_cast<const uint16_t*>(kv->k);
+  a.v = static_cast<const uint16_t*>(kv->v);
+  a.bt = kv->block_table;
+  a.num_pages = kv->num_pages;
+  a.lg_page = ilog2(kv->page_size);
+  a.max_pages = kv->max_pages;
+  a.Hkv = kv->Hkv;
+  a.q = static_cast<const uint16_t*>(q);
+  a.B = B;
+  a.n_q = n_q;
+  a.Hq = Hq;
+  a.G = Hq / kv->Hkv;
+  a.mode = m;
+  a.rowmask = tail_mask;
+  a.indices = indices;
+  a.counts = counts;
+  a.cap = cap;
+  a.tail_begin = tail_begin;
+  a.tail_len = tail_len;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.c0 = a.c1 = -1;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(lcs::attn_launch(plan, a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Internal declarations shared by the host API and the kernel translation units.
+// Nothing here is part of the public ABI (include/lcs.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lcs {
+
+// ---------------------------------------------------------------------------
+// Attention (verify, sparse token lists, sparse block lists)
+// ---------------------------------------------------------------------------
+enum AttnMode : int32_t {
+  MODE_DENSE = 0,          // verify: every cache position [0, L + n_q)
+  MODE_LIST_SHARED = 1,    // sparse: one token list per sequence
+  MODE_LIST_PER_HEAD = 2,  // sparse: one token list per (sequence, KV head)
+  MODE_BLOCK = 3           // sparse: per-row block lists, merged into a union
+};
+
+constexpr int kStepTokens = 32;   // tokens consumed per inner step of a wave
+constexpr int kWaves = 4;         // waves per workgroup (one token stream each)
+constexpr int kMaxRowsPerWG = 64; // q-rows (n_q * G) handled by one workgroup
+constexpr int kMaxSplits = 128;   // split-K partials per (sequence, KV head, row chunk)
+constexpr int kTargetWGs = 1024;  // launch size the split policy aims for
+
+struct AttnArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* bt;
+  int32_t num_pages, lg_page, max_pages, Hkv;
+  const uint16_t* q;
+  int32_t B, n_q, Hq, G, rows, n_rc;
+  int32_t mode;
+  // dense verify
+  const int32_t* prefix_len;
+  int32_t max_prefix_len;
+  // dense: tree mask; sparse: tail mask.  [B][n_q] or null
+  const uint64_t* rowmask;
+  // sparse lists
+  const int32_t* indices;
+  const int32_t* counts;
+  int32_t cap;
+  const int32_t* tail_begin;
+  const int32_t* tail_len;
+  // block-union plan (workspace)
+  const int32_t* ublk;
+  const uint64_t* umask;
+  const int32_t* ucount;
+  int32_t ucap;
+  float scale, scale_log2;
+  // Collect-2-Query (dense only)
+  int32_t c0, c1;
+  float* logits;
+  int64_t logits_ld;
+  // split-K
+  float* part;
+  int32_t n_split, sps;
+  // final outputs
+  float* out;
+  float* lse;
+};
+
+struct AttnPlan {
+  int32_t D, QT, rows, n_rc, n_split, sps, T_max;
+  size_t part_bytes, ublk_bytes, umask_bytes, ucount_bytes, total_bytes;
+};
+
+// Split policy and workspace layout; identical on every call with the same sizes.
+AttnPlan attn_plan(int32_t mode, int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d,
+                   int32_t page_size, int32_t max_prefix_len, int32_t cap, int32_t max_tail_len);
+
+// Launch the attention kernels on `stream`.  Returns hipSuccess or the launch error.
+hipError_t attn_launch(const AttnPlan& plan, AttnArgs args, void* workspace, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Selection
+// ---------------------------------------------------------------------------
+enum SelMode : int32_t { LCS_SEL_SHARED = 0, LCS_SEL_PER_HEAD = 1, LCS_SEL_BLOCK = 2 };
+
+constexpr int kSelChunk = 4096;   // items per workgroup in the streaming passes
+constexpr int kHistBins = 4096;   // first radix digit: top 12 bits of the key
+
+struct SelArgs {
+  const float* logits;
+  int64_t ld;
+  int32_t B, Hq, Hkv, G, n_sets, mode;
+  const int32_t* prefix_len;
+  int32_t max_len;
+  int32_t top_k, n_sink, n_recent, lg_bs, vec4;
+  int32_t* indices;
+  int32_t* counts;
+  int32_t cap;
+  // workspace
+  uint32_t* keys;        // [NS][item_cap]
+  uint32_t* hist;        // [NS][kHistBins]
+  uint32_t* cand_count;  // [NS]
+  uint64_t* cand;        // [NS][item_cap]
+  uint32_t* chunk_above; // [NS][n_chunks]
+  uint32_t* chunk_off;   // [NS][n_chunks]
+  uint64_t* thr;         // [NS][2]
+  int32_t item_cap, n_chunks, n_pos_chunks;
+};
+
+struct SelPlan {
+  int32_t n_sets, item_cap, n_chunks, n_pos_chunks;
+  size_t keys_bytes, hist_bytes, cc_bytes, cand_bytes, ca_bytes, co_bytes, thr_bytes, total_bytes;
+};
+
+SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t max_len,
+                    int32_t block_size);
+
+hipError_t select_launch(const SelPlan& plan, SelArgs args, void* workspace, hipStream_t stream);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace lcs

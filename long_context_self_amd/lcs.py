@@ -1,0 +1,207 @@
+"""Thin Python binding of liblcs.so (include/lcs.h): argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; this module only
+turns torch tensors into device pointers, sizes workspaces and raises on a
+non-OK status.  PyTorch supplies device memory and the current stream.
+
+The library must have been built (``python -m long_context_self_amd._build``
+or ``__graft_entry__.build()``); loading fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+import torch
+
+from ._build import lib_path
+
+LCS_OK, LCS_E_ARG, LCS_E_SHAPE, LCS_E_WORKSPACE, LCS_E_UNSUPPORTED, LCS_E_HIP = range(6)
+SET_MODES = {"shared": 0, "per_kv_head": 1, "block": 2}
+
+STATUS_NAMES = {0: "LCS_OK", 1: "LCS_E_ARG", 2: "LCS_E_SHAPE", 3: "LCS_E_WORKSPACE",
+                4: "LCS_E_UNSUPPORTED", 5: "LCS_E_HIP"}
+
+
+class LcsError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class PagedKVDesc(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32)]
+
+
+_i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_KV = ctypes.POINTER(PagedKVDesc)
+
+SIGNATURES = {
+    "lcs_verify_workspace_bytes": (_sz, [_i32, _i32, _i32, _KV, _i32]),
+    "lcs_verify_attn": (_i32, [_KV, _p, _i32, _i32, _i32, _p, _i32, _p, _f, _i32, _i32, _p, _p, _i64,
+                              _p, _p, _sz, _p]),
+    "lcs_select_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "lcs_select_topk": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                              _p, _p, _i32, _p, _sz, _p]),
+    "lcs_sparse_workspace_bytes": (_sz, [_i32, _i32, _i32, _KV, _i32, _i32, _i32]),
+    "lcs_sparse_draft_attn": (_i32, [_KV, _p, _i32, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _i32, _p,
+                                    _f, _p, _p, _p, _sz, _p]),
+    "lcs_last_error": (ctypes.c_char_p, []),
+    "lcs_version": (ctypes.c_char_p, []),
+}
+
+_LIB = None
+
+
+def load() -> ctypes.CDLL:
+    """Load liblcs.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                               "or python -m long_context_self_amd._build")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def _check(status: int) -> None:
+    if status != LCS_OK:
+        raise LcsError(status, load().lcs_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to liblcs must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclasses.dataclass
+class PagedKV:
+    """Device-side paged cache: k, v bf16 [num_pages][Hkv][page_size][d]; block_table int32 [B][max_pages]."""
+    k: torch.Tensor
+    v: torch.Tensor
+    block_table: torch.Tensor
+
+    def desc(self) -> PagedKVDesc:
+        n, hkv, ps, d = self.k.shape
+        return PagedKVDesc(_ptr(self.k), _ptr(self.v), _ptr(self.block_table), n, ps,
+                           self.block_table.shape[1], hkv, d)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None and ws.numel() >= nbytes:
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def verify_workspace_bytes(kv: PagedKV, B: int, n_q: int, Hq: int, max_prefix_len: int) -> int:
+    d = kv.desc()
+    return load().lcs_verify_workspace_bytes(B, n_q, Hq, ctypes.byref(d), max_prefix_len)
+
+
+def verify_attn(kv: PagedKV, q: torch.Tensor, prefix_len: torch.Tensor, max_prefix_len: int,
+                scale: float, collect_rows: Tuple[int, int], tree_mask: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                with_logits: bool = True):
+    """lcs_verify_attn.  q bf16 [B][n_q][Hq][d].  Returns (out, logits, lse)."""
+    B, n_q, Hq, d = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, n_q, Hq, d), dtype=torch.float32, device=dev)
+    if logits is None and with_logits:
+        logits = torch.empty((B, Hq, 2, max(max_prefix_len, 1)), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, n_q, Hq), dtype=torch.float32, device=dev)
+    desc = kv.desc()
+    need = load().lcs_verify_workspace_bytes(B, n_q, Hq, ctypes.byref(desc), max_prefix_len)
+    ws = _workspace(need, dev, workspace)
+    ld = logits.shape[-1] if logits is not None else 0
+    _check(load().lcs_verify_attn(ctypes.byref(desc), _ptr(q), B, n_q, Hq, _ptr(prefix_len),
+                                  max_prefix_len, _ptr(tree_mask), scale, collect_rows[0],
+                                  collect_rows[1], _ptr(out), _ptr(logits), ld, _ptr(lse),
+                                  ws.data_ptr(), ws.numel(), _stream()))
+    return out, logits, lse
+
+
+def select_workspace_bytes(B: int, Hq: int, Hkv: int, mode: str, max_prefix_len: int,
+                           block_size: int = 0) -> int:
+    return load().lcs_select_workspace_bytes(B, Hq, Hkv, SET_MODES[mode], max_prefix_len, block_size)
+
+
+def select_topk(logits: torch.Tensor, prefix_len: torch.Tensor, max_prefix_len: int, Hkv: int,
+                mode: str, top_k: int, n_sink: int, n_recent: int, block_size: int = 0,
+                cap: Optional[int] = None, indices: Optional[torch.Tensor] = None,
+                counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """lcs_select_topk.  logits fp32 [B][Hq][2][ld].  Returns (indices [B][n_sets][cap], counts [B][n_sets])."""
+    B, Hq = logits.shape[0], logits.shape[1]
+    dev = logits.device
+    n_sets = 1 if mode == "shared" else Hkv
+    if cap is None:
+        if mode == "block":
+            nb = -(-max_prefix_len // block_size)
+            cap = min(nb, -(-n_sink // block_size) + top_k + -(-n_recent // block_size) + 1)
+        else:
+            cap = min(max_prefix_len, n_sink + top_k + n_recent)
+        cap = max(cap, 1)
+    if indices is None:
+        indices = torch.full((B, n_sets, cap), -1, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.zeros((B, n_sets), dtype=torch.int32, device=dev)
+    need = load().lcs_select_workspace_bytes(B, Hq, Hkv, SET_MODES[mode], max_prefix_len, block_size)
+    ws = _workspace(need, dev, workspace)
+    _check(load().lcs_select_topk(_ptr(logits), logits.stride(2), B, Hq, Hkv, _ptr(prefix_len),
+                                  max_prefix_len, SET_MODES[mode], top_k, n_sink, n_recent, block_size,
+                                  _ptr(indices), _ptr(counts), cap, ws.data_ptr(), ws.numel(),
+                                  _stream()))
+    return indices, counts
+
+
+def sparse_workspace_bytes(kv: PagedKV, B: int, n_q: int, Hq: int, mode: str, cap: int,
+                           max_tail_len: int) -> int:
+    d = kv.desc()
+    return load().lcs_sparse_workspace_bytes(B, n_q, Hq, ctypes.byref(d), SET_MODES[mode], cap, max_tail_len)
+
+
+def sparse_draft_attn(kv: PagedKV, q: torch.Tensor, mode: str, indices: torch.Tensor,
+                      counts: torch.Tensor, tail_begin: torch.Tensor, tail_len: torch.Tensor,
+                      max_tail_len: int, scale: float, tail_mask: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None):
+    """lcs_sparse_draft_attn.  q bf16 [B][n_q][Hq][d].  Returns (out, lse)."""
+    B, n_q, Hq, d = q.shape
+    dev = q.device
+    cap = indices.shape[-1]
+    if out is None:
+        out = torch.empty((B, n_q, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, n_q, Hq), dtype=torch.float32, device=dev)
+    desc = kv.desc()
+    need = load().lcs_sparse_workspace_bytes(B, n_q, Hq, ctypes.byref(desc), SET_MODES[mode], cap,
+                                             max_tail_len)
+    ws = _workspace(need, dev, workspace)
+    _check(load().lcs_sparse_draft_attn(ctypes.byref(desc), _ptr(q), B, n_q, Hq, SET_MODES[mode],
+                                        _ptr(indices), _ptr(counts), cap, _ptr(tail_begin),
+                                        _ptr(tail_len), max_tail_len, _ptr(tail_mask), scale,
+                                        _ptr(out), _ptr(lse), ws.data_ptr(), ws.numel(), _stream()))
+    return out, lse
+
+
+def version() -> str:
+    return load().lcs_version().decode()

@@ -1,0 +1,126 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad calls on
+the host before touching a device (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lcs.h")
+
+
+def lib():
+    from long_context_self_amd import lcs
+    if not os.path.exists(lcs.lib_path()):
+        pytest.skip("liblcs.so not built")
+    return lcs, lcs.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lcs_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lcs, L = lib()
+    names = declared_symbols()
+    assert {"lcs_verify_attn", "lcs_select_topk", "lcs_sparse_draft_attn", "lcs_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert lcs.version().startswith("lcs ")
+
+
+def fake_kv(lcs, **kw):
+    d = dict(k=0x1000, v=0x2000, block_table=0x3000, num_pages=10, page_size=16, max_pages=4, Hkv=2, d=128)
+    d.update(kw)
+    return lcs.PagedKVDesc(**d)
+
+
+def verify(lcs, L, kv, **kw):
+    a = dict(q=0x4000, B=1, n_q=5, Hq=4, prefix_len=0x5000, max_len=40, tree=None, scale=0.1, r0=0, r1=4,
+             out=0x6000, logits=0x7000, ld=40, lse=None, ws=0x8000, wsb=1 << 20)
+    a.update(kw)
+    return L.lcs_verify_attn(ctypes.byref(kv), a["q"], a["B"], a["n_q"], a["Hq"], a["prefix_len"], a["max_len"],
+                             a["tree"], a["scale"], a["r0"], a["r1"], a["out"], a["logits"], a["ld"], a["lse"],
+                             a["ws"], a["wsb"], None)
+
+
+def test_verify_host_errors():
+    lcs, L = lib()
+    kv = fake_kv(lcs)
+    assert verify(lcs, L, fake_kv(lcs, d=96)) == lcs.LCS_E_UNSUPPORTED
+    assert b"head dim" in L.lcs_last_error()
+    assert verify(lcs, L, fake_kv(lcs, page_size=12)) == lcs.LCS_E_UNSUPPORTED
+    assert verify(lcs, L, fake_kv(lcs, k=0)) == lcs.LCS_E_ARG
+    assert verify(lcs, L, kv, Hq=3) == lcs.LCS_E_SHAPE
+    assert verify(lcs, L, kv, n_q=65) == lcs.LCS_E_UNSUPPORTED
+    assert verify(lcs, L, kv, n_q=0) == lcs.LCS_E_SHAPE
+    assert verify(lcs, L, kv, q=0) == lcs.LCS_E_ARG
+    assert verify(lcs, L, kv, q=0x4002) == lcs.LCS_E_ARG          # misaligned
+    assert verify(lcs, L, kv, r1=5) == lcs.LCS_E_ARG
+    assert verify(lcs, L, kv, ld=39) == lcs.LCS_E_SHAPE
+    assert verify(lcs, L, kv, max_len=60) == lcs.LCS_E_SHAPE       # 60 + 5 > 4 pages * 16
+    assert verify(lcs, L, kv, max_len=-1) == lcs.LCS_E_SHAPE
+    assert verify(lcs, L, kv, scale=float("inf")) == lcs.LCS_E_ARG
+    assert verify(lcs, L, kv, wsb=0) == lcs.LCS_E_WORKSPACE
+    assert verify(lcs, L, kv, B=0) == lcs.LCS_OK                   # empty batch: nothing launched
+    assert verify(lcs, L, kv, B=0, q=0, out=0, prefix_len=0) == lcs.LCS_OK
+
+
+def test_select_host_errors():
+    lcs, L = lib()
+
+    def sel(**kw):
+        a = dict(lg=0x1000, ld=100, B=1, Hq=4, Hkv=2, pl=0x2000, maxL=100, mode=0, k=10, ns=4, nr=8, bs=0,
+                 idx=0x3000, cnt=0x4000, cap=22, ws=0x5000, wsb=1 << 24)
+        a.update(kw)
+        return L.lcs_select_topk(a["lg"], a["ld"], a["B"], a["Hq"], a["Hkv"], a["pl"], a["maxL"], a["mode"],
+                                 a["k"], a["ns"], a["nr"], a["bs"], a["idx"], a["cnt"], a["cap"], a["ws"],
+                                 a["wsb"], None)
+
+    assert sel(B=0) == lcs.LCS_OK
+    assert sel(B=0, lg=0, idx=0, cnt=0, pl=0) == lcs.LCS_OK
+    assert sel(mode=7) == lcs.LCS_E_ARG
+    assert sel(lg=0) == lcs.LCS_E_ARG
+    assert sel(Hq=5) == lcs.LCS_E_SHAPE
+    assert sel(k=-1) == lcs.LCS_E_ARG
+    assert sel(cap=21) == lcs.LCS_E_SHAPE
+    assert sel(ld=99) == lcs.LCS_E_SHAPE
+    assert sel(mode=2, bs=12) == lcs.LCS_E_UNSUPPORTED
+    assert sel(maxL=1 << 24, ld=1 << 24) == lcs.LCS_E_UNSUPPORTED
+    assert sel(wsb=10) == lcs.LCS_E_WORKSPACE
+    assert L.lcs_select_workspace_bytes(1, 4, 2, 0, 100, 0) > 0
+
+
+def test_sparse_host_errors():
+    lcs, L = lib()
+    kv = fake_kv(lcs)
+
+    def sp(kvd=kv, **kw):
+        a = dict(q=0x1000, B=1, n_q=1, Hq=4, mode=0, idx=0x2000, cnt=0x3000, cap=10, tb=0x4000, tl=0x5000,
+                 mtl=4, tm=None, scale=0.1, out=0x6000, lse=None, ws=0x7000, wsb=1 << 24)
+        a.update(kw)
+        return L.lcs_sparse_draft_attn(ctypes.byref(kvd), a["q"], a["B"], a["n_q"], a["Hq"], a["mode"], a["idx"],
+                                       a["cnt"], a["cap"], a["tb"], a["tl"], a["mtl"], a["tm"], a["scale"],
+                                       a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+    assert sp(B=0) == lcs.LCS_OK
+    assert sp(mode=3) == lcs.LCS_E_ARG
+    assert sp(tb=0) == lcs.LCS_E_ARG
+    assert sp(idx=0) == lcs.LCS_E_ARG
+    assert sp(n_q=65) == lcs.LCS_E_UNSUPPORTED
+    assert sp(tm=0x8000, mtl=65) == lcs.LCS_E_UNSUPPORTED
+    assert sp(mode=2) == lcs.LCS_E_UNSUPPORTED          # page 16 is not a multiple of 32
+    assert sp(fake_kv(lcs, page_size=64), mode=2, ws=None) == lcs.LCS_E_WORKSPACE
+    assert sp(wsb=0, cap=100000, mtl=100) == lcs.LCS_E_WORKSPACE
+
+
+def test_workspace_queries_are_deterministic():
+    lcs, L = lib()
+    kv = fake_kv(lcs, page_size=16, max_pages=4096, num_pages=4096 * 8, Hkv=8)
+    a = L.lcs_verify_workspace_bytes(1, 9, 32, ctypes.byref(kv), 32768)
+    b = L.lcs_verify_workspace_bytes(1, 9, 32, ctypes.byref(kv), 32768)
+    assert a == b and a > 0
+    assert L.lcs_verify_workspace_bytes(1, 9, 33, ctypes.byref(kv), 32768) == 0

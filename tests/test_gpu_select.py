@@ -1,0 +1,130 @@
+"""GPU parity of lcs_select_topk.
+
+* Bit-exact: the CPU rule in the pinned fp32 order, run on the GPU's own logits,
+  gives identical index arrays and counts.
+* Against oracle logits: at least 99% overlap with the fp64 selection (near-ties
+  at the k-th place may legitimately swap between fp32 and fp64 scores).
+"""
+import numpy as np
+import pytest
+
+from long_context_self_amd import synth
+from oracle import attention as oa
+from oracle import select as osel
+
+from gpu_helpers import bf16_dev, i32_dev, kv_dev, require_gpu, scale_for
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_select(logits_np, prefix_len, Hkv, mode, top_k, n_sink, n_recent, bs=0, poison=True):
+    torch, lcs = require_gpu()
+    lg = torch.from_numpy(np.ascontiguousarray(logits_np, dtype=np.float32)).cuda()
+    pl = i32_dev(prefix_len, torch)
+    idx, cnt = lcs.select_topk(lg, pl, int(np.max(prefix_len)), Hkv, mode, top_k, n_sink, n_recent,
+                               block_size=bs)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+def cpu_rule(logits_np, prefix_len, Hkv, mode, top_k, n_sink, n_recent, bs=0, precision="f32"):
+    res = osel.select(logits_np, prefix_len, Hkv, mode, top_k, n_sink, n_recent, bs, precision)
+    return res
+
+
+def assert_exact(idx, cnt, res):
+    for b in range(len(res)):
+        for s in range(len(res[b])):
+            ref = res[b][s]
+            assert cnt[b, s] == ref.size, f"count b={b} s={s}: {cnt[b, s]} vs {ref.size}"
+            assert np.array_equal(idx[b, s, :ref.size], ref), f"indices differ at b={b} s={s}"
+
+
+def gpu_logits(cfg, kv, q):
+    torch, lcs = require_gpu()
+    dkv = kv_dev(kv, torch, lcs)
+    maxL = int(kv.prefix_len.max())
+    _, logits, _ = lcs.verify_attn(dkv, bf16_dev(q, torch), i32_dev(kv.prefix_len, torch), maxL,
+                                   scale_for(cfg.d), (0, q.shape[1] - 1))
+    torch.cuda.synchronize()
+    return logits.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,L,B,mode", [("tiny", None, 1, "shared"),
+                                           ("llama8b_32k", 8192, 1, "shared"),
+                                           ("qwen14b_64k", 9000, 2, "per_kv_head"),
+                                           ("stress_128k", 5000, 3, "shared")])
+def test_bit_exact_on_gpu_logits_and_overlap(name, L, B, mode):
+    cfg = synth.CONFIGS[name]
+    cfg = cfg.with_(B=B, L=L if L else cfg.L)
+    lens = [cfg.L - 101 * b for b in range(B)]
+    top_k = min(cfg.top_k, cfg.L // 8)
+    kv = synth.make_paged_kv(cfg, seed=7, lens=lens)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=7)
+    glog = gpu_logits(cfg, kv, q)
+    idx, cnt = gpu_select(glog, kv.prefix_len, cfg.Hkv, mode, top_k, cfg.n_sink, cfg.n_recent)
+    assert_exact(idx, cnt, cpu_rule(glog, kv.prefix_len, cfg.Hkv, mode, top_k, cfg.n_sink, cfg.n_recent))
+    # against the fp64 oracle end to end
+    _, olog, _ = oa.verify_attn(q, kv.k, kv.v, kv.block_table, kv.prefix_len, cfg.page_size,
+                                scale_for(cfg.d))
+    ref = osel.select(olog, kv.prefix_len, cfg.Hkv, mode, top_k, cfg.n_sink, cfg.n_recent)
+    for b in range(B):
+        for s in range(len(ref[b])):
+            got = set(idx[b, s, :cnt[b, s]].tolist())
+            overlap = len(got & set(ref[b][s].tolist())) / ref[b][s].size
+            assert overlap >= 0.99, f"overlap {overlap}"
+
+
+@pytest.mark.parametrize("mode", ["shared", "per_kv_head", "block"])
+def test_ties_and_ragged(mode):
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv = 3, 8, 2
+    lens = np.array([9000, 4096, 777], dtype=np.int32)
+    ld = 9004
+    lg = (rng.integers(-3, 4, size=(B, Hq, 2, ld))).astype(np.float32)   # heavy ties
+    lg[:, :, :, 100] = -0.0
+    bs = 16 if mode == "block" else 0
+    k = 40 if mode == "block" else 600
+    idx, cnt = gpu_select(lg, lens, Hkv, mode, k, 5, 33, bs)
+    assert_exact(idx, cnt, cpu_rule(lg, lens, Hkv, mode, k, 5, 33, bs))
+
+
+@pytest.mark.parametrize("mode", ["shared", "block"])
+def test_short_context_keeps_everything(mode):
+    rng = np.random.default_rng(4)
+    lens = np.array([50, 0, 3], dtype=np.int32)
+    lg = rng.standard_normal((3, 4, 2, 64)).astype(np.float32)
+    bs = 8 if mode == "block" else 0
+    idx, cnt = gpu_select(lg, lens, 2, mode, 64, 4, 16, bs)
+    assert_exact(idx, cnt, cpu_rule(lg, lens, 2, mode, 64, 4, 16, bs))
+
+
+def test_zero_k_and_windows_only():
+    rng = np.random.default_rng(5)
+    lens = np.array([5000], dtype=np.int32)
+    lg = rng.standard_normal((1, 4, 2, 5000)).astype(np.float32)
+    idx, cnt = gpu_select(lg, lens, 2, "shared", 0, 4, 64)
+    assert_exact(idx, cnt, cpu_rule(lg, lens, 2, "shared", 0, 4, 64))
+
+
+def test_deterministic_repeat():
+    rng = np.random.default_rng(6)
+    lens = np.array([40000, 39000], dtype=np.int32)
+    lg = rng.standard_normal((2, 8, 2, 40000)).astype(np.float32)
+    a = gpu_select(lg, lens, 8, "per_kv_head", 2048, 4, 64)
+    b = gpu_select(lg, lens, 8, "per_kv_head", 2048, 4, 64)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert_exact(a[0], a[1], cpu_rule(lg, lens, 8, "per_kv_head", 2048, 4, 64))
+
+
+def test_full_stress_128k_shape():
+    """Full 128K x B8 shape of the long-context workload on synthetic logits."""
+    rng = np.random.default_rng(8)
+    cfg = synth.CONFIGS["stress_128k"]
+    lens = np.full(cfg.B, cfg.L, dtype=np.int32)
+    lg = (rng.standard_normal((cfg.B, cfg.Hq, 2, cfg.L)) * 1.4).astype(np.float32)
+    idx, cnt = gpu_select(lg, lens, cfg.Hkv, "shared", cfg.top_k, cfg.n_sink, cfg.n_recent)
+    for b in (0, cfg.B - 1):        # CPU rule on two of the eight sequences
+        ref = osel.topk_tokens(osel.scores_f32_pinned(lg, b, cfg.L, range(cfg.Hq)), cfg.L,
+                               cfg.top_k, cfg.n_sink, cfg.n_recent)
+        assert cnt[b, 0] == ref.size and np.array_equal(idx[b, 0, :ref.size], ref)

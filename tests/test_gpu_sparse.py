@@ -1,0 +1,159 @@
+"""GPU parity of lcs_sparse_draft_attn (token lists, per-KV-head lists, block lists)."""
+import numpy as np
+import pytest
+
+from long_context_self_amd import synth
+from oracle import attention as oa
+from oracle import select as osel
+
+from gpu_helpers import bf16_dev, i32_dev, kv_dev, require_gpu, scale_for, u64_dev
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+
+
+def run_sparse(cfg, kv, q, mode, idx, cnt, tail_begin, tail_len, tail_mask=None):
+    torch, lcs = require_gpu()
+    dkv = kv_dev(kv, torch, lcs)
+    B, n_q = q.shape[0], q.shape[1]
+    out = torch.full((B, n_q, cfg.Hq, cfg.d), float("nan"), device="cuda")
+    lse = torch.full((B, n_q, cfg.Hq), float("nan"), device="cuda")
+    tm = u64_dev(tail_mask, torch) if tail_mask is not None else None
+    lcs.sparse_draft_attn(dkv, bf16_dev(q, torch), mode, i32_dev(idx, torch), i32_dev(cnt, torch),
+                          i32_dev(tail_begin, torch), i32_dev(tail_len, torch), int(np.max(tail_len)),
+                          scale_for(cfg.d), tail_mask=tm, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def check(cfg, kv, q, mode, idx, cnt, tb, tl, tm=None):
+    out, lse = run_sparse(cfg, kv, q, mode, idx, cnt, tb, tl, tm)
+    o_out, o_lse = oa.sparse_attn(q, kv.k, kv.v, kv.block_table, cfg.page_size, mode, idx, cnt,
+                                  tb, tl, scale_for(cfg.d), tail_mask=tm)
+    assert np.isfinite(out).all()
+    err = np.max(np.abs(out - o_out))
+    assert err <= OUT_TOL, f"max-abs err {err}"
+    fin = np.isfinite(o_lse)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.max(np.abs(lse[fin] - o_lse[fin]), initial=0) <= 1e-3
+    return out, lse, err
+
+
+def selected(cfg, kv, q, mode):
+    _, olog, _ = oa.verify_attn(q, kv.k, kv.v, kv.block_table, kv.prefix_len, cfg.page_size,
+                                scale_for(cfg.d))
+    res = osel.select(olog, kv.prefix_len, cfg.Hkv, mode, cfg.top_k, cfg.n_sink, cfg.n_recent)
+    cap = max(a.size for r in res for a in r)
+    return osel.pack(res, cap)
+
+
+@pytest.mark.parametrize("name,L,B,mode", [("tiny", None, 1, "shared"),
+                                           ("llama8b_32k", 6000, 1, "shared"),
+                                           ("qwen14b_64k", 7000, 2, "per_kv_head"),
+                                           ("stress_128k", 5000, 2, "shared")])
+def test_draft_steps(name, L, B, mode):
+    cfg = synth.CONFIGS[name]
+    cfg = cfg.with_(B=B, L=L if L else cfg.L, top_k=min(cfg.top_k, (L or cfg.L) // 4))
+    lens = [cfg.L - 53 * b for b in range(B)]
+    kv = synth.make_paged_kv(cfg, seed=11, lens=lens)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=11)
+    idx, cnt = selected(cfg, kv, q, mode)
+    for j in (0, cfg.n_draft - 1):
+        qd = synth.make_queries(cfg, kv, 1, seed=11, tag=100 + j)
+        tl = np.full(B, cfg.n_q + j + 1, dtype=np.int32)
+        _, _, err = check(cfg, kv, qd, mode, idx, cnt, kv.prefix_len, tl)
+        print(f"{name} draft step {j}: max-abs err {err:.3e}")
+
+
+def test_full_selection_equals_dense_verify():
+    torch, lcs = require_gpu()
+    cfg = synth.CONFIGS["llama8b_32k"].with_(L=2000, B=2)
+    kv = synth.make_paged_kv(cfg, seed=12, lens=[2000, 1111])
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=12)
+    cap = 2000
+    idx = np.full((2, 1, cap), -1, dtype=np.int32)
+    cnt = np.zeros((2, 1), dtype=np.int32)
+    for b in range(2):
+        L = int(kv.prefix_len[b])
+        idx[b, 0, :L] = np.arange(L)
+        cnt[b, 0] = L
+    tm = np.stack([synth.chain_tail_masks(cfg.n_q)] * 2)
+    out_s, _, _ = check(cfg, kv, q, "shared", idx, cnt, kv.prefix_len, np.full(2, cfg.n_q, np.int32), tm)
+    dkv = kv_dev(kv, torch, lcs)
+    out_v, _, _ = lcs.verify_attn(dkv, bf16_dev(q, torch), i32_dev(kv.prefix_len, torch), 2000,
+                                  scale_for(cfg.d), (0, cfg.n_q - 1))
+    assert np.max(np.abs(out_s - out_v.cpu().numpy())) <= 1e-4
+
+
+def test_edge_cases():
+    cfg = synth.CONFIGS["tiny"].with_(B=3)
+    kv = synth.make_paged_kv(cfg, seed=13, lens=[1024, 500, 40])
+    q = synth.make_queries(cfg, kv, 1, seed=13)
+    cap = 8
+    idx = np.full((3, 1, cap), -1, dtype=np.int32)
+    cnt = np.array([[1], [0], [0]], dtype=np.int32)
+    idx[0, 0, 0] = 77                 # single index, no tail -> that V row
+    tb = kv.prefix_len.copy()
+    tl = np.array([0, 3, 0], dtype=np.int32)   # b=1: tail only; b=2: nothing visible
+    out, lse, _ = check(cfg, kv, q, "shared", idx, cnt, tb, tl)
+    for h in range(cfg.Hq):
+        vrow = oa.paged_rows(kv.v, kv.block_table, 0, h // cfg.G, np.array([77]), cfg.page_size)[0]
+        assert np.max(np.abs(out[0, 0, h] - vrow)) <= 1e-6
+    assert np.all(out[2] == 0) and np.all(np.isneginf(lse[2]))
+
+
+def block_case(cfg, seed, L=None):
+    L = L or cfg.L
+    cfg = cfg.with_(L=L)
+    kv = synth.make_paged_kv(cfg, seed=seed)
+    nblk = L // cfg.page_size
+    sets = synth.make_block_sets(cfg, nblk, seed=seed)
+    cnt = np.full((cfg.B, cfg.n_q, cfg.Hkv), cfg.blocks_per_row, dtype=np.int32)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=seed)
+    tm = np.stack([synth.tree_tail_masks(cfg.n_q, cfg.tree_branches)] * cfg.B)
+    tl = np.full(cfg.B, cfg.n_q, dtype=np.int32)
+    return cfg, kv, q, sets, cnt, tm, tl
+
+
+def test_block_merged_full_nsa_16k():
+    cfg, kv, q, sets, cnt, tm, tl = block_case(synth.CONFIGS["nsa_16k"], seed=0)
+    out, lse, err = check(cfg, kv, q, "block", sets, cnt, kv.prefix_len, tl, tm)
+    print(f"block merged: max-abs err {err:.3e}")
+
+
+def test_block_merged_equals_unmerged():
+    """SSV section 4.2: the merged schedule must not change any row's result.  The
+    unmerged reference runs each row alone (n_q = 1) through the same entry point."""
+    cfg, kv, q, sets, cnt, tm, tl = block_case(synth.CONFIGS["nsa_16k"], seed=1, L=4096)
+    merged, mlse = run_sparse(cfg, kv, q, "block", sets, cnt, kv.prefix_len, tl, tm)
+    for i in range(cfg.n_q):
+        tm_i = tm[:, i:i + 1].copy()
+        tm_i_shift = tm_i        # row i keeps its own tail bits
+        one, olse = run_sparse(cfg, kv, q[:, i:i + 1].copy(), "block", sets[:, i:i + 1].copy(),
+                               cnt[:, i:i + 1].copy(), kv.prefix_len, tl, tm_i_shift)
+        assert np.max(np.abs(one[:, 0] - merged[:, i])) <= 1e-5
+        assert np.max(np.abs(olse[:, 0] - mlse[:, i])) <= 1e-5
+
+
+def test_block_partial_last_block_and_ragged_counts():
+    cfg = synth.CONFIGS["nsa_16k"].with_(B=2, L=1000, n_q=4, tree_branches=2, blocks_per_row=5,
+                                         core_blocks=2)
+    kv = synth.make_paged_kv(cfg, seed=3)
+    nblk = (cfg.L + cfg.page_size - 1) // cfg.page_size      # last block is partial
+    sets = synth.make_block_sets(cfg, nblk, seed=3)
+    cnt = np.array([[[5] * cfg.Hkv, [3] * cfg.Hkv, [0] * cfg.Hkv, [5] * cfg.Hkv]] * 2, dtype=np.int32)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=3)
+    tm = np.stack([synth.tree_tail_masks(4, 2)] * 2)
+    check(cfg, kv, q, "block", sets, cnt, kv.prefix_len, np.full(2, 4, np.int32), tm)
+
+
+def test_full_llama8b_32k_draft_step():
+    cfg = synth.CONFIGS["llama8b_32k"]
+    kv = synth.make_paged_kv(cfg, seed=0)
+    rng = np.random.default_rng(0)
+    idx = np.sort(rng.choice(cfg.L, size=cfg.top_k + cfg.n_sink + cfg.n_recent, replace=False))
+    idx = idx.astype(np.int32)[None, None, :]
+    cnt = np.array([[idx.shape[-1]]], dtype=np.int32)
+    qd = synth.make_queries(cfg, kv, 1, seed=0, tag=200)
+    check(cfg, kv, qd, "shared", idx, cnt, kv.prefix_len, np.array([cfg.n_q + 1], np.int32))

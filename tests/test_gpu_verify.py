@@ -1,0 +1,154 @@
+"""GPU parity of lcs_verify_attn against the fp64 oracle.
+
+Tolerances (bf16 inputs, fp32 accumulation): attention outputs within 1e-2
+max-abs, Collect-2-Query logits within 1e-3 relative, where "relative" is
+|g - o| / max(|o|, rms of the oracle row) so that near-zero logits do not blow
+the ratio up.
+"""
+import numpy as np
+import pytest
+
+from long_context_self_amd import synth
+from oracle import attention as oa
+
+from gpu_helpers import (bf16_dev, i32_dev, kv_dev, logit_rel_err, require_gpu, scale_for,
+                         u64_dev)
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LOGIT_TOL = 1e-3
+
+
+def run_verify(cfg, kv, q, tree=None, ld_extra=0):
+    torch, lcs = require_gpu()
+    dkv = kv_dev(kv, torch, lcs)
+    B, n_q = cfg.B, q.shape[1]
+    maxL = int(kv.prefix_len.max())
+    out = torch.full((B, n_q, cfg.Hq, cfg.d), float("nan"), device="cuda")
+    logits = torch.full((B, cfg.Hq, 2, maxL + ld_extra), float("nan"), device="cuda")
+    lse = torch.full((B, n_q, cfg.Hq), float("nan"), device="cuda")
+    tm = u64_dev(tree, torch) if tree is not None else None
+    lcs.verify_attn(dkv, bf16_dev(q, torch), i32_dev(kv.prefix_len, torch), maxL, scale_for(cfg.d),
+                    (0, n_q - 1), tree_mask=tm, out=out, logits=logits, lse=lse)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), logits.cpu().numpy(), lse.cpu().numpy()
+
+
+def check(cfg, kv, q, tree=None, ld_extra=0):
+    out, logits, lse = run_verify(cfg, kv, q, tree, ld_extra)
+    maxL = int(kv.prefix_len.max())
+    o_out, o_logits, o_lse = oa.verify_attn(q, kv.k, kv.v, kv.block_table, kv.prefix_len,
+                                            cfg.page_size, scale_for(cfg.d), tree_mask=tree,
+                                            logits_ld=maxL + ld_extra)
+    err = np.max(np.abs(out - o_out))
+    assert np.isfinite(out).all(), "unwritten or non-finite outputs"
+    assert err <= OUT_TOL, f"out max-abs err {err}"
+    assert np.max(np.abs(lse - o_lse)) <= 1e-3
+    for b in range(cfg.B):
+        L = int(kv.prefix_len[b])
+        e = logit_rel_err(logits[b, :, :, :L], o_logits[b, :, :, :L])
+        assert e <= LOGIT_TOL, f"logit rel err {e} (b={b})"
+        assert np.isnan(logits[b, :, :, L:]).all(), "columns past the prefix were written"
+    return err
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny(seed):
+    cfg = synth.CONFIGS["tiny"]
+    kv = synth.make_paged_kv(cfg, seed=seed)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=seed)
+    err = check(cfg, kv, q)
+    print(f"tiny seed {seed}: out max-abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("name,L,B", [("llama8b_32k", 2048, 1), ("qwen14b_64k", 1500, 2),
+                                      ("stress_128k", 1333, 2)])
+def test_reduced_configs(name, L, B):
+    cfg = synth.CONFIGS[name].with_(L=L, B=B)
+    lens = [L - 37 * b for b in range(B)]          # ragged, not tile aligned
+    kv = synth.make_paged_kv(cfg, seed=1, lens=lens)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=1)
+    err = check(cfg, kv, q, ld_extra=5)
+    print(f"{name} L={L} B={B}: out max-abs err {err:.3e}")
+
+
+def test_ragged_tree_mask_many_rows():
+    # 8 tree rows x G=8 -> 64 rows per workgroup (four 16-row MFMA tiles)
+    cfg = synth.Config("t", B=3, Hq=16, Hkv=2, d=128, L=300, page_size=16, n_q=8, n_draft=0,
+                       top_k=8, n_sink=0, n_recent=0, mode="shared", crit_frac=0.02)
+    kv = synth.make_paged_kv(cfg, seed=4, lens=[300, 17, 0])
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=4)
+    tree = np.stack([synth.tree_tail_masks(8, 2)] * cfg.B)
+    check(cfg, kv, q, tree=tree)
+
+
+def test_row_chunks_beyond_64():
+    # n_q * G = 9 * 8 = 72 rows: two row chunks per KV head
+    cfg = synth.Config("t", B=1, Hq=16, Hkv=2, d=64, L=777, page_size=32, n_q=9, n_draft=0,
+                       top_k=8, n_sink=0, n_recent=0, mode="shared", crit_frac=0.02)
+    kv = synth.make_paged_kv(cfg, seed=5)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=5)
+    check(cfg, kv, q)
+
+
+def test_v_ones_gives_ones():
+    cfg = synth.CONFIGS["llama8b_32k"].with_(L=1000)
+    kv = synth.make_paged_kv(cfg, seed=2)
+    kv.v[:] = 0x3F80
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=2)
+    out, _, _ = run_verify(cfg, kv, q)
+    assert np.max(np.abs(out - 1.0)) <= 1e-5
+
+
+def test_deterministic():
+    cfg = synth.CONFIGS["llama8b_32k"].with_(L=3000)
+    kv = synth.make_paged_kv(cfg, seed=3)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=3)
+    a = run_verify(cfg, kv, q)
+    b = run_verify(cfg, kv, q)
+    for x, y in zip(a, b):
+        assert np.array_equal(np.nan_to_num(x, nan=7.0).view(np.uint32),
+                              np.nan_to_num(y, nan=7.0).view(np.uint32))
+
+
+def test_full_llama8b_32k_sampled():
+    """Full 32K shape in the launch configuration the benchmark uses; the oracle
+    checks sampled (row, head) outputs one by one and whole logit rows of sampled heads."""
+    cfg = synth.CONFIGS["llama8b_32k"]
+    kv = synth.make_paged_kv(cfg, seed=0)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=0)
+    out, logits, lse = run_verify(cfg, kv, q)
+    L = cfg.L
+    sc = scale_for(cfg.d)
+    qf = oa.bf16_to_f64(q)
+    rng = np.random.default_rng(0)
+    for _ in range(12):
+        i = int(rng.integers(cfg.n_q))
+        h = int(rng.integers(cfg.Hq))
+        g = h // cfg.G
+        pos = np.arange(L + i + 1)
+        K = oa.paged_rows(kv.k, kv.block_table, 0, g, pos, cfg.page_size)
+        V = oa.paged_rows(kv.v, kv.block_table, 0, g, pos, cfg.page_size)
+        o, p, l = oa.attention_one(qf[0, i, h], K, V, sc)
+        assert np.max(np.abs(out[0, i, h] - o)) <= OUT_TOL
+        assert abs(lse[0, i, h] - l) <= 1e-3
+        if i in (0, cfg.n_q - 1):
+            c = 0 if i == 0 else 1
+            ref = sc * (K[:L] @ qf[0, i, h])
+            assert logit_rel_err(logits[0, h, c, :L], ref) <= LOGIT_TOL
+    assert np.isfinite(out).all()
+
+
+def test_empty_batch_and_errors():
+    torch, lcs = require_gpu()
+    cfg = synth.CONFIGS["tiny"]
+    kv = synth.make_paged_kv(cfg, seed=0)
+    dkv = kv_dev(kv, torch, lcs)
+    q = bf16_dev(synth.make_queries(cfg, kv, cfg.n_q), torch)
+    pl = i32_dev(kv.prefix_len, torch)
+    with pytest.raises(lcs.LcsError) as e:
+        lcs.verify_attn(dkv, q, pl, cfg.L, 0.125, (0, cfg.n_q))       # row out of range
+    assert e.value.status == lcs.LCS_E_ARG
+    # B = 0 is a no-op
+    lcs.verify_attn(dkv, q[:0], pl, cfg.L, 0.125, (0, cfg.n_q - 1))
