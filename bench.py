@@ -1,0 +1,276 @@
+"""Benchmark of the verify / select / sparse-draft attention path on one MI355X.
+
+One step is one speculative decode iteration of the attention hot path of an
+n-layer model (default: the Llama-3-8B-shaped layer at 32K context, 32 layers):
+
+    for each of the k draft steps:  sparse_draft_attn on every layer
+    for every layer:                verify_attn (k+1 rows, two logit rows collected)
+    for every layer:                select_topk (next iteration's sparse set)
+
+Every layer owns its own KV cache copy, so consecutive calls on one layer are
+separated by the other layers' traffic (several GB) and read HBM, not the
+256 MB Infinity Cache; this is the situation of a real multi-layer model.
+
+Prints one JSON line.  `value` is the achieved algorithmic HBM bandwidth of the
+whole step (bytes the method must move / step time); the per-call latencies in
+microseconds are in `kernels`.  `roofline` is for the dominant kernel (verify).
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_llama8b_32k_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "long_context_self_amd", "csrc", f) for f in ("attn.hip", "lcs_internal.h")]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="llama8b_32k")
+    p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    return p.parse_args()
+
+
+def algorithmic_bytes(cfg, S_draft, tail_lens):
+    """Bytes each call must move at minimum (bf16 = 2 B, fp32 / int32 = 4 B)."""
+    B, Hq, Hkv, d, L, n_q = cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.L, cfg.n_q
+    verify = (4 * B * Hkv * d * (L + n_q)        # K and V of every cached position
+              + 2 * B * n_q * Hq * d             # Q
+              + 4 * B * n_q * Hq * d             # O (fp32)
+              + 4 * B * n_q * Hq                 # lse
+              + 8 * B * Hq * L)                  # two collected logit rows (fp32)
+    n_sets = 1 if cfg.mode == "shared" else Hkv
+    select = 8 * B * Hq * L + 4 * B * n_sets * S_draft + 4 * B * n_sets
+    drafts = []
+    for tl in tail_lens:
+        drafts.append(4 * B * Hkv * d * (S_draft + tl)   # gathered K and V rows, all KV heads
+                      + 4 * B * n_sets * S_draft          # index list
+                      + 2 * B * Hq * d + 4 * B * Hq * d + 4 * B * Hq)
+    return verify, select, drafts
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(per_launch_bytes):
+    """HBM bytes per verify launch from committed rocprofv3 counter runs, if they match this source."""
+    try:
+        rec = json.load(open(PROFILE_TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, kv, q, qd, idx, budget_s):
+    """fp64 oracle on a bounded sample: one KV head of one layer per round (verify for
+    its G heads, the shared select over all heads' rows, and k draft steps)."""
+    from oracle import attention as oa
+    from oracle import select as osel
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    scale = 1.0 / math.sqrt(cfg.d)
+    G = cfg.G
+    # one KV group: a 1-KV-head view of the cache and G query heads
+    k1 = kv.k[:, :1]
+    v1 = kv.v[:, :1]
+    q1 = q[:, :, :G]
+    bytes_done = 0
+    rounds = 0
+    t0 = time.perf_counter()
+    while True:
+        _, lg, _ = oa.verify_attn(q1, k1, v1, kv.block_table, kv.prefix_len, cfg.page_size, scale)
+        full_lg = np.repeat(lg, cfg.Hkv, axis=1)   # stand-in rows for the other heads' scores
+        sel = osel.select(full_lg, kv.prefix_len, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent)
+        i_, c_ = osel.pack(sel, max(a.size for r in sel for a in r))
+        for j in range(cfg.n_draft):
+            tl = np.full(cfg.B, cfg.n_q + j + 1, dtype=np.int32)
+            oa.sparse_attn(qd[j][:, :, :G], k1, v1, kv.block_table, cfg.page_size, cfg.mode,
+                           i_, c_, kv.prefix_len, tl, scale)
+        S = int(c_[0, 0])
+        v_b, s_b, d_b = algorithmic_bytes(cfg, S, [cfg.n_q + j + 1 for j in range(cfg.n_draft)])
+        bytes_done += (v_b + sum(d_b)) / cfg.Hkv + s_b
+        rounds += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(bytes_done / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rounds} rounds of one KV head (G={G} query heads) of one {cfg.name} layer: "
+                      f"verify + shared select + {cfg.n_draft} draft steps, fp64 NumPy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the multi-GPU "
+              "sharding of this path is described in the design notes, not built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from long_context_self_amd import lcs, synth
+
+    cfg = synth.CONFIGS[args.config]
+    assert cfg.mode in ("shared", "per_kv_head"), "bench covers the token-set workloads"
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    scale = 1.0 / math.sqrt(cfg.d)
+    kv = synth.make_paged_kv(cfg, seed=0)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=0)
+    qd = [synth.make_queries(cfg, kv, 1, seed=0, tag=100 + j) for j in range(cfg.n_draft)]
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    k0, v0 = bf16(kv.k), bf16(kv.v)
+    bt = torch.from_numpy(kv.block_table).to(dev)
+    R = args.layers
+    layers = [lcs.PagedKV(k0 if r == 0 else k0.clone(), v0 if r == 0 else v0.clone(), bt) for r in range(R)]
+    qv = bf16(q)
+    qds = [bf16(x) for x in qd]
+    pl = torch.from_numpy(kv.prefix_len).to(dev)
+    B, Hq, L = cfg.B, cfg.Hq, cfg.L
+    n_sets = 1 if cfg.mode == "shared" else cfg.Hkv
+    S = cfg.n_sink + cfg.top_k + cfg.n_recent
+    outs = torch.empty((B, cfg.n_q, Hq, cfg.d), dtype=torch.float32, device=dev)
+    lses = torch.empty((B, cfg.n_q, Hq), dtype=torch.float32, device=dev)
+    logits = [torch.empty((B, Hq, 2, L), dtype=torch.float32, device=dev) for _ in range(R)]
+    idx = [torch.empty((B, n_sets, S), dtype=torch.int32, device=dev) for _ in range(R)]
+    cnt = [torch.empty((B, n_sets), dtype=torch.int32, device=dev) for _ in range(R)]
+    dout = torch.empty((B, 1, Hq, cfg.d), dtype=torch.float32, device=dev)
+    dlse = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
+    tls = [torch.full((B,), cfg.n_q + j + 1, dtype=torch.int32, device=dev) for j in range(cfg.n_draft)]
+    max_tl = cfg.n_q + cfg.n_draft
+    ws_v = torch.empty(lcs.verify_workspace_bytes(layers[0], B, cfg.n_q, Hq, L), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(lcs.select_workspace_bytes(B, Hq, cfg.Hkv, cfg.mode, L), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(lcs.sparse_workspace_bytes(layers[0], B, 1, Hq, cfg.mode, S, max_tl),
+                       dtype=torch.uint8, device=dev)
+
+    def verify(r):
+        lcs.verify_attn(layers[r], qv, pl, L, scale, cfg.collect_rows, out=outs, logits=logits[r], lse=lses,
+                        workspace=ws_v)
+
+    def select(r):
+        lcs.select_topk(logits[r], pl, L, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
+                        indices=idx[r], counts=cnt[r], workspace=ws_s)
+
+    def draft(r, j):
+        lcs.sparse_draft_attn(layers[r], qds[j], cfg.mode, idx[r], cnt[r], pl, tls[j], max_tl, scale,
+                              out=dout, lse=dlse, workspace=ws_d)
+
+    for r in range(R):       # the first iteration's sparse sets
+        verify(r)
+        select(r)
+    torch.cuda.synchronize()
+
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    phase_ms = {"draft": 0.0, "verify": 0.0, "select": 0.0}
+
+    def step(timed):
+        ev = []
+        e0 = E(); e0.record(); ev.append(("start", e0))
+        for j in range(cfg.n_draft):
+            for r in range(R):
+                draft(r, j)
+        e1 = E(); e1.record(); ev.append(("draft", e1))
+        for r in range(R):
+            verify(r)
+        e2 = E(); e2.record(); ev.append(("verify", e2))
+        for r in range(R):
+            select(r)
+        e3 = E(); e3.record(); ev.append(("select", e3))
+        return ev
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        events.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for ev in events:
+        for (_, a), (name, b) in zip(ev[:-1], ev[1:]):
+            phase_ms[name] += a.elapsed_time(b)
+    ms_per_step = wall * 1e3 / args.steps
+    n_draft_calls = args.steps * cfg.n_draft * R
+    t_draft_us = phase_ms["draft"] * 1e3 / n_draft_calls
+    t_verify_us = phase_ms["verify"] * 1e3 / (args.steps * R)
+    t_select_us = phase_ms["select"] * 1e3 / (args.steps * R)
+
+    s_count = int(cnt[0].min().item())
+    tail_lens = [cfg.n_q + j + 1 for j in range(cfg.n_draft)]
+    vb, sb, db = algorithmic_bytes(cfg, s_count, tail_lens)
+    step_bytes = R * (vb + sb + sum(db))
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    v_gbs = vb / (t_verify_us * 1e-6) / 1e9
+    s_gbs = sb / (t_select_us * 1e-6) / 1e9
+    d_gbs = (sum(db) / len(db)) / (t_draft_us * 1e-6) / 1e9
+    flops_verify = 4 * B * Hq * cfg.n_q * (L + cfg.n_q) * cfg.d
+    gamma_attn = t_draft_us / t_verify_us
+
+    result = {
+        "metric": "draft-step & verify-step attention latency (us), achieved HBM GB/s vs peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "Hq": Hq, "Hkv": cfg.Hkv, "d": cfg.d, "L": L,
+                   "page_size": cfg.page_size, "n_q": cfg.n_q, "n_draft": cfg.n_draft,
+                   "select": f"{cfg.mode} top-{cfg.top_k}+{cfg.n_sink} sink+{cfg.n_recent} recent",
+                   "layers": R},
+        "kernels": {
+            "verify": {"us": round(t_verify_us, 2), "bytes": vb, "GB/s": round(v_gbs, 1),
+                       "frac_hbm_peak": round(v_gbs / HBM_PEAK_GBS, 4),
+                       "TFLOP/s": round(flops_verify / (t_verify_us * 1e-6) / 1e12, 2)},
+            "select": {"us": round(t_select_us, 2), "bytes": sb, "GB/s": round(s_gbs, 1),
+                       "frac_hbm_peak": round(s_gbs / HBM_PEAK_GBS, 4)},
+            "draft_step": {"us": round(t_draft_us, 2), "bytes": int(sum(db) / len(db)),
+                           "GB/s": round(d_gbs, 1), "frac_hbm_peak": round(d_gbs / HBM_PEAK_GBS, 4),
+                           "selected": s_count},
+        },
+        "gamma_attn": round(gamma_attn, 4),
+        "roofline": {"bound": "hbm", "achieved": round(v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(v_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_record(vb),
+                     "kernel": "verify_attn (attn_kernel + split-K combine), per launch"},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, kv, q, qd, None, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -140,7 +140,7 @@ lcs_status lcs_verify_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int
  * logits with the same fp32 summation order.
  *
  *  logits       fp32 [B][Hq][2][logits_ld] as written by lcs_verify_attn.
- *  block_size   BLOCK mode only: power of two in [4, 4096]; ignored otherwise.
+ *  block_size   BLOCK mode only: power of two in [4, 512]; ignored otherwise.
  *  workspace    at least lcs_select_workspace_bytes(...) bytes, no initialisation.
  * Limits: max_prefix_len < 2^24.
  * ------------------------------------------------------------------------- */

@@ -93,6 +93,7 @@ template <int D, int KS, int DPL>
 struct StepBuf {
   u32x4 k[2][KS];
   VRow<DPL> v[8];
+  uint32_t vok;     // bit t set when V token t of this lane is a real cache row
 };
 
 struct SeqInfo {
@@ -129,96 +130,172 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, int g) {
   return si;
 }
 
-// Token slot metadata for one step: each lane computes slot (lane & 31).
-// row = K/V row index ((page*Hkv + g)*P + slot) or -1; vis = bit i set when
-// verifier row i may attend to the token.
-__device__ __forceinline__ void step_meta(const AttnArgs& a, const SeqInfo& si, int b, int g,
-                                          int step, uint64_t colmask, int lane, int& row,
-                                          uint64_t& vis) {
-  const int t = lane & 31;
-  const int lgP = a.lg_page;
-  const int P = 1 << lgP;
-  int pos = -1;
-  int jt = -1;          // tail slot index, or -1
-  uint64_t v = 0;
-  if (a.mode == MODE_DENSE) {
-    const int u = step * kStepTokens + t;
-    if (u < si.L) {
-      pos = u;
-      v = kAll;
-    } else if (u < si.L + a.n_q) {
-      pos = u;
-      jt = u - si.L;
-    }
-  } else if (a.mode == MODE_BLOCK) {
-    const int spb = P / kStepTokens;
-    const int blk_steps = si.U * spb;
-    if (step < blk_steps) {
-      const int e = step / spb;
-      const int sub = step - e * spb;
-      const int blk = si.ub[e];
-      const uint64_t m = si.um[e];
-      const int p = blk * P + sub * kStepTokens + t;
-      if (blk >= 0 && blk < a.max_pages && p < si.tb) {
-        pos = p;
-        v = m;
+// ---------------------------------------------------------------------------
+// Token metadata.  A wave owns a contiguous range of 32-token steps.  For each
+// window of kMW steps it builds, one window ahead, the K/V row index and the
+// row-visibility mask of every token slot in a per-wave LDS ring, in three
+// stages spread over the first three steps of the previous window (positions
+// and index-list loads; block-table loads; rows, masks and flags to LDS).  No
+// global load therefore sits between a step and the issue of its data loads.
+// ---------------------------------------------------------------------------
+constexpr int kMW = 4;                      // steps per metadata window
+constexpr int kMT = kMW * kStepTokens;      // token slots per window
+constexpr int kTokPerLane = kMT / 64;       // slots each lane builds per window
+
+struct WaveMeta {
+  int32_t row[2][kMT];
+  uint64_t vis[2][kMT];
+  uint32_t full[2][kMW];
+};
+
+struct MetaStage {
+  int pos[kTokPerLane];
+  int jt[kTokPerLane];
+  int page[kTokPerLane];
+  uint64_t v[kTokPerLane];
+};
+
+// Stage A: logical position of each slot (index-list loads in list modes).
+__device__ __forceinline__ void meta_stage_a(const AttnArgs& a, const SeqInfo& si, int wbase, int w1,
+                                             int lane, MetaStage& ms) {
+  const int P = 1 << a.lg_page;
+#pragma unroll
+  for (int r = 0; r < kTokPerLane; ++r) {
+    const int tok = lane + 64 * r;
+    const int step = wbase + tok / kStepTokens;
+    const int t = tok & (kStepTokens - 1);
+    int pos = -1, jt = -1;
+    uint64_t v = 0;
+    if (step < w1) {
+      if (a.mode == MODE_DENSE) {
+        const int u = step * kStepTokens + t;
+        if (u < si.L) {
+          pos = u;
+          v = kAll;
+        } else if (u < si.L + a.n_q) {
+          pos = u;
+          jt = u - si.L;
+        }
+      } else if (a.mode == MODE_BLOCK) {
+        const int spb = P / kStepTokens;
+        const int blk_steps = si.U * spb;
+        if (step < blk_steps) {
+          const int e = step / spb;
+          const int blk = si.ub[e];
+          const int p = blk * P + (step - e * spb) * kStepTokens + t;
+          if (blk >= 0 && blk < a.max_pages && p < si.tb) {
+            pos = p;
+            v = si.um[e];
+          }
+        } else {
+          const int u = (step - blk_steps) * kStepTokens + t;
+          if (u < si.tl) {
+            pos = si.tb + u;
+            jt = u;
+          }
+        }
+      } else {
+        const int u = step * kStepTokens + t;
+        // the index load is issued for every slot (clamped), keeping wait counts static
+        const int32_t* src = (si.cnt > 0) ? si.list + min(max(u, 0), si.cnt - 1) : a.bt;
+        const int lp = *src;
+        if (u < si.cnt) {
+          pos = lp;
+          v = kAll;
+        } else if (u - si.cnt < si.tl) {
+          jt = u - si.cnt;
+          pos = si.tb + jt;
+        }
       }
-    } else {
-      const int u = (step - blk_steps) * kStepTokens + t;
-      if (u < si.tl) {
-        pos = si.tb + u;
-        jt = u;
-      }
     }
-  } else {
-    const int u = step * kStepTokens + t;
-    if (u < si.cnt) {
-      pos = si.list[u];
-      v = kAll;
-    } else if (u - si.cnt < si.tl) {
-      jt = u - si.cnt;
-      pos = si.tb + jt;
-    }
+    ms.pos[r] = pos;
+    ms.jt[r] = jt;
+    ms.v[r] = v;
   }
-  // tail visibility comes from the column mask held by lane jt (all lanes shuffle)
-  const uint64_t cm = shfl64(colmask, jt & 63);
-  if (jt >= 0) v = (jt < 64 || a.rowmask == nullptr) ? cm : 0;
-  row = -1;
-  if (pos >= 0 && (pos >> lgP) < a.max_pages) {
-    const int page = a.bt[(size_t)b * a.max_pages + (pos >> lgP)];
-    if ((unsigned)page < (unsigned)a.num_pages) row = ((page * a.Hkv + g) << lgP) | (pos & (P - 1));
-  }
-  if (row < 0) v = 0;
-  vis = v;
 }
 
+// Stage B: physical page of each slot (block-table loads).
+__device__ __forceinline__ void meta_stage_b(const AttnArgs& a, int b, MetaStage& ms) {
+#pragma unroll
+  for (int r = 0; r < kTokPerLane; ++r) {
+    const int pos = ms.pos[r];
+    const int pi = pos >> a.lg_page;
+    const bool ok = pos >= 0 && pi < a.max_pages;
+    // issued for every slot (clamped in range), keeping wait counts static
+    const int page = a.bt[(size_t)b * a.max_pages + (ok ? pi : 0)];
+    ms.page[r] = ok ? page : -1;
+  }
+}
+
+// Stage C: row index, visibility mask and per-step "everything visible" flag to LDS.
+__device__ __forceinline__ void meta_stage_c(const AttnArgs& a, int g, uint64_t colmask, int lane,
+                                             const MetaStage& ms, WaveMeta& wm, int buf) {
+  const int P = 1 << a.lg_page;
+#pragma unroll
+  for (int r = 0; r < kTokPerLane; ++r) {
+    const int tok = lane + 64 * r;
+    const int jt = ms.jt[r];
+    const uint64_t cm = shfl64(colmask, jt & 63);     // every lane takes part in the shuffle
+    uint64_t v = ms.v[r];
+    if (jt >= 0) v = (jt < 64 || a.rowmask == nullptr) ? cm : 0;
+    int row = -1;
+    const int page = ms.page[r];
+    if ((unsigned)page < (unsigned)a.num_pages) row = ((page * a.Hkv + g) << a.lg_page) | (ms.pos[r] & (P - 1));
+    if (row < 0) v = 0;
+    wm.row[buf][tok] = row;
+    wm.vis[buf][tok] = v;
+    const uint64_t ok = __ballot(row >= 0 && v == kAll);
+    if (lane == 0) {
+      wm.full[buf][2 * r] = (uint32_t)ok == 0xffffffffu;
+      wm.full[buf][2 * r + 1] = (uint32_t)(ok >> 32) == 0xffffffffu;
+    }
+  }
+}
+
+// Issue the K and V loads of local step ls of window buffer buf.
 template <int D, int KS, int DPL>
-__device__ __forceinline__ void step_load(const AttnArgs& a, int row, int x, int j,
-                                          StepBuf<D, KS, DPL>& buf) {
-  const int rk0 = __shfl(row, x);
-  const int rk1 = __shfl(row, 16 + x);
+__device__ __forceinline__ void step_load(const AttnArgs& a, const WaveMeta& wm, int buf, int ls, int x,
+                                          int j, StepBuf<D, KS, DPL>& sb) {
+  const int32_t* rows = wm.row[buf] + ls * kStepTokens;
+  const int rk0 = rows[x];
+  const int rk1 = rows[16 + x];
   const uint16_t* k0 = a.k + (size_t)max(rk0, 0) * D + 8 * j;
   const uint16_t* k1 = a.k + (size_t)max(rk1, 0) * D + 8 * j;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    buf.k[0][ks] = *reinterpret_cast<const u32x4*>(k0 + 32 * ks);
-    buf.k[1][ks] = *reinterpret_cast<const u32x4*>(k1 + 32 * ks);
+    sb.k[0][ks] = *reinterpret_cast<const u32x4*>(k0 + 32 * ks);
+    sb.k[1][ks] = *reinterpret_cast<const u32x4*>(k1 + 32 * ks);
   }
+  const int4 rv0 = *reinterpret_cast<const int4*>(rows + 4 * j);
+  const int4 rv1 = *reinterpret_cast<const int4*>(rows + 16 + 4 * j);
+  const int rv[8] = {rv0.x, rv0.y, rv0.z, rv0.w, rv1.x, rv1.y, rv1.z, rv1.w};
+  // every load is issued (invalid slots read row 0) so the wait counts stay static;
+  // invalid rows are zeroed at use, since a masked weight times a NaN would poison O
+  uint32_t vok = 0;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const int tok = (t < 4) ? (4 * j + t) : (12 + 4 * j + t);
-    const int rv = __shfl(row, tok);
-    if (rv >= 0)
-      buf.v[t].load(a.v + (size_t)rv * D + DPL * x);
-    else
-      buf.v[t].zero();
+    sb.v[t].load(a.v + (size_t)max(rv[t], 0) * D + DPL * x);
+    vok |= (rv[t] >= 0 ? 1u : 0u) << t;
   }
+  sb.vok = vok;
 }
 
 template <int D, int QT>
 __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
   constexpr int DPL = D / 16;   // dims per lane per token in the V^T operand
   constexpr int KS = D / 32;    // k-steps of the QK^T product
+  constexpr int QLD = D + 8;    // LDS row stride of Q in bf16 (pads bank conflicts away)
+  constexpr int kPer = 4 * DPL + 2;                       // merge floats per lane per q-tile
+  constexpr size_t kQBytes = (size_t)QT * 16 * QLD * 2;
+  constexpr size_t kMetaBytes = sizeof(WaveMeta) * kWaves;
+  constexpr size_t kMergeBytes = (size_t)(kWaves - 1) * QT * kPer * 64 * 4;
+  constexpr size_t kLoopBytes = kQBytes + kMetaBytes;
+  constexpr size_t kSmem = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmem];
+  uint16_t* s_q = reinterpret_cast<uint16_t*>(smem_raw);
+  WaveMeta* s_meta = reinterpret_cast<WaveMeta*>(smem_raw + kQBytes);
+  float* s_merge = reinterpret_cast<float*>(smem_raw);
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -230,10 +307,30 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
   const int b = blockIdx.z;
   const int r0 = rc * kMaxRowsPerWG;
   const int nrows = min(kMaxRowsPerWG, a.rows - r0);
+  WaveMeta& wm = s_meta[wave];
+
+  // Q rows of this workgroup -> LDS (rows past nrows are zero)
+  for (int e = tid; e < QT * 16 * (D / 8); e += 256) {
+    const int r = e / (D / 8);
+    const int c = e - r * (D / 8);
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (r < nrows) {
+      const int rr = r0 + r;
+      const int i = rr / a.G;
+      const int h = g * a.G + (rr - i * a.G);
+      v = *reinterpret_cast<const u32x4*>(a.q + ((size_t)(b * a.n_q + i) * a.Hq + h) * D + 8 * c);
+    }
+    *reinterpret_cast<u32x4*>(s_q + r * QLD + 8 * c) = v;
+  }
 
   const SeqInfo si = seq_info(a, b, g);
   const int st0 = s * a.sps;
   const int st1 = (s == a.n_split - 1) ? si.T : min(si.T, st0 + a.sps);
+  // contiguous per-wave step ranges
+  const int nst = max(st1 - st0, 0);
+  const int qw = (nst + kWaves - 1) / kWaves;
+  const int w0 = st0 + wave * qw;
+  const int w1 = min(st1, w0 + qw);
 
   // Column mask of verifier/tail slot `lane`: bit i = row i sees that slot.
   uint64_t colmask;
@@ -245,31 +342,14 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     colmask = (a.mode == MODE_DENSE) ? (kAll << lane) : kAll;
   }
 
-  uint64_t rowbit[QT];
-  u32x4 qop[QT][KS];
-  float* lgp[QT][2];
+  // verifier row index of this lane's q-row in each tile (64 = padding row)
+  int rowi[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int r = 16 * qt + x;
-    rowbit[qt] = 0;
-    lgp[qt][0] = lgp[qt][1] = nullptr;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qop[qt][ks] = u32x4{0, 0, 0, 0};
-    if (r < nrows) {
-      const int rr = r0 + r;
-      const int i = rr / a.G;
-      const int h = g * a.G + (rr - i * a.G);
-      rowbit[qt] = 1ull << i;
-      const uint16_t* qp = a.q + ((size_t)(b * a.n_q + i) * a.Hq + h) * D + 8 * j;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qop[qt][ks] = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
-      if (a.mode == MODE_DENSE && a.logits != nullptr) {
-        float* base = a.logits + (size_t)(b * a.Hq + h) * 2 * a.logits_ld;
-        if (i == a.c0) lgp[qt][0] = base;
-        if (i == a.c1) lgp[qt][1] = base + a.logits_ld;
-      }
-    }
+    rowi[qt] = (r < nrows) ? (r0 + r) / a.G : 64;
   }
+  const bool collect = a.mode == MODE_DENSE && a.logits != nullptr;
 
   float m[QT], l[QT];
   f32x4 O[QT][DPL];
@@ -280,115 +360,138 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) O[qt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  __syncthreads();   // Q in LDS
 
-  int step = st0 + wave;
-  StepBuf<D, KS, DPL> cur;
-  int row_c = -1;
-  uint64_t vis_c = 0;
-  if (step < st1) {
-    step_meta(a, si, b, g, step, colmask, lane, row_c, vis_c);
-    step_load<D, KS, DPL>(a, row_c, x, j, cur);
-  }
-  for (; step < st1; step += kWaves) {
-    // issue the next step's loads before consuming this one
-    const int nstep = step + kWaves;
-    StepBuf<D, KS, DPL> nxt;
-    int row_n = -1;
-    uint64_t vis_n = 0;
-    if (nstep < st1) {
-      step_meta(a, si, b, g, nstep, colmask, lane, row_n, vis_n);
-      step_load<D, KS, DPL>(a, row_n, x, j, nxt);
-    }
-
-    // ---- S^T = K Q^T for two 16-token tiles
-    f32x4 S[2][QT];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma16(cur.k[tt][ks], qop[qt][ks], acc);
-        S[tt][qt] = acc;
-      }
-
-    // ---- visibility of the 8 tokens this lane holds (tokens 16tt + 4j + i)
-    const bool full = __all(row_c >= 0 && vis_c == kAll);
-    uint64_t vt[2][4];
-    if (!full) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vt[tt][i] = shfl64(vis_c, 16 * tt + 4 * j + i);
-    }
-
-    // ---- V^T operands: transpose 8 tokens x DPL dims per lane
-    u32x4 VT[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e)
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        VT[e][w] = velem<DPL>(cur.v[2 * w], e) | (velem<DPL>(cur.v[2 * w + 1], e) << 16);
-
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float t8[8];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sv = S[tt][qt][i] * a.scale_log2;
-          if (!full && (vt[tt][i] & rowbit[qt]) == 0) sv = -INFINITY;
-          t8[4 * tt + i] = sv;
+  if (w0 < w1) {
+    MetaStage ms;
+    meta_stage_a(a, si, w0, w1, lane, ms);
+    meta_stage_b(a, b, ms);
+    meta_stage_c(a, g, colmask, lane, ms, wm, 0);
+    StepBuf<D, KS, DPL> cur;
+    step_load<D, KS, DPL>(a, wm, 0, 0, x, j, cur);
+    for (int wb = w0, k = 0; wb < w1; wb += kMW, ++k) {
+      const int buf = k & 1;
+      const bool next_win = wb + kMW < w1;
+      const int nloc = min(kMW, w1 - wb);
+      for (int ls = 0; ls < nloc; ++ls) {
+        const int step = wb + ls;
+        if (next_win) {
+          if (ls == 0) meta_stage_a(a, si, wb + kMW, w1, lane, ms);
+          if (ls == 1) meta_stage_b(a, b, ms);
+          if (ls == 2) meta_stage_c(a, g, colmask, lane, ms, wm, buf ^ 1);
         }
-      // Collect-2-Query: scaled logits of the two collected rows, prefix columns only
+        // next step's loads go out before this step is consumed (the last step re-reads itself)
+        StepBuf<D, KS, DPL> nxt;
+        {
+          int nb = buf, nls = ls + 1;
+          if (nls == kMW) { nb = buf ^ 1; nls = 0; }
+          if (step + 1 >= w1) { nb = buf; nls = ls; }
+          step_load<D, KS, DPL>(a, wm, nb, nls, x, j, nxt);
+        }
+
+        // ---- S^T = K Q^T for two 16-token tiles (Q^T operand from LDS)
+        f32x4 S[2][QT];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float* dst = lgp[qt][c];
-        if (dst != nullptr) {
+        for (int qt = 0; qt < QT; ++qt) {
+          S[0][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          S[1][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int p0 = step * kStepTokens + 16 * tt + 4 * j;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (p0 + i < si.L) dst[p0 + i] = S[tt][qt][i] * a.scale;
+          for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 qop = *reinterpret_cast<const u32x4*>(s_q + (16 * qt + x) * QLD + 32 * ks + 8 * j);
+            S[0][qt] = mfma16(cur.k[0][ks], qop, S[0][qt]);
+            S[1][qt] = mfma16(cur.k[1][ks], qop, S[1][qt]);
           }
         }
-      }
-      float rmax = t8[0];
+
+        // ---- visibility of the 8 tokens this lane holds (tokens 16tt + 4j + i)
+        const bool full = wm.full[buf][ls] != 0;
+        uint64_t vt[2][4];
+        if (!full) {
+          const uint64_t* vr = wm.vis[buf] + ls * kStepTokens;
 #pragma unroll
-      for (int u = 1; u < 8; ++u) rmax = fmaxf(rmax, t8[u]);
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-      const float mnew = fmaxf(m[qt], rmax);
-      const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m[qt] - msafe);
-      m[qt] = mnew;
-      float psum = 0.f;
-      u32x4 phi, plo;
+          for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int u = 0; u < 8; u += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(t8[u] - msafe);
-        const float p1 = __builtin_amdgcn_exp2f(t8[u + 1] - msafe);
-        psum += p0 + p1;
-        const uint32_t h0 = bf16_rne(p0), h1 = bf16_rne(p1);
-        const uint32_t l0 = bf16_rne(p0 - bf16_to_f32(h0));
-        const uint32_t l1 = bf16_rne(p1 - bf16_to_f32(h1));
-        phi[u >> 1] = h0 | (h1 << 16);
-        plo[u >> 1] = l0 | (l1 << 16);
-      }
-      l[qt] = l[qt] * alpha + psum;
+            for (int i = 0; i < 4; ++i) vt[tt][i] = vr[16 * tt + 4 * j + i];
+        }
+
+        // ---- online softmax per q-tile; P as bf16 hi + lo B-operands
+        u32x4 phi[QT], plo[QT];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        O[qt][e] *= alpha;
-        O[qt][e] = mfma16(VT[e], phi, O[qt][e]);
-        O[qt][e] = mfma16(VT[e], plo, O[qt][e]);
+        for (int qt = 0; qt < QT; ++qt) {
+          float t8[8];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float sv = S[tt][qt][i] * a.scale_log2;
+              if (!full && ((vt[tt][i] >> rowi[qt]) & 1ull) == 0) sv = -INFINITY;
+              t8[4 * tt + i] = sv;
+            }
+          // Collect-2-Query: scaled logits of the two collected rows, prefix columns only
+          if (collect && (rowi[qt] == a.c0 || rowi[qt] == a.c1)) {
+            const int rr = r0 + 16 * qt + x;
+            const int h = g * a.G + (rr - rowi[qt] * a.G);
+            float* base = a.logits + (size_t)(b * a.Hq + h) * 2 * a.logits_ld;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              if (rowi[qt] != (c == 0 ? a.c0 : a.c1)) continue;
+              float* dst = base + c * a.logits_ld;
+#pragma unroll
+              for (int tt = 0; tt < 2; ++tt) {
+                const int p0 = step * kStepTokens + 16 * tt + 4 * j;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (p0 + i < si.L) dst[p0 + i] = S[tt][qt][i] * a.scale;
+              }
+            }
+          }
+          float rmax = t8[0];
+#pragma unroll
+          for (int u = 1; u < 8; ++u) rmax = fmaxf(rmax, t8[u]);
+          rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+          rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+          const float mnew = fmaxf(m[qt], rmax);
+          const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
+          const float alpha = __builtin_amdgcn_exp2f(m[qt] - msafe);
+          m[qt] = mnew;
+          float psum = 0.f;
+#pragma unroll
+          for (int u = 0; u < 8; u += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(t8[u] - msafe);
+            const float p1 = __builtin_amdgcn_exp2f(t8[u + 1] - msafe);
+            psum += p0 + p1;
+            const uint32_t h0 = bf16_rne(p0), h1 = bf16_rne(p1);
+            const uint32_t l0 = bf16_rne(p0 - bf16_to_f32(h0));
+            const uint32_t l1 = bf16_rne(p1 - bf16_to_f32(h1));
+            phi[qt][u >> 1] = h0 | (h1 << 16);
+            plo[qt][u >> 1] = l0 | (l1 << 16);
+          }
+          l[qt] = l[qt] * alpha + psum;
+          if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) O[qt][e] *= alpha;
+          }
+        }
+
+        // ---- O^T += V^T P^T, one transposed V tile at a time
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+          u32x4 vte;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = (cur.vok >> (2 * w)) & 1u ? velem<DPL>(cur.v[2 * w], e) : 0u;
+            const uint32_t hi = (cur.vok >> (2 * w + 1)) & 1u ? velem<DPL>(cur.v[2 * w + 1], e) : 0u;
+            vte[w] = lo | (hi << 16);
+          }
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            O[qt][e] = mfma16(vte, phi[qt], O[qt][e]);
+            O[qt][e] = mfma16(vte, plo[qt], O[qt][e]);
+          }
+        }
+        cur = nxt;
       }
     }
-
-    cur = nxt;
-    row_c = row_n;
-    vis_c = vis_n;
   }
 
   // full row sums (fixed order)
@@ -399,10 +502,9 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
   }
 
   // ---- merge the 4 waves' states through LDS in wave order 0,1,2,3
-  constexpr int kPer = 4 * DPL + 2;   // floats per lane per q-tile
-  __shared__ float smem[(kWaves - 1) * QT * kPer * 64];
+  __syncthreads();   // every wave is done with Q and its metadata ring
   if (wave > 0) {
-    float* w = smem + (size_t)(wave - 1) * QT * kPer * 64;
+    float* w = s_merge + (size_t)(wave - 1) * QT * kPer * 64;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
@@ -416,7 +518,7 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
   __syncthreads();
   if (wave != 0) return;
   for (int ow = 1; ow < kWaves; ++ow) {
-    const float* w = smem + (size_t)(ow - 1) * QT * kPer * 64;
+    const float* w = s_merge + (size_t)(ow - 1) * QT * kPer * 64;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float mb = w[(qt * kPer + 4 * DPL) * 64 + lane];
@@ -476,53 +578,83 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge split-K partials of one (b, g, row chunk) in split order.
+// Merge split-K partials in split order.  One wave per q-row: lane s first loads the
+// (m, l) of split s, so the per-split loads are issued together rather than one
+// after another; then every lane accumulates its columns over the splits.
+constexpr int kCombineRows = 4;
+
 template <int D>
 __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
-  const int pid = blockIdx.x;
+  const int pid = blockIdx.x;                   // (b*Hkv + g)*n_rc + rc
   const int rc = pid % a.n_rc;
   const int bg = pid / a.n_rc;
   const int g = bg % a.Hkv;
   const int b = bg / a.Hkv;
   const int r0 = rc * kMaxRowsPerWG;
   const int nrows = min(kMaxRowsPerWG, a.rows - r0);
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.y * kCombineRows + (threadIdx.x >> 6);
+  if (r >= nrows) return;
   const size_t pstride = (size_t)kMaxRowsPerWG * (D + 2);
   const float* base = a.part + (size_t)pid * a.n_split * pstride;
-  __shared__ float wsh[kMaxSplits][kMaxRowsPerWG];
-  __shared__ float inv[kMaxRowsPerWG];
-  const int tid = threadIdx.x;
-  if (tid < nrows) {
-    float M = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, base[s * pstride + kMaxRowsPerWG * D + tid]);
-    const float Ms = (M == -INFINITY) ? 0.f : M;
-    float Ls = 0.f;
-    for (int s = 0; s < a.n_split; ++s) {
-      const float ms = base[s * pstride + kMaxRowsPerWG * D + tid];
-      const float ws = __builtin_amdgcn_exp2f(ms - Ms);
-      wsh[s][tid] = ws;
-      Ls += ws * base[s * pstride + kMaxRowsPerWG * D + kMaxRowsPerWG + tid];
-    }
-    inv[tid] = (Ls > 0.f) ? 1.f / Ls : 0.f;
-    if (a.lse != nullptr) {
-      const int rr = r0 + tid;
-      const int i = rr / a.G;
-      const int h = g * a.G + (rr - i * a.G);
-      a.lse[(size_t)(b * a.n_q + i) * a.Hq + h] = (Ls > 0.f) ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
-    }
+  const float* mcol = base + (size_t)kMaxRowsPerWG * D + r;
+  // splits are at most kMaxSplits = 128: two per lane
+  float mv[2], lv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int sp = lane + 64 * u;
+    mv[u] = (sp < a.n_split) ? mcol[sp * pstride] : -INFINITY;
+    lv[u] = (sp < a.n_split) ? mcol[sp * pstride + kMaxRowsPerWG] : 0.f;
   }
-  __syncthreads();
-  constexpr int C4 = D / 4;
-  for (int item = tid; item < nrows * C4; item += blockDim.x) {
-    const int r = item / C4;
-    const int c = item - r * C4;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.n_split; ++s)
-      acc += wsh[s][r] * *reinterpret_cast<const f32x4*>(base + s * pstride + (size_t)r * D + 4 * c);
-    const int rr = r0 + r;
-    const int i = rr / a.G;
-    const int h = g * a.G + (rr - i * a.G);
-    *reinterpret_cast<f32x4*>(a.out + ((size_t)(b * a.n_q + i) * a.Hq + h) * D + 4 * c) = acc * inv[r];
+  float M = fmaxf(mv[0], mv[1]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float Ms = (M == -INFINITY) ? 0.f : M;
+  float wv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) wv[u] = __builtin_amdgcn_exp2f(mv[u] - Ms);
+  // L = sum over splits in split order: gather the weighted l's to lane 0's order via LDS
+  __shared__ float s_w[kCombineRows][kMaxSplits];
+  __shared__ float s_l[kCombineRows][kMaxSplits];
+  const int wr = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    s_w[wr][lane + 64 * u] = wv[u];
+    s_l[wr][lane + 64 * u] = wv[u] * lv[u];
   }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  float Ls = 0.f;
+  for (int sp = 0; sp < a.n_split; ++sp) Ls += s_l[wr][sp];
+  constexpr int CPL = D / 64;                   // columns per lane (2 or 1)
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  const float* ocol = base + (size_t)r * D + CPL * lane;
+  int sp = 0;
+  for (; sp + 4 <= a.n_split; sp += 4) {
+    float ov[4][CPL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ov[u][c] = ocol[(sp + u) * pstride + c];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] += s_w[wr][sp + u] * ov[u][c];
+  }
+  for (; sp < a.n_split; ++sp)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] += s_w[wr][sp] * ocol[sp * pstride + c];
+  const float inv = (Ls > 0.f) ? 1.f / Ls : 0.f;
+  const int rr = r0 + r;
+  const int i = rr / a.G;
+  const int h = g * a.G + (rr - i * a.G);
+  float* op = a.out + ((size_t)(b * a.n_q + i) * a.Hq + h) * D + CPL * lane;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) op[c] = acc[c] * inv;
+  if (lane == 0 && a.lse != nullptr)
+    a.lse[(size_t)(b * a.n_q + i) * a.Hq + h] = (Ls > 0.f) ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 // Union of the n_q rows' block lists of one (b, g), ascending, with per-block row masks
@@ -594,7 +726,9 @@ hipError_t launch_main(const AttnPlan& p, const AttnArgs& a, hipStream_t stream)
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(a.B * a.Hkv * p.n_rc), dim3(256), 0, stream, a);
+  const int rows_wg = p.rows < kMaxRowsPerWG ? p.rows : kMaxRowsPerWG;
+  hipLaunchKernelGGL((combine_kernel<D>), dim3(a.B * a.Hkv * p.n_rc, (rows_wg + kCombineRows - 1) / kCombineRows),
+                     dim3(64 * kCombineRows), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -631,6 +765,11 @@ AttnPlan attn_plan(int32_t mode, int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv
   if (ns > ns_cap) ns = ns_cap;
   if (ns > kMaxSplits) ns = kMaxSplits;
   if (ns < 1) ns = 1;
+  // one workgroup per CU at a time: fill whole rounds of the 256 CUs
+  if (pairs * ns > kNumCUs) {
+    const long long whole = (pairs * ns) / kNumCUs * kNumCUs / pairs;
+    if (whole >= 1) ns = whole;
+  }
   p.n_split = (int32_t)ns;
   p.sps = (int32_t)((T + ns - 1) / ns);
   p.part_bytes = (p.n_split > 1) ? align_up((size_t)pairs * p.n_split * kMaxRowsPerWG * (d + 2) * 4, 256) : 0;

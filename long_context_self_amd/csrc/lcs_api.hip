@@ -131,7 +131,7 @@ lcs_status lcs_verify_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int
 size_t lcs_select_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, lcs_set_mode mode,
                                   int32_t max_prefix_len, int32_t block_size) {
   if (B < 0 || Hkv < 1 || Hq < 1 || max_prefix_len < 0) return 0;
-  if (mode == LCS_SET_BLOCK && (!is_pow2(block_size) || block_size < 4 || block_size > 4096)) return 0;
+  if (mode == LCS_SET_BLOCK && (!is_pow2(block_size) || block_size < 4 || block_size > lcs::kScorePos)) return 0;
   return lcs::select_plan(B, Hq, Hkv, (int32_t)mode, max_prefix_len, block_size).total_bytes;
 }
 
@@ -156,8 +156,8 @@ lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, in
                                               (long long)logits_ld, max_prefix_len);
   long long items = max_prefix_len, need;
   if (mode == LCS_SET_BLOCK) {
-    if (!is_pow2(block_size) || block_size < 4 || block_size > 4096)
-      return fail(LCS_E_UNSUPPORTED, "block_size %d is not a power of two in [4, 4096]", block_size);
+    if (!is_pow2(block_size) || block_size < 4 || block_size > lcs::kScorePos)
+      return fail(LCS_E_UNSUPPORTED, "block_size %d is not a power of two in [4, %d]", block_size, lcs::kScorePos);
     items = (max_prefix_len + block_size - 1) / block_size;
     need = (n_sink + block_size - 1) / block_size + (long long)top_k + (n_recent + block_size - 1) / block_size + 1;
   } else {

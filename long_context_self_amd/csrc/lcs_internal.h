@@ -23,6 +23,7 @@ constexpr int kWaves = 4;         // waves per workgroup (one token stream each)
 constexpr int kMaxRowsPerWG = 64; // q-rows (n_q * G) handled by one workgroup
 constexpr int kMaxSplits = 128;   // split-K partials per (sequence, KV head, row chunk)
 constexpr int kTargetWGs = 1024;  // launch size the split policy aims for
+constexpr int kNumCUs = 256;      // MI355X compute units
 
 struct AttnArgs {
   const uint16_t* k;
@@ -78,8 +79,10 @@ hipError_t attn_launch(const AttnPlan& plan, AttnArgs args, void* workspace, hip
 // ---------------------------------------------------------------------------
 enum SelMode : int32_t { LCS_SEL_SHARED = 0, LCS_SEL_PER_HEAD = 1, LCS_SEL_BLOCK = 2 };
 
-constexpr int kSelChunk = 4096;   // items per workgroup in the streaming passes
-constexpr int kHistBins = 4096;   // first radix digit: top 12 bits of the key
+constexpr int kScorePos = 512;         // positions per workgroup of the score pass
+constexpr int kItemChunk = 1024;       // items per workgroup of the collect and emit passes
+constexpr int kMaxItemChunks = 16384;  // items < 2^24
+constexpr int kHistBins = 4096;        // first radix digit: top 12 bits of the key
 
 struct SelArgs {
   const float* logits;

@@ -71,91 +71,93 @@ __device__ __forceinline__ Win window(const SelArgs& a, int b) {
   return w;
 }
 
+// Block-wide exclusive prefix sum over NT threads (NT a multiple of 64).
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wave[w] = x;
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const uint32_t t = s_wave[i];
+    pre += (i < w) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + x - v;
+}
+
 __global__ void zero_kernel(SelArgs a, int NS) {
   const int n = NS * kHistBins;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) a.hist[i] = 0;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < NS; i += gridDim.x * blockDim.x) a.cand_count[i] = 0;
 }
 
+// sigma, keys and the first-digit histogram for kScorePos positions of one set.
 __global__ void __launch_bounds__(256) score_kernel(SelArgs a) {
   const int set = blockIdx.y;
   const int b = set / a.n_sets;
   const int s = set - b * a.n_sets;
   const Win w = window(a, b);
   if (w.all || a.top_k == 0) return;
-  const int p0 = blockIdx.x * kSelChunk;
+  const int p0 = blockIdx.x * kScorePos;
   if (p0 >= w.L) return;
   const int tid = threadIdx.x;
   const int h0 = (a.mode == LCS_SEL_SHARED) ? 0 : s * a.G;
   const int nh = (a.mode == LCS_SEL_SHARED) ? a.Hq : a.G;
 
   __shared__ uint32_t lh[kHistBins];
-  __shared__ uint32_t bm[kSelChunk / 4];
+  __shared__ uint32_t bm[kScorePos / 4];
   for (int i = tid; i < kHistBins; i += 256) lh[i] = 0;
   if (a.mode == LCS_SEL_BLOCK)
-    for (int i = tid; i < kSelChunk / 4; i += 256) bm[i] = 0;
+    for (int i = tid; i < kScorePos / 4; i += 256) bm[i] = 0;
   __syncthreads();
 
-  // sigma for positions p0 + it*1024 + 4*tid + [0, 4)
-  f32x4 acc[4];
-#pragma unroll
-  for (int it = 0; it < 4; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int p = p0 + 2 * tid;          // this thread's two positions
+  float acc0 = 0.f, acc1 = 0.f;
   const float* base = a.logits + (size_t)b * a.Hq * 2 * a.ld;
-  const bool fast = a.vec4 && (p0 + kSelChunk <= w.L);
-  if (fast) {
-#pragma unroll 4
+  if (a.vec4 && p + 1 < w.L) {
+#pragma unroll 8
     for (int hh = 0; hh < nh; ++hh) {
-      const float* r0 = base + (size_t)(h0 + hh) * 2 * a.ld + p0 + 4 * tid;
-      const float* r1 = r0 + a.ld;
-      f32x4 x0[4], x1[4];
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        x0[it] = *reinterpret_cast<const f32x4*>(r0 + it * 1024);
-        x1[it] = *reinterpret_cast<const f32x4*>(r1 + it * 1024);
-      }
-#pragma unroll
-      for (int it = 0; it < 4; ++it) acc[it] = acc[it] + (x0[it] + x1[it]);
+      const float* r0 = base + (size_t)(h0 + hh) * 2 * a.ld + p;
+      const float2 x0 = *reinterpret_cast<const float2*>(r0);
+      const float2 x1 = *reinterpret_cast<const float2*>(r0 + a.ld);
+      acc0 = acc0 + (x0.x + x1.x);
+      acc1 = acc1 + (x0.y + x1.y);
     }
-  } else {
+  } else if (p < w.L) {
     for (int hh = 0; hh < nh; ++hh) {
-      const float* r0 = base + (size_t)(h0 + hh) * 2 * a.ld;
-      const float* r1 = r0 + a.ld;
-#pragma unroll
-      for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int p = p0 + it * 1024 + 4 * tid + k;
-          if (p < w.L) acc[it][k] = acc[it][k] + (r0[p] + r1[p]);
-        }
+      const float* r0 = base + (size_t)(h0 + hh) * 2 * a.ld + p;
+      acc0 = acc0 + (r0[0] + r0[a.ld]);
+      if (p + 1 < w.L) acc1 = acc1 + (r0[1] + r0[a.ld + 1]);
     }
   }
-
+  const uint32_t k0 = f2key(acc0), k1 = f2key(acc1);
   uint32_t* keys = a.keys + (size_t)set * a.item_cap;
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int p = p0 + it * 1024 + 4 * tid;
-    uint32_t kk[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) kk[k] = f2key(acc[it][k]);
-    if (a.mode != LCS_SEL_BLOCK) {
-      if (p + 3 < w.L) {
-        *reinterpret_cast<u32x4*>(keys + p) = u32x4{kk[0], kk[1], kk[2], kk[3]};
-      } else {
-        for (int k = 0; k < 4; ++k)
-          if (p + k < w.L) keys[p + k] = kk[k];
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (p + k >= w.lo && p + k < w.hi) atomicAdd(&lh[kk[k] >> 20], 1u);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (p + k < w.L) atomicMax(&bm[(it * 1024 + 4 * tid + k) >> a.lg_bs], kk[k]);
+  if (a.mode != LCS_SEL_BLOCK) {
+    if (p + 1 < w.L) {
+      *reinterpret_cast<uint2*>(keys + p) = make_uint2(k0, k1);
+    } else if (p < w.L) {
+      keys[p] = k0;
     }
+    if (p >= w.lo && p < w.hi) atomicAdd(&lh[k0 >> 20], 1u);
+    if (p + 1 >= w.lo && p + 1 < w.hi) atomicAdd(&lh[k1 >> 20], 1u);
+  } else {
+    if (p < w.L) atomicMax(&bm[(2 * tid) >> a.lg_bs], k0);
+    if (p + 1 < w.L) atomicMax(&bm[(2 * tid + 1) >> a.lg_bs], k1);
   }
   __syncthreads();
   if (a.mode == LCS_SEL_BLOCK) {
-    const int nbc = kSelChunk >> a.lg_bs;
+    const int nbc = kScorePos >> a.lg_bs;
     const int c0 = p0 >> a.lg_bs;
     for (int cl = tid; cl < nbc; cl += 256) {
       const int c = c0 + cl;
@@ -171,38 +173,33 @@ __global__ void __launch_bounds__(256) score_kernel(SelArgs a) {
     if (lh[i]) atomicAdd(&gh[i], lh[i]);
 }
 
-// Threshold bin of set `set` from its histogram: the bin holding the k-th largest item.
-__device__ void find_bin(const SelArgs& a, int set, uint32_t* ts, int& bin_out, uint32_t& above_out,
-                         int* sh_bin, uint32_t* sh_above) {
+// Threshold bin of a set from its histogram: the bin holding the k-th largest item.
+__device__ void find_bin(const SelArgs& a, int set, uint32_t* s_wave, int* sh_bin, uint32_t* sh_above) {
   const int tid = threadIdx.x;
   const uint32_t* h = a.hist + (size_t)set * kHistBins;
+  uint32_t hv[16];
   uint32_t c = 0;
-  for (int e = 0; e < 16; ++e) c += h[16 * tid + e];
-  // inclusive scan from the top: ts[t] = sum over threads t' >= t
-  ts[tid] = c;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t v = (tid + off < 256) ? ts[tid + off] : 0;
-    __syncthreads();
-    ts[tid] += v;
-    __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    hv[e] = h[16 * tid + e];
+    c += hv[e];
   }
+  uint32_t total;
+  const uint32_t excl = block_excl_scan<256>(c, s_wave, total);
   const uint32_t K = (uint32_t)a.top_k;
-  const uint32_t above_t = ts[tid] - c;             // items in bins above this thread's range
+  const uint32_t above_t = total - excl - c;       // items in bins above this thread's range
   if (above_t < K && above_t + c >= K) {
     uint32_t cum = above_t;
-    for (int bin = 16 * tid + 15; bin >= 16 * tid; --bin) {
-      if (cum + h[bin] >= K) {
-        *sh_bin = bin;
+    for (int e = 15; e >= 0; --e) {
+      if (cum + hv[e] >= K) {
+        *sh_bin = 16 * tid + e;
         *sh_above = cum;
         break;
       }
-      cum += h[bin];
+      cum += hv[e];
     }
   }
   __syncthreads();
-  bin_out = *sh_bin;
-  above_out = *sh_above;
 }
 
 __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
@@ -211,10 +208,10 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
   const Win w = window(a, b);
   if (w.all || a.top_k == 0) return;
   const int tid = threadIdx.x;
-  __shared__ uint32_t ts[256];
+  __shared__ uint32_t s_wave[4];
   __shared__ int sh_bin;
   __shared__ uint32_t sh_above;
-  __shared__ uint64_t lq[kSelChunk];
+  __shared__ uint64_t lq[kItemChunk];
   __shared__ uint32_t lqn, lqbase, nab;
   if (tid == 0) {
     sh_bin = 0;
@@ -223,25 +220,27 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
     nab = 0;
   }
   __syncthreads();
-  int bin;
-  uint32_t above;
-  find_bin(a, set, ts, bin, above, &sh_bin, &sh_above);
+  find_bin(a, set, s_wave, &sh_bin, &sh_above);
+  const int bin = sh_bin;
   if (blockIdx.x == 0 && tid == 0) {
     a.thr[(size_t)set * 2 + 0] = (uint64_t)bin;
-    a.thr[(size_t)set * 2 + 1] = (uint64_t)above;
+    a.thr[(size_t)set * 2 + 1] = (uint64_t)sh_above;
   }
-  const int i0 = blockIdx.x * kSelChunk;
-  const int lo = max(w.lo, i0), hi = min(w.hi, i0 + kSelChunk);
+  const int i0 = blockIdx.x * kItemChunk;
   const uint32_t* keys = a.keys + (size_t)set * a.item_cap;
   uint32_t my_above = 0;
-  for (int it = lo + tid; it < hi; it += 256) {
-    const uint32_t key = keys[it];
-    const int dg = (int)(key >> 20);
-    if (dg > bin) {
-      ++my_above;
-    } else if (dg == bin) {
-      const uint32_t slot = atomicAdd(&lqn, 1u);
-      lq[slot] = composite(key, it);
+#pragma unroll
+  for (int e = 0; e < kItemChunk / 256; ++e) {
+    const int it = i0 + e * 256 + tid;
+    if (it >= w.lo && it < w.hi) {
+      const uint32_t key = keys[it];
+      const int dg = (int)(key >> 20);
+      if (dg > bin) {
+        ++my_above;
+      } else if (dg == bin) {
+        const uint32_t slot = atomicAdd(&lqn, 1u);
+        lq[slot] = composite(key, it);
+      }
     }
   }
   atomicAdd(&nab, my_above);
@@ -263,63 +262,79 @@ __global__ void __launch_bounds__(1024) finalize_kernel(SelArgs a) {
   if (w.all || a.top_k == 0) return;
   const int tid = threadIdx.x;
   __shared__ uint32_t hist[2048];
-  __shared__ uint32_t cc[kHistBins];
-  __shared__ uint64_t sh_prefix, sh_mask;
+  __shared__ uint32_t cc[kMaxItemChunks];
+  __shared__ uint32_t s_wave[16];
+  __shared__ uint64_t sh_prefix;
   __shared__ uint32_t sh_rem;
   const uint32_t above = (uint32_t)a.thr[(size_t)set * 2 + 1];
-  const uint32_t need = (uint32_t)a.top_k - above;
   const int n_c = min((int)a.cand_count[set], a.item_cap);
   const uint64_t* cand = a.cand + (size_t)set * a.item_cap;
   if (tid == 0) {
     sh_prefix = 0;
-    sh_mask = 0;
-    sh_rem = need;
+    sh_rem = (uint32_t)a.top_k - above;
   }
-  __syncthreads();
+  uint64_t mask = 0;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 33 - 11 * pass;
-    for (int i = tid; i < 2048; i += 1024) hist[i] = 0;
+    hist[tid] = 0;
+    hist[tid + 1024] = 0;
     __syncthreads();
-    const uint64_t prefix = sh_prefix, mask = sh_mask;
+    const uint64_t prefix = sh_prefix;
+    const uint32_t rem = sh_rem;
     for (int e = tid; e < n_c; e += 1024) {
       const uint64_t c = cand[e];
       if ((c & mask) == prefix) atomicAdd(&hist[(c >> shift) & 2047u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t rem = sh_rem;
-      int d = 2047;
-      for (; d > 0; --d) {
-        if (hist[d] >= rem) break;
-        rem -= hist[d];
+    // the digit holding the rem-th largest remaining composite (suffix sums over bins)
+    const uint32_t hl = hist[2 * tid], hh = hist[2 * tid + 1];
+    const uint32_t c = hl + hh;
+    uint32_t total;
+    const uint32_t excl = block_excl_scan<1024>(c, s_wave, total);
+    const uint32_t above_t = total - excl - c;
+    if (above_t < rem && above_t + c >= rem) {
+      if (above_t + hh >= rem) {
+        sh_prefix = prefix | ((uint64_t)(2 * tid + 1) << shift);
+        sh_rem = rem - above_t;
+      } else {
+        sh_prefix = prefix | ((uint64_t)(2 * tid) << shift);
+        sh_rem = rem - above_t - hh;
       }
-      sh_rem = rem;
-      sh_prefix = prefix | ((uint64_t)d << shift);
-      sh_mask = mask | ((uint64_t)2047u << shift);
     }
+    mask |= (uint64_t)2047u << shift;
     __syncthreads();
   }
   const uint64_t cstar = sh_prefix;
-  // per-chunk kept counts -> exclusive offsets (after the sink window)
+  // per-chunk kept counts -> exclusive offsets after the sink window
   for (int c = tid; c < a.n_chunks; c += 1024) cc[c] = a.chunk_above[(size_t)set * a.n_chunks + c];
   __syncthreads();
   for (int e = tid; e < n_c; e += 1024) {
     const uint64_t c = cand[e];
     if (c >= cstar) {
       const int item = (int)(kItemMask - (uint32_t)(c & kItemMask));
-      atomicAdd(&cc[item / kSelChunk], 1u);
+      atomicAdd(&cc[item / kItemChunk], 1u);
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t run = (uint32_t)w.lo;
-    uint32_t* off = a.chunk_off + (size_t)set * a.n_chunks;
-    for (int c = 0; c < a.n_chunks; ++c) {
-      off[c] = run;
-      run += cc[c];
-    }
-    a.thr[(size_t)set * 2 + 1] = cstar;
+  constexpr int per = kMaxItemChunks / 1024;
+  uint32_t loc[per];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int e = 0; e < per; ++e) {
+    const int c = per * tid + e;
+    loc[e] = (c < a.n_chunks) ? cc[c] : 0u;
+    sum += loc[e];
   }
+  uint32_t total;
+  uint32_t run = (uint32_t)w.lo + block_excl_scan<1024>(sum, s_wave, total);
+  uint32_t* off = a.chunk_off + (size_t)set * a.n_chunks;
+#pragma unroll
+  for (int e = 0; e < per; ++e) {
+    const int c = per * tid + e;
+    if (c < a.n_chunks) off[c] = run;
+    run += loc[e];
+  }
+  if (tid == 0) a.thr[(size_t)set * 2 + 1] = cstar;
 }
 
 __global__ void __launch_bounds__(256) emit_kernel(SelArgs a) {
@@ -327,10 +342,10 @@ __global__ void __launch_bounds__(256) emit_kernel(SelArgs a) {
   const int b = set / a.n_sets;
   const Win w = window(a, b);
   const int tid = threadIdx.x;
-  const int i0 = blockIdx.x * kSelChunk;
+  const int i0 = blockIdx.x * kItemChunk;
   int32_t* out = a.indices + (size_t)set * a.cap;
   if (w.all) {
-    for (int it = i0 + tid; it < min(w.n, i0 + kSelChunk); it += 256)
+    for (int it = i0 + tid; it < min(w.n, i0 + kItemChunk); it += 256)
       if (it < a.cap) out[it] = it;
     if (blockIdx.x == 0 && tid == 0) a.counts[set] = min(w.n, a.cap);
     return;
@@ -339,33 +354,28 @@ __global__ void __launch_bounds__(256) emit_kernel(SelArgs a) {
   const int bin = (K > 0) ? (int)a.thr[(size_t)set * 2 + 0] : 0;
   const uint64_t cstar = (K > 0) ? a.thr[(size_t)set * 2 + 1] : ~0ull;
   const uint32_t* keys = a.keys + (size_t)set * a.item_cap;
-  __shared__ uint32_t ts[256];
-  // thread t owns items [i0 + 16t, i0 + 16t + 16)
+  __shared__ uint32_t s_wave[4];
+  constexpr int IPT = kItemChunk / 256;       // items per thread, consecutive
   uint32_t flags = 0;
-  int cnt = 0;
-  for (int e = 0; e < 16; ++e) {
-    const int it = i0 + 16 * tid + e;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const int it = i0 + IPT * tid + e;
     if (it >= w.lo && it < w.hi && K > 0) {
       const uint32_t key = keys[it];
       const int dg = (int)(key >> 20);
-      const bool keep = dg > bin || (dg == bin && composite(key, it) >= cstar);
-      if (keep) {
+      if (dg > bin || (dg == bin && composite(key, it) >= cstar)) {
         flags |= 1u << e;
         ++cnt;
       }
     }
   }
-  ts[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t v = (tid >= off) ? ts[tid - off] : 0;
-    __syncthreads();
-    ts[tid] += v;
-    __syncthreads();
-  }
-  uint32_t pos = ((K > 0) ? a.chunk_off[(size_t)set * a.n_chunks + blockIdx.x] : (uint32_t)w.lo) + ts[tid] - cnt;
-  for (int e = 0; e < 16; ++e) {
-    const int it = i0 + 16 * tid + e;
+  uint32_t total;
+  uint32_t pos = ((K > 0) ? a.chunk_off[(size_t)set * a.n_chunks + blockIdx.x] : (uint32_t)w.lo) +
+                 block_excl_scan<256>(cnt, s_wave, total);
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const int it = i0 + IPT * tid + e;
     if (it >= w.n) break;
     if (it < w.lo) {
       if (it < a.cap) out[it] = it;
@@ -391,8 +401,8 @@ SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t ma
   if (mode == LCS_SEL_BLOCK) items = (max_len + block_size - 1) / block_size;
   if (items < 1) items = 1;
   p.item_cap = (int32_t)align_up((size_t)items, 4);
-  p.n_chunks = (int32_t)((items + kSelChunk - 1) / kSelChunk);
-  p.n_pos_chunks = (int32_t)(((long long)(max_len > 0 ? max_len : 1) + kSelChunk - 1) / kSelChunk);
+  p.n_chunks = (int32_t)((items + kItemChunk - 1) / kItemChunk);
+  p.n_pos_chunks = (int32_t)(((long long)(max_len > 0 ? max_len : 1) + kScorePos - 1) / kScorePos);
   p.keys_bytes = align_up(NS * p.item_cap * 4, 256);
   p.hist_bytes = align_up(NS * kHistBins * 4, 256);
   p.cc_bytes = align_up(NS * 4, 256);
