@@ -94,7 +94,7 @@ typedef struct {
  *  tree_mask    device uint64 [B][n_q] or NULL.  NULL: row i sees verifier
  *               slots j <= i (a chain).  Otherwise row i sees slot j iff bit j
  *               of tree_mask[b][i] is set.  Every row sees the whole prefix.
- *  scale        softmax scale (1/sqrt(d) in the pages' models).
+ *  scale        softmax scale, finite and > 0 (1/sqrt(d) in the pages' models).
  *  out          fp32 [B][n_q][Hq][d]: softmax(scale q K^T) V.
  *  logits       fp32 [B][Hq][2][logits_ld]: scale*q.k of the two collected rows
  *               for columns p < prefix_len[b]; other columns are untouched.

@@ -12,17 +12,24 @@
 //    verifier rows with different block sets load each shared block once; each row
 //    keeps its own selection and its own causal boundary (Figure 6 text).
 //
-// How (gfx950, wave64, MFMA)
+// How (gfx950, wave64, MFMA, LDS DMA)
 //  * One workgroup = 4 waves = one (sequence, KV head, row chunk, split).  Every
 //    q-row of the KV group (n_q verifier rows x G query heads) is a row of the MFMA
 //    tile, so each K/V byte fetched from HBM serves all G heads and all n_q rows.
-//  * A wave consumes 32 cache positions per step.  S^T = K Q^T runs on
-//    v_mfma_f32_16x16x32_bf16 with K rows loaded straight from global memory into
-//    the A-operand layout (lane = token, 8 contiguous dims); O^T = V^T P^T uses the
-//    V rows transposed in registers (8 tokens x 8 dims per lane, v_perm only) and
-//    P taken directly from the S^T accumulator layout, so no LDS is touched in the
-//    hot loop.  P is split into bf16 hi + lo parts so the PV product keeps ~16
-//    mantissa bits of the softmax weights.
+//  * A wave owns a contiguous run of 32-token steps.  Every byte it streams goes
+//    global -> LDS with global_load_lds_dwordx4 (K/V tiles) or _dword (index-list
+//    and block-table entries) into per-wave LDS slots, two steps ahead, with the
+//    vmcnt waits placed by hand.  No vector register waits on global memory inside
+//    the loop, so the wave keeps 32 KB in flight while it computes.
+//  * Each lane DMAs exactly the 16-byte pieces it later needs as MFMA operands:
+//    S^T = K Q^T on v_mfma_f32_16x16x32_bf16 takes K rows (lane = token, 8
+//    contiguous dims) as A; O^T = V^T P^T takes 8 tokens x 8 dims per lane,
+//    transposed in registers (v_perm), as A, and P straight from the S^T
+//    accumulator layout as B.  P is split into bf16 hi + lo parts so the PV product
+//    keeps ~16 mantissa bits of the softmax weights.  d = 64 uses the same operand
+//    layout with the upper half of the V^T rows idle.
+//  * Token metadata (row index, row-visibility mask) for a window of kMW steps is
+//    built one window ahead in three stages spread over three steps.
 //  * Online softmax in base 2 with the running max and sum per q-row kept in the
 //    lane that owns the row; the 4 waves' states are merged through LDS in a fixed
 //    order, and a split-K combine merges the workgroups' partials in a fixed order,
@@ -40,10 +47,12 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef void __attribute__((address_space(3)))* lptr_t;
 
 constexpr uint64_t kAll = ~0ull;
 constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kTau = 8.f;   // log2 headroom of the lazily updated softmax reference max
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -56,6 +65,16 @@ __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// max over the four lanes {l, l^16, l^32, l^48} (the 4 lane groups holding one MFMA
+// column) with gfx950 permlane swaps: VALU only, no LDS round trip.
+__device__ __forceinline__ float fmax2(float a, float b) { return a > b ? a : b; }
+__device__ __forceinline__ float colmax4(float v) {
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float a = fmax2(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return fmax2(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+}
+
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
@@ -64,37 +83,30 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) {
   return __builtin_bit_cast(float, h << 16);
 }
 
-// V rows: DPL dims per lane (8 for d = 128, 4 for d = 64).
-template <int DPL> struct VRow;
-template <> struct VRow<8> {
-  uint32_t w[4];
-  __device__ __forceinline__ void load(const uint16_t* p) {
-    u32x4 t = *reinterpret_cast<const u32x4*>(p);
-    w[0] = t[0]; w[1] = t[1]; w[2] = t[2]; w[3] = t[3];
-  }
-  __device__ __forceinline__ void zero() { w[0] = w[1] = w[2] = w[3] = 0; }
-};
-template <> struct VRow<4> {
-  uint32_t w[2];
-  __device__ __forceinline__ void load(const uint16_t* p) {
-    u32x2 t = *reinterpret_cast<const u32x2*>(p);
-    w[0] = t[0]; w[1] = t[1];
-  }
-  __device__ __forceinline__ void zero() { w[0] = w[1] = 0; }
-};
-
-// Element e (a bf16) of row r.
-template <int DPL>
-__device__ __forceinline__ uint32_t velem(const VRow<DPL>& r, int e) {
-  return (e & 1) ? (r.w[e >> 1] >> 16) : (r.w[e >> 1] & 0xffffu);
+// Global -> LDS DMA.  Issued through inline asm so that the compiler's wait-count
+// pass, which cannot tell which LDS bytes a DMA writes and would otherwise drain every
+// outstanding load before each LDS read, stays out of the pipeline: the waits for
+// these loads are placed by hand (wait_vm).  M0 carries the wave-uniform LDS base;
+// nothing else in these kernels uses M0.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lptr_t)p);
+}
+// 16 bytes per lane from src into LDS at dst + 16 * lane (dst wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr(dst))
+               : "memory", "m0");
+}
+// 4 bytes per lane from src into LDS at dst + 4 * lane (dst wave-uniform).
+__device__ __forceinline__ void dma4(const void* src, void* dst) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds_addr(dst))
+               : "memory", "m0");
 }
 
-template <int D, int KS, int DPL>
-struct StepBuf {
-  u32x4 k[2][KS];
-  VRow<DPL> v[8];
-  uint32_t vok;     // bit t set when V token t of this lane is a real cache row
-};
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 struct SeqInfo {
   int L, cnt, tb, tl, U, T;
@@ -104,16 +116,17 @@ struct SeqInfo {
 };
 
 // Sequence-level bounds for (b, g); every quantity read from device memory is clamped.
+template <int MODE>
 __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, int g) {
   SeqInfo si{};
   const int P = 1 << a.lg_page;
-  if (a.mode == MODE_DENSE) {
+  if (MODE == MODE_DENSE) {
     si.L = min(max(a.prefix_len[b], 0), a.max_prefix_len);
     si.T = (si.L + a.n_q + kStepTokens - 1) / kStepTokens;
   } else {
     si.tb = a.tail_begin[b];
     si.tl = max(a.tail_len[b], 0);
-    if (a.mode == MODE_BLOCK) {
+    if (MODE == MODE_BLOCK) {
       const size_t o = (size_t)(b * a.Hkv + g);
       si.U = min(max(a.ucount[o], 0), a.ucap);
       si.ub = a.ublk + o * a.ucap;
@@ -131,174 +144,201 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, int g) {
 }
 
 // ---------------------------------------------------------------------------
-// Token metadata.  A wave owns a contiguous range of 32-token steps.  For each
-// window of kMW steps it builds, one window ahead, the K/V row index and the
-// row-visibility mask of every token slot in a per-wave LDS ring, in three
-// stages spread over the first three steps of the previous window (positions
-// and index-list loads; block-table loads; rows, masks and flags to LDS).  No
-// global load therefore sits between a step and the issue of its data loads.
+// Token metadata.  For each window of kMW steps a wave builds, one window ahead,
+// the K/V row index and the row-visibility mask of every token slot in its LDS
+// area: stage A DMAs index-list entries (list mode), stage B DMAs block-table
+// entries, stage C turns them into rows, masks and per-step "all visible" flags.
+// The stage scratch (indices, pages) lives in the next window's mask buffer.
 // ---------------------------------------------------------------------------
 constexpr int kMW = 4;                      // steps per metadata window
 constexpr int kMT = kMW * kStepTokens;      // token slots per window
-constexpr int kTokPerLane = kMT / 64;       // slots each lane builds per window
+constexpr int kTokPerLane = kMT / 64;       // slots each lane handles per stage
 
 struct WaveMeta {
   int32_t row[2][kMT];
-  uint64_t vis[2][kMT];
+  uint64_t vis[2][kMT];     // also stage scratch: int32 index[kMT], int32 page[kMT]
   uint32_t full[2][kMW];
 };
 
-struct MetaStage {
-  int pos[kTokPerLane];
-  int jt[kTokPerLane];
-  int page[kTokPerLane];
-  uint64_t v[kTokPerLane];
-};
-
-// Stage A: logical position of each slot (index-list loads in list modes).
-__device__ __forceinline__ void meta_stage_a(const AttnArgs& a, const SeqInfo& si, int wbase, int w1,
-                                             int lane, MetaStage& ms) {
+// Logical position of slot tok of a window starting at step wbase; jt = tail slot or -1;
+// v = row-visibility mask of a non-tail token.  idx = the DMA'd index-list entry.
+template <int MODE>
+__device__ __forceinline__ void slot_pos(const AttnArgs& a, const SeqInfo& si, int wbase, int w1, int tok,
+                                         int idx, int& pos, int& jt, uint64_t& v) {
   const int P = 1 << a.lg_page;
-#pragma unroll
-  for (int r = 0; r < kTokPerLane; ++r) {
-    const int tok = lane + 64 * r;
-    const int step = wbase + tok / kStepTokens;
-    const int t = tok & (kStepTokens - 1);
-    int pos = -1, jt = -1;
-    uint64_t v = 0;
-    if (step < w1) {
-      if (a.mode == MODE_DENSE) {
-        const int u = step * kStepTokens + t;
-        if (u < si.L) {
-          pos = u;
-          v = kAll;
-        } else if (u < si.L + a.n_q) {
-          pos = u;
-          jt = u - si.L;
-        }
-      } else if (a.mode == MODE_BLOCK) {
-        const int spb = P / kStepTokens;
-        const int blk_steps = si.U * spb;
-        if (step < blk_steps) {
-          const int e = step / spb;
-          const int blk = si.ub[e];
-          const int p = blk * P + (step - e * spb) * kStepTokens + t;
-          if (blk >= 0 && blk < a.max_pages && p < si.tb) {
-            pos = p;
-            v = si.um[e];
-          }
-        } else {
-          const int u = (step - blk_steps) * kStepTokens + t;
-          if (u < si.tl) {
-            pos = si.tb + u;
-            jt = u;
-          }
-        }
-      } else {
-        const int u = step * kStepTokens + t;
-        // the index load is issued for every slot (clamped), keeping wait counts static
-        const int32_t* src = (si.cnt > 0) ? si.list + min(max(u, 0), si.cnt - 1) : a.bt;
-        const int lp = *src;
-        if (u < si.cnt) {
-          pos = lp;
-          v = kAll;
-        } else if (u - si.cnt < si.tl) {
-          jt = u - si.cnt;
-          pos = si.tb + jt;
-        }
+  const int step = wbase + tok / kStepTokens;
+  const int t = tok & (kStepTokens - 1);
+  pos = -1;
+  jt = -1;
+  v = 0;
+  // block mode: the union entry of each half-wave's step (lanes 0-31 and 32-63 hold
+  // different steps), read with wave-uniform loads while every lane is active
+  int blk = -1;
+  uint64_t bmask = 0;
+  if (MODE == MODE_BLOCK && si.U > 0) {
+    const int spb = P / kStepTokens;
+    const int e_lo = min(__builtin_amdgcn_readfirstlane(step) / spb, si.U - 1);
+    const int e_hi = min(__builtin_amdgcn_readlane(step, 32) / spb, si.U - 1);
+    const int b_lo = si.ub[max(e_lo, 0)], b_hi = si.ub[max(e_hi, 0)];
+    const uint64_t m_lo = si.um[max(e_lo, 0)], m_hi = si.um[max(e_hi, 0)];
+    const bool lo_half = (threadIdx.x & 63) < 32;
+    blk = lo_half ? b_lo : b_hi;
+    bmask = lo_half ? m_lo : m_hi;
+  }
+  if (step >= w1) return;
+  if (MODE == MODE_DENSE) {
+    const int u = step * kStepTokens + t;
+    if (u < si.L) {
+      pos = u;
+      v = kAll;
+    } else if (u < si.L + a.n_q) {
+      pos = u;
+      jt = u - si.L;
+    }
+  } else if (MODE == MODE_BLOCK) {
+    const int spb = P / kStepTokens;
+    const int blk_steps = si.U * spb;
+    if (step < blk_steps) {
+      const int e = step / spb;
+      const int p = blk * P + (step - e * spb) * kStepTokens + t;
+      if (blk >= 0 && blk < a.max_pages && p < si.tb) {
+        pos = p;
+        v = bmask;
+      }
+    } else {
+      const int u = (step - blk_steps) * kStepTokens + t;
+      if (u < si.tl) {
+        pos = si.tb + u;
+        jt = u;
       }
     }
-    ms.pos[r] = pos;
-    ms.jt[r] = jt;
-    ms.v[r] = v;
-  }
-}
-
-// Stage B: physical page of each slot (block-table loads).
-__device__ __forceinline__ void meta_stage_b(const AttnArgs& a, int b, MetaStage& ms) {
-#pragma unroll
-  for (int r = 0; r < kTokPerLane; ++r) {
-    const int pos = ms.pos[r];
-    const int pi = pos >> a.lg_page;
-    const bool ok = pos >= 0 && pi < a.max_pages;
-    // issued for every slot (clamped in range), keeping wait counts static
-    const int page = a.bt[(size_t)b * a.max_pages + (ok ? pi : 0)];
-    ms.page[r] = ok ? page : -1;
-  }
-}
-
-// Stage C: row index, visibility mask and per-step "everything visible" flag to LDS.
-__device__ __forceinline__ void meta_stage_c(const AttnArgs& a, int g, uint64_t colmask, int lane,
-                                             const MetaStage& ms, WaveMeta& wm, int buf) {
-  const int P = 1 << a.lg_page;
-#pragma unroll
-  for (int r = 0; r < kTokPerLane; ++r) {
-    const int tok = lane + 64 * r;
-    const int jt = ms.jt[r];
-    const uint64_t cm = shfl64(colmask, jt & 63);     // every lane takes part in the shuffle
-    uint64_t v = ms.v[r];
-    if (jt >= 0) v = (jt < 64 || a.rowmask == nullptr) ? cm : 0;
-    int row = -1;
-    const int page = ms.page[r];
-    if ((unsigned)page < (unsigned)a.num_pages) row = ((page * a.Hkv + g) << a.lg_page) | (ms.pos[r] & (P - 1));
-    if (row < 0) v = 0;
-    wm.row[buf][tok] = row;
-    wm.vis[buf][tok] = v;
-    const uint64_t ok = __ballot(row >= 0 && v == kAll);
-    if (lane == 0) {
-      wm.full[buf][2 * r] = (uint32_t)ok == 0xffffffffu;
-      wm.full[buf][2 * r + 1] = (uint32_t)(ok >> 32) == 0xffffffffu;
+  } else {
+    const int u = step * kStepTokens + t;
+    if (u < si.cnt) {
+      pos = idx;
+      v = kAll;
+    } else if (u - si.cnt < si.tl) {
+      jt = u - si.cnt;
+      pos = si.tb + jt;
     }
   }
 }
 
-// Issue the K and V loads of local step ls of window buffer buf.
-template <int D, int KS, int DPL>
-__device__ __forceinline__ void step_load(const AttnArgs& a, const WaveMeta& wm, int buf, int ls, int x,
-                                          int j, StepBuf<D, KS, DPL>& sb) {
-  const int32_t* rows = wm.row[buf] + ls * kStepTokens;
-  const int rk0 = rows[x];
-  const int rk1 = rows[16 + x];
-  const uint16_t* k0 = a.k + (size_t)max(rk0, 0) * D + 8 * j;
-  const uint16_t* k1 = a.k + (size_t)max(rk1, 0) * D + 8 * j;
+// Stage A (list mode): DMA the index-list entry of every slot into scratch index[].
+template <int MODE>
+__device__ __forceinline__ void meta_stage_a(const AttnArgs& a, const SeqInfo& si, int wbase, int lane,
+                                             WaveMeta& wm, int nb) {
+  if (MODE != MODE_LIST_SHARED) return;
+  int32_t* sidx = reinterpret_cast<int32_t*>(wm.vis[nb]);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    sb.k[0][ks] = *reinterpret_cast<const u32x4*>(k0 + 32 * ks);
-    sb.k[1][ks] = *reinterpret_cast<const u32x4*>(k1 + 32 * ks);
+  for (int r = 0; r < kTokPerLane; ++r) {
+    const int tok = lane + 64 * r;
+    const int u = (wbase + tok / kStepTokens) * kStepTokens + (tok & (kStepTokens - 1));
+    // every lane issues (clamped into the list, or the block table when the list is empty)
+    const int32_t* src = (si.cnt > 0) ? si.list + min(max(u, 0), si.cnt - 1) : a.bt;
+    dma4(src, sidx + 64 * r);
   }
+}
+
+// Stage B: DMA the block-table entry of every slot into scratch page[].
+template <int MODE>
+__device__ __forceinline__ void meta_stage_b(const AttnArgs& a, const SeqInfo& si, int b, int wbase, int w1,
+                                             int lane, WaveMeta& wm, int nb) {
+  const int32_t* sidx = reinterpret_cast<const int32_t*>(wm.vis[nb]);
+  int32_t* spg = reinterpret_cast<int32_t*>(wm.vis[nb]) + kMT;
+#pragma unroll
+  for (int r = 0; r < kTokPerLane; ++r) {
+    const int tok = lane + 64 * r;
+    int pos, jt;
+    uint64_t v;
+    slot_pos<MODE>(a, si, wbase, w1, tok, (MODE == MODE_LIST_SHARED) ? sidx[tok] : 0, pos, jt, v);
+    const int pi = pos >> a.lg_page;
+    const bool ok = pos >= 0 && pi < a.max_pages;
+    dma4(a.bt + (size_t)b * a.max_pages + (ok ? pi : 0), spg + 64 * r);
+  }
+}
+
+// Stage C: rows, masks and per-step flags of the window into buffer nb.
+template <int MODE>
+__device__ __forceinline__ void meta_stage_c(const AttnArgs& a, const SeqInfo& si, int g, int wbase, int w1,
+                                             uint64_t colmask, int lane, WaveMeta& wm, int nb) {
+  const int P = 1 << a.lg_page;
+  const int32_t* sidx = reinterpret_cast<const int32_t*>(wm.vis[nb]);
+  const int32_t* spg = sidx + kMT;
+  int idx[kTokPerLane], page[kTokPerLane];
+#pragma unroll
+  for (int r = 0; r < kTokPerLane; ++r) {
+    idx[r] = (MODE == MODE_LIST_SHARED) ? sidx[lane + 64 * r] : 0;
+    page[r] = spg[lane + 64 * r];
+  }
+#pragma unroll
+  for (int r = 0; r < kTokPerLane; ++r) {
+    const int tok = lane + 64 * r;
+    int pos, jt;
+    uint64_t v;
+    slot_pos<MODE>(a, si, wbase, w1, tok, idx[r], pos, jt, v);
+    const uint64_t cm = shfl64(colmask, jt & 63);     // every lane takes part in the shuffle
+    if (jt >= 0) v = (jt < 64 || a.rowmask == nullptr) ? cm : 0;
+    int row = -1;
+    if (pos >= 0 && (pos >> a.lg_page) < a.max_pages && (unsigned)page[r] < (unsigned)a.num_pages)
+      row = ((page[r] * a.Hkv + g) << a.lg_page) | (pos & (P - 1));
+    if (row < 0) v = 0;
+    wm.row[nb][tok] = row;
+    wm.vis[nb][tok] = v;
+    const uint64_t ok = __ballot(row >= 0 && v == kAll);
+    if (lane == 0) {
+      wm.full[nb][2 * r] = (uint32_t)ok == 0xffffffffu;
+      wm.full[nb][2 * r + 1] = (uint32_t)(ok >> 32) == 0xffffffffu;
+    }
+  }
+}
+
+// DMA the K and V operands of the step described by rows (32 slots) into a ring slot.
+// K: each 16-token tile is moved as whole rows (every request a full cache line):
+// DMA i of a tile carries 64/RCH consecutive token rows, lane l taking token
+// i*(64/RCH) + l/RCH and storing 16-byte chunk p = l % RCH of that row at LDS chunk p;
+// it fetches global chunk p ^ (token % RCH), so that the later MFMA-layout reads
+// (16 lanes, one chunk index each, 16 different rows) fall on different banks.
+// Tile tt occupies blocks [tt*16/(64/RCH), ...) of 1 KB; V: token t -> block KDMA+t.
+template <int D>
+__device__ __forceinline__ void step_dma(const AttnArgs& a, const int32_t* rows, char* slot, int lane, int x, int j) {
+  constexpr int RCH = D / 8;          // 16-byte chunks per row
+  constexpr int RPI = 64 / RCH;       // rows per DMA
+  constexpr int IPT = 16 / RPI;       // DMAs per 16-token tile
+  const int rq = lane / RCH, p = lane % RCH;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int tok = 16 * tt + RPI * i + rq;
+      const int c = p ^ (tok % RCH);
+      dma16(a.k + (size_t)max(rows[tok], 0) * D + 8 * c, slot + (tt * IPT + i) * 1024);
+    }
   const int4 rv0 = *reinterpret_cast<const int4*>(rows + 4 * j);
   const int4 rv1 = *reinterpret_cast<const int4*>(rows + 16 + 4 * j);
   const int rv[8] = {rv0.x, rv0.y, rv0.z, rv0.w, rv1.x, rv1.y, rv1.z, rv1.w};
-  // every load is issued (invalid slots read row 0) so the wait counts stay static;
-  // invalid rows are zeroed at use, since a masked weight times a NaN would poison O
-  uint32_t vok = 0;
+  const int dx = 8 * (x & (D / 8 - 1));   // d = 64: lanes x >= 8 repeat x - 8 (rows unused)
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    sb.v[t].load(a.v + (size_t)max(rv[t], 0) * D + DPL * x);
-    vok |= (rv[t] >= 0 ? 1u : 0u) << t;
-  }
-  sb.vok = vok;
+  for (int t = 0; t < 8; ++t) dma16(a.v + (size_t)max(rv[t], 0) * D + dx, slot + (2 * IPT + t) * 1024);
 }
 
-template <int D, int QT>
-__global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
-  constexpr int DPL = D / 16;   // dims per lane per token in the V^T operand
-  constexpr int KS = D / 32;    // k-steps of the QK^T product
-  constexpr int QLD = D + 8;    // LDS row stride of Q in bf16 (pads bank conflicts away)
-  constexpr int kPer = 4 * DPL + 2;                       // merge floats per lane per q-tile
-  constexpr size_t kQBytes = (size_t)QT * 16 * QLD * 2;
-  constexpr size_t kMetaBytes = sizeof(WaveMeta) * kWaves;
-  constexpr size_t kMergeBytes = (size_t)(kWaves - 1) * QT * kPer * 64 * 4;
-  constexpr size_t kLoopBytes = kQBytes + kMetaBytes;
+template <int D, int QT, int MODE>
+__global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;                  // k-steps of the QK^T product
+  constexpr int NDMA = 2 * KS + 8;            // 16-byte DMAs per lane per step
+  constexpr int kSlot = NDMA * 1024;          // ring slot bytes per wave
+  constexpr int QCH = D / 8;                  // 16-byte chunks per Q row
+  constexpr int kPer = 4 * 8 + 2;             // merge floats per lane per q-tile
+  constexpr size_t kQBytes = (size_t)QT * 16 * D * 2;
+  constexpr size_t kWaveBytes = sizeof(WaveMeta) + 2 * (size_t)kSlot;
+  constexpr size_t kLoopBytes = kQBytes + kWaves * kWaveBytes;
+  constexpr size_t kMergeBytes = (size_t)kWaves * QT * kPer * 64 * 4;
   constexpr size_t kSmem = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmem];
-  uint16_t* s_q = reinterpret_cast<uint16_t*>(smem_raw);
-  WaveMeta* s_meta = reinterpret_cast<WaveMeta*>(smem_raw + kQBytes);
-  float* s_merge = reinterpret_cast<float*>(smem_raw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int x = lane & 15;
   const int j = lane >> 4;
   const int s = blockIdx.x;
@@ -307,23 +347,14 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
   const int b = blockIdx.z;
   const int r0 = rc * kMaxRowsPerWG;
   const int nrows = min(kMaxRowsPerWG, a.rows - r0);
-  WaveMeta& wm = s_meta[wave];
 
-  // Q rows of this workgroup -> LDS (rows past nrows are zero)
-  for (int e = tid; e < QT * 16 * (D / 8); e += 256) {
-    const int r = e / (D / 8);
-    const int c = e - r * (D / 8);
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (r < nrows) {
-      const int rr = r0 + r;
-      const int i = rr / a.G;
-      const int h = g * a.G + (rr - i * a.G);
-      v = *reinterpret_cast<const u32x4*>(a.q + ((size_t)(b * a.n_q + i) * a.Hq + h) * D + 8 * c);
-    }
-    *reinterpret_cast<u32x4*>(s_q + r * QLD + 8 * c) = v;
-  }
+  uint16_t* s_q = reinterpret_cast<uint16_t*>(smem_raw);
+  unsigned char* wbase_lds = smem_raw + kQBytes + (size_t)wave * kWaveBytes;
+  WaveMeta& wm = *reinterpret_cast<WaveMeta*>(wbase_lds);
+  char* ring = reinterpret_cast<char*>(wbase_lds + sizeof(WaveMeta));
+  float* s_merge = reinterpret_cast<float*>(smem_raw);
 
-  const SeqInfo si = seq_info(a, b, g);
+  const SeqInfo si = seq_info<MODE>(a, b, g);
   const int st0 = s * a.sps;
   const int st1 = (s == a.n_split - 1) ? si.T : min(si.T, st0 + a.sps);
   // contiguous per-wave step ranges
@@ -339,7 +370,7 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     const uint64_t* rm = a.rowmask + (size_t)b * a.n_q;
     for (int i = 0; i < a.n_q; ++i) colmask |= ((rm[i] >> lane) & 1ull) << i;
   } else {
-    colmask = (a.mode == MODE_DENSE) ? (kAll << lane) : kAll;
+    colmask = (MODE == MODE_DENSE) ? (kAll << lane) : kAll;
   }
 
   // verifier row index of this lane's q-row in each tile (64 = padding row)
@@ -349,47 +380,115 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     const int r = 16 * qt + x;
     rowi[qt] = (r < nrows) ? (r0 + r) / a.G : 64;
   }
-  const bool collect = a.mode == MODE_DENSE && a.logits != nullptr;
+  const bool collect = MODE == MODE_DENSE && a.logits != nullptr;
 
   float m[QT], l[QT];
-  f32x4 O[QT][DPL];
+  f32x4 O[QT][8];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     m[qt] = -INFINITY;
     l[qt] = 0.f;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) O[qt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 8; ++e) O[qt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // Prologue: window-0 metadata DMAs go out together with the Q loads, so the block-table
+  // round trip overlaps the Q fetch and the Q -> LDS copy.
+  if (w0 < w1) {
+    if (MODE == MODE_LIST_SHARED) meta_stage_a<MODE>(a, si, w0, lane, wm, 0);
+    else meta_stage_b<MODE>(a, si, b, w0, w1, lane, wm, 0);
+  }
+  // Q rows of this workgroup: 16-byte chunk c of row r goes to LDS chunk c ^ (r % QCH)
+  constexpr int kQPer = (QT * 16 * QCH + 255) / 256;
+  u32x4 qv[kQPer];
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int e = tid + 256 * u;
+    const int r = e / QCH;
+    const int c = e - r * QCH;
+    qv[u] = u32x4{0, 0, 0, 0};
+    if (e < QT * 16 * QCH && r < nrows) {
+      const int rr = r0 + r;
+      const int i = rr / a.G;
+      const int h = g * a.G + (rr - i * a.G);
+      qv[u] = *reinterpret_cast<const u32x4*>(a.q + ((size_t)(b * a.n_q + i) * a.Hq + h) * D + 8 * c);
+    }
+  }
+  wait_vm<0>();
+  if (MODE == MODE_LIST_SHARED && w0 < w1) meta_stage_b<MODE>(a, si, b, w0, w1, lane, wm, 0);
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int e = tid + 256 * u;
+    const int r = e / QCH;
+    const int c = e - r * QCH;
+    if (e < QT * 16 * QCH) *reinterpret_cast<u32x4*>(s_q + (r * QCH + (c ^ (r % QCH))) * 8) = qv[u];
   }
   __syncthreads();   // Q in LDS
+  // Q^T B-operands of this lane (q-row x of each tile, 8 dims per k-step), kept in registers
+  u32x4 qop[QT][KS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int r = 16 * qt + x;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = 4 * ks + j;
+      qop[qt][ks] = *reinterpret_cast<const u32x4*>(s_q + (r * QCH + (c ^ (r % QCH))) * 8);
+    }
+  }
 
   if (w0 < w1) {
-    MetaStage ms;
-    meta_stage_a(a, si, w0, w1, lane, ms);
-    meta_stage_b(a, b, ms);
-    meta_stage_c(a, g, colmask, lane, ms, wm, 0);
-    StepBuf<D, KS, DPL> cur;
-    step_load<D, KS, DPL>(a, wm, 0, 0, x, j, cur);
+    wait_vm<0>();
+    meta_stage_c<MODE>(a, si, g, w0, w1, colmask, lane, wm, 0);
+    wait_lgkm0();
+    step_dma<D>(a, wm.row[0], ring, lane, x, j);
+    if (w0 + 1 < w1) step_dma<D>(a, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
+    // software pipeline: iteration s issues S(s), then PV(s-1) from the previous
+    // iteration's registers, so the matrix core works through PV(s-1) while the VALU
+    // does softmax(s).  The first PV runs on zero P and V (adds exact zeros).
+    u32x4 vprev[8], phi[QT], plo[QT];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) vprev[t] = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) phi[qt] = plo[qt] = u32x4{0, 0, 0, 0};
+    const float c2 = a.scale_log2;
     for (int wb = w0, k = 0; wb < w1; wb += kMW, ++k) {
       const int buf = k & 1;
       const bool next_win = wb + kMW < w1;
       const int nloc = min(kMW, w1 - wb);
       for (int ls = 0; ls < nloc; ++ls) {
         const int step = wb + ls;
+        char* slot = ring + ((step - w0) & 1) * kSlot;
+        // this step's DMAs are done once at most one step's worth is outstanding
+        if (step + 1 < w1) wait_vm<NDMA>();
+        else wait_vm<0>();
+        u32x4 kop[2][KS], vcur[8];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int kpos = ((4 * ks + j) ^ (x % QCH)) * 16;   // swizzled chunk of row x
+          kop[0][ks] = *reinterpret_cast<const u32x4*>(slot + x * (2 * D) + kpos);
+          kop[1][ks] = *reinterpret_cast<const u32x4*>(slot + (16 + x) * (2 * D) + kpos);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vcur[t] = *reinterpret_cast<const u32x4*>(slot + (2 * KS + t) * 1024 + 16 * lane);
+        const bool full = wm.full[buf][ls] != 0;
+        if (!full) {
+          // invalid slots were loaded from row 0: zero them, since a masked weight
+          // times a NaN in an unused cache slot would still poison O
+          const int32_t* rows = wm.row[buf] + ls * kStepTokens;
+          const int4 rv0 = *reinterpret_cast<const int4*>(rows + 4 * j);
+          const int4 rv1 = *reinterpret_cast<const int4*>(rows + 16 + 4 * j);
+          const int rv[8] = {rv0.x, rv0.y, rv0.z, rv0.w, rv1.x, rv1.y, rv1.z, rv1.w};
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if (rv[t] < 0) vcur[t] = u32x4{0, 0, 0, 0};
+        }
+        wait_lgkm0();   // the slot is in registers: it may be refilled
+        // next window's metadata, one stage per step, issued before the data DMAs
         if (next_win) {
-          if (ls == 0) meta_stage_a(a, si, wb + kMW, w1, lane, ms);
-          if (ls == 1) meta_stage_b(a, b, ms);
-          if (ls == 2) meta_stage_c(a, g, colmask, lane, ms, wm, buf ^ 1);
+          if (ls == 0) meta_stage_a<MODE>(a, si, wb + kMW, lane, wm, buf ^ 1);
+          if (ls == 1) meta_stage_b<MODE>(a, si, b, wb + kMW, w1, lane, wm, buf ^ 1);
+          if (ls == 2) meta_stage_c<MODE>(a, si, g, wb + kMW, w1, colmask, lane, wm, buf ^ 1);
         }
-        // next step's loads go out before this step is consumed (the last step re-reads itself)
-        StepBuf<D, KS, DPL> nxt;
-        {
-          int nb = buf, nls = ls + 1;
-          if (nls == kMW) { nb = buf ^ 1; nls = 0; }
-          if (step + 1 >= w1) { nb = buf; nls = ls; }
-          step_load<D, KS, DPL>(a, wm, nb, nls, x, j, nxt);
-        }
-
-        // ---- S^T = K Q^T for two 16-token tiles (Q^T operand from LDS)
+        // ---- S^T(s) = K Q^T for two 16-token tiles
         f32x4 S[2][QT];
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
@@ -397,91 +496,18 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
           S[1][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 qop = *reinterpret_cast<const u32x4*>(s_q + (16 * qt + x) * QLD + 32 * ks + 8 * j);
-            S[0][qt] = mfma16(cur.k[0][ks], qop, S[0][qt]);
-            S[1][qt] = mfma16(cur.k[1][ks], qop, S[1][qt]);
+            S[0][qt] = mfma16(kop[0][ks], qop[qt][ks], S[0][qt]);
+            S[1][qt] = mfma16(kop[1][ks], qop[qt][ks], S[1][qt]);
           }
         }
-
-        // ---- visibility of the 8 tokens this lane holds (tokens 16tt + 4j + i)
-        const bool full = wm.full[buf][ls] != 0;
-        uint64_t vt[2][4];
-        if (!full) {
-          const uint64_t* vr = wm.vis[buf] + ls * kStepTokens;
+        // ---- O^T += V^T(s-1) P^T(s-1), one transposed V tile at a time
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vt[tt][i] = vr[16 * tt + 4 * j + i];
-        }
-
-        // ---- online softmax per q-tile; P as bf16 hi + lo B-operands
-        u32x4 phi[QT], plo[QT];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          float t8[8];
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float sv = S[tt][qt][i] * a.scale_log2;
-              if (!full && ((vt[tt][i] >> rowi[qt]) & 1ull) == 0) sv = -INFINITY;
-              t8[4 * tt + i] = sv;
-            }
-          // Collect-2-Query: scaled logits of the two collected rows, prefix columns only
-          if (collect && (rowi[qt] == a.c0 || rowi[qt] == a.c1)) {
-            const int rr = r0 + 16 * qt + x;
-            const int h = g * a.G + (rr - rowi[qt] * a.G);
-            float* base = a.logits + (size_t)(b * a.Hq + h) * 2 * a.logits_ld;
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              if (rowi[qt] != (c == 0 ? a.c0 : a.c1)) continue;
-              float* dst = base + c * a.logits_ld;
-#pragma unroll
-              for (int tt = 0; tt < 2; ++tt) {
-                const int p0 = step * kStepTokens + 16 * tt + 4 * j;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  if (p0 + i < si.L) dst[p0 + i] = S[tt][qt][i] * a.scale;
-              }
-            }
-          }
-          float rmax = t8[0];
-#pragma unroll
-          for (int u = 1; u < 8; ++u) rmax = fmaxf(rmax, t8[u]);
-          rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
-          rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-          const float mnew = fmaxf(m[qt], rmax);
-          const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-          const float alpha = __builtin_amdgcn_exp2f(m[qt] - msafe);
-          m[qt] = mnew;
-          float psum = 0.f;
-#pragma unroll
-          for (int u = 0; u < 8; u += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(t8[u] - msafe);
-            const float p1 = __builtin_amdgcn_exp2f(t8[u + 1] - msafe);
-            psum += p0 + p1;
-            const uint32_t h0 = bf16_rne(p0), h1 = bf16_rne(p1);
-            const uint32_t l0 = bf16_rne(p0 - bf16_to_f32(h0));
-            const uint32_t l1 = bf16_rne(p1 - bf16_to_f32(h1));
-            phi[qt][u >> 1] = h0 | (h1 << 16);
-            plo[qt][u >> 1] = l0 | (l1 << 16);
-          }
-          l[qt] = l[qt] * alpha + psum;
-          if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) O[qt][e] *= alpha;
-          }
-        }
-
-        // ---- O^T += V^T P^T, one transposed V tile at a time
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) {
+        for (int e = 0; e < 8; ++e) {
           u32x4 vte;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            const uint32_t lo = (cur.vok >> (2 * w)) & 1u ? velem<DPL>(cur.v[2 * w], e) : 0u;
-            const uint32_t hi = (cur.vok >> (2 * w + 1)) & 1u ? velem<DPL>(cur.v[2 * w + 1], e) : 0u;
-            vte[w] = lo | (hi << 16);
+            const uint32_t w0v = vprev[2 * w][e >> 1], w1v = vprev[2 * w + 1][e >> 1];
+            vte[w] = (e & 1) ? ((w0v >> 16) | (w1v & 0xffff0000u)) : ((w0v & 0xffffu) | (w1v << 16));
           }
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt) {
@@ -489,7 +515,106 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
             O[qt][e] = mfma16(vte, plo[qt], O[qt][e]);
           }
         }
-        cur = nxt;
+
+        // ---- Collect-2-Query: scaled logits of the two collected rows, prefix columns only.
+        //      Stored before the next DMA batch is issued: stores count in vmcnt too, and
+        //      one issued after the batch would make the next step's wait drain the batch.
+        if (collect) {
+          const int p0 = step * kStepTokens + 4 * j;
+          const bool whole = a.lvec4 && step * kStepTokens + kStepTokens <= si.L;
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            const bool m0 = rowi[qt] == a.c0, m1 = rowi[qt] == a.c1;
+            if (!__any(m0 || m1)) continue;
+            const int rr = r0 + 16 * qt + x;
+            const int h = g * a.G + (rr - rowi[qt] * a.G);
+            float* base = a.logits + (size_t)(b * a.Hq + h) * 2 * a.logits_ld + p0;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              if (!(c == 0 ? m0 : m1)) continue;
+              float* dst = base + c * a.logits_ld;
+              if (whole) {
+                *reinterpret_cast<f32x4*>(dst) = S[0][qt] * a.scale;
+                *reinterpret_cast<f32x4*>(dst + 16) = S[1][qt] * a.scale;
+              } else {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                  for (int i = 0; i < 4; ++i)
+                    if (p0 + 16 * tt + i < si.L) dst[16 * tt + i] = S[tt][qt][i] * a.scale;
+              }
+            }
+          }
+        }
+        if (step + 2 < w1) {
+          const int ns = ls + 2;
+          const int32_t* nrows_p = (ns < kMW) ? wm.row[buf] + ns * kStepTokens
+                                              : wm.row[buf ^ 1] + (ns - kMW) * kStepTokens;
+          step_dma<D>(a, nrows_p, slot, lane, x, j);
+        }
+
+        // ---- online softmax(s) per q-tile.  The reference max m only moves when a row's
+        //      max grows by more than 2^kTau, so the O rescale (AGPR round trips) is rare;
+        //      weights stay below 2^kTau.  P goes out as bf16 hi + lo B-operands.
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          float t8[8];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t8[4 * tt + i] = S[tt][qt][i];
+          if (!full) {
+            const uint64_t* vr = wm.vis[buf] + ls * kStepTokens;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (((vr[16 * tt + 4 * j + i] >> rowi[qt]) & 1ull) == 0) t8[4 * tt + i] = -INFINITY;
+          }
+          const float rmax = colmax4(fmax2(fmax2(fmax2(t8[0], t8[1]), fmax2(t8[2], t8[3])),
+                                           fmax2(fmax2(t8[4], t8[5]), fmax2(t8[6], t8[7]))));
+          const float mx = rmax * c2;
+          const bool grow = mx > m[qt] + kTau;
+          if (__any(grow)) {
+            // rows that keep their reference (possibly still -inf) keep alpha = 1
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m[qt] - mx) : 1.f;
+            l[qt] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) O[qt][e] *= alpha;
+            m[qt] = grow ? mx : m[qt];
+          }
+          const float nms = (m[qt] == -INFINITY) ? 0.f : -m[qt];
+          float psum = 0.f;
+#pragma unroll
+          for (int u = 0; u < 8; u += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(t8[u], c2, nms));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(t8[u + 1], c2, nms));
+            psum += p0 + p1;
+            const uint32_t h0 = bf16_rne(p0), h1 = bf16_rne(p1);
+            const uint32_t l0 = bf16_rne(p0 - bf16_to_f32(h0));
+            const uint32_t l1 = bf16_rne(p1 - bf16_to_f32(h1));
+            phi[qt][u >> 1] = h0 | (h1 << 16);
+            plo[qt][u >> 1] = l0 | (l1 << 16);
+          }
+          l[qt] += psum;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vprev[t] = vcur[t];
+      }
+    }
+    // drain: PV of the last step
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      u32x4 vte;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t w0v = vprev[2 * w][e >> 1], w1v = vprev[2 * w + 1][e >> 1];
+        vte[w] = (e & 1) ? ((w0v >> 16) | (w1v & 0xffff0000u)) : ((w0v & 0xffffu) | (w1v << 16));
+      }
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        O[qt][e] = mfma16(vte, phi[qt], O[qt][e]);
+        O[qt][e] = mfma16(vte, plo[qt], O[qt][e]);
       }
     }
   }
@@ -501,78 +626,80 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     l[qt] += __shfl_xor(l[qt], 32);
   }
 
-  // ---- merge the 4 waves' states through LDS in wave order 0,1,2,3
-  __syncthreads();   // every wave is done with Q and its metadata ring
-  if (wave > 0) {
-    float* w = s_merge + (size_t)(wave - 1) * QT * kPer * 64;
+  // ---- merge the 4 waves' states through LDS.  Every wave publishes (m, l, O); then
+  //      wave w merges dims {8i + 2w, 8i + 2w + 1} of every row, in wave order 0..3.
+  __syncthreads();   // every wave is done with Q, its metadata and its ring
+  {
+    float* w = s_merge + (size_t)wave * QT * kPer * 64;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e)
+      for (int e = 0; e < 8; ++e)
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[(qt * kPer + e * 4 + i) * 64 + lane] = O[qt][e][i];
-      w[(qt * kPer + 4 * DPL) * 64 + lane] = m[qt];
-      w[(qt * kPer + 4 * DPL + 1) * 64 + lane] = l[qt];
+      w[(qt * kPer + 32) * 64 + lane] = m[qt];
+      w[(qt * kPer + 33) * 64 + lane] = l[qt];
     }
   }
   __syncthreads();
-  if (wave != 0) return;
-  for (int ow = 1; ow < kWaves; ++ow) {
-    const float* w = s_merge + (size_t)(ow - 1) * QT * kPer * 64;
+  const int e0 = 2 * wave;          // this wave's two O tiles (dims 32j + 8i + e0 + {0, 1})
+  float mo[QT], lo_[QT], oo[QT][2][4];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float mb = w[(qt * kPer + 4 * DPL) * 64 + lane];
-      const float lb = w[(qt * kPer + 4 * DPL + 1) * 64 + lane];
-      const float M = fmaxf(m[qt], mb);
-      const float Ms = (M == -INFINITY) ? 0.f : M;
-      const float wa = __builtin_amdgcn_exp2f(m[qt] - Ms);
-      const float wb = __builtin_amdgcn_exp2f(mb - Ms);
-      m[qt] = M;
-      l[qt] = wa * l[qt] + wb * lb;
+  for (int qt = 0; qt < QT; ++qt) {
+    float M = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e)
+    for (int ow = 0; ow < kWaves; ++ow) M = fmax2(M, s_merge[((size_t)ow * QT * kPer + qt * kPer + 32) * 64 + lane]);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          O[qt][e][i] = wa * O[qt][e][i] + wb * w[(qt * kPer + e * 4 + i) * 64 + lane];
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oo[qt][h][i] = 0.f;
+#pragma unroll
+    for (int ow = 0; ow < kWaves; ++ow) {
+      const float* w = s_merge + (size_t)ow * QT * kPer * 64;
+      const float mw = w[(qt * kPer + 32) * 64 + lane];
+      const float sc = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Ms);
+      L += sc * w[(qt * kPer + 33) * 64 + lane];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oo[qt][h][i] += sc * w[(qt * kPer + (e0 + h) * 4 + i) * 64 + lane];
     }
+    mo[qt] = M;
+    lo_[qt] = L;
   }
 
-  // ---- write: final output when there is a single split, else a partial
+  // ---- write: lane (x, j) holds q-row x, dims 32j + 8i + e0 + {0,1} (i < 4); for d = 64
+  //      only j < 2 holds real dims.  Final output with one split, else a partial.
+  if (32 * j >= D) return;
   const size_t pstride = (size_t)kMaxRowsPerWG * (D + 2);
   const size_t pidx = ((size_t)(b * a.Hkv + g) * a.n_rc + rc) * a.n_split + s;
+  const int d0 = 32 * j + e0;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int r = 16 * qt + x;
     if (r >= nrows) continue;
-    const int d0 = 4 * DPL * j;
     if (a.n_split == 1) {
       const int rr = r0 + r;
       const int i = rr / a.G;
       const int h = g * a.G + (rr - i * a.G);
-      const float inv = (l[qt] > 0.f) ? 1.f / l[qt] : 0.f;
+      const float inv = (lo_[qt] > 0.f) ? 1.f / lo_[qt] : 0.f;
       float* op = a.out + ((size_t)(b * a.n_q + i) * a.Hq + h) * D + d0;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4)
-#pragma unroll
-        for (int e4 = 0; e4 < DPL; e4 += 4) {
-          f32x4 v4 = f32x4{O[qt][e4][i4], O[qt][e4 + 1][i4], O[qt][e4 + 2][i4], O[qt][e4 + 3][i4]};
-          *reinterpret_cast<f32x4*>(op + DPL * i4 + e4) = v4 * inv;
-        }
-      if (j == 0 && a.lse != nullptr)
+        *reinterpret_cast<float2*>(op + 8 * i4) = make_float2(oo[qt][0][i4] * inv, oo[qt][1][i4] * inv);
+      if (wave == 0 && j == 0 && a.lse != nullptr)
         a.lse[(size_t)(b * a.n_q + i) * a.Hq + h] =
-            (l[qt] > 0.f) ? (m[qt] + __log2f(l[qt])) * kLn2 : -INFINITY;
+            (lo_[qt] > 0.f) ? (mo[qt] + __log2f(lo_[qt])) * kLn2 : -INFINITY;
     } else {
       float* pp = a.part + pidx * pstride;
       float* op = pp + (size_t)r * D + d0;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-#pragma unroll
-        for (int e4 = 0; e4 < DPL; e4 += 4)
-          *reinterpret_cast<f32x4*>(op + DPL * i4 + e4) =
-              f32x4{O[qt][e4][i4], O[qt][e4 + 1][i4], O[qt][e4 + 2][i4], O[qt][e4 + 3][i4]};
-      if (j == 0) {
-        pp[(size_t)kMaxRowsPerWG * D + r] = m[qt];
-        pp[(size_t)kMaxRowsPerWG * D + kMaxRowsPerWG + r] = l[qt];
+      for (int i4 = 0; i4 < 4; ++i4) *reinterpret_cast<float2*>(op + 8 * i4) = make_float2(oo[qt][0][i4], oo[qt][1][i4]);
+      if (wave == 0 && j == 0) {
+        pp[(size_t)kMaxRowsPerWG * D + r] = mo[qt];
+        pp[(size_t)kMaxRowsPerWG * D + kMaxRowsPerWG + r] = lo_[qt];
       }
     }
   }
@@ -715,14 +842,14 @@ __global__ void __launch_bounds__(256) block_union_kernel(AttnArgs a) {
   if (tid == 0) const_cast<int32_t*>(a.ucount)[bg] = min(total, a.ucap);
 }
 
-template <int D>
-hipError_t launch_main(const AttnPlan& p, const AttnArgs& a, hipStream_t stream) {
+template <int D, int MODE>
+hipError_t launch_main_mode(const AttnPlan& p, const AttnArgs& a, hipStream_t stream) {
   dim3 grid(p.n_split, a.Hkv * p.n_rc, a.B);
   switch (p.QT) {
-    case 1: hipLaunchKernelGGL((attn_kernel<D, 1>), grid, dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((attn_kernel<D, 2>), grid, dim3(256), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((attn_kernel<D, 3>), grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((attn_kernel<D, 4>), grid, dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((attn_kernel<D, 1, MODE>), grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_kernel<D, 2, MODE>), grid, dim3(256), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((attn_kernel<D, 3, MODE>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((attn_kernel<D, 4, MODE>), grid, dim3(256), 0, stream, a); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
@@ -730,6 +857,14 @@ hipError_t launch_main(const AttnPlan& p, const AttnArgs& a, hipStream_t stream)
   hipLaunchKernelGGL((combine_kernel<D>), dim3(a.B * a.Hkv * p.n_rc, (rows_wg + kCombineRows - 1) / kCombineRows),
                      dim3(64 * kCombineRows), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_main(const AttnPlan& p, const AttnArgs& a, hipStream_t stream) {
+  // the two token-list modes differ only in which list a KV head reads
+  if (a.mode == MODE_DENSE) return launch_main_mode<D, MODE_DENSE>(p, a, stream);
+  if (a.mode == MODE_BLOCK) return launch_main_mode<D, MODE_BLOCK>(p, a, stream);
+  return launch_main_mode<D, MODE_LIST_SHARED>(p, a, stream);
 }
 
 }  // namespace

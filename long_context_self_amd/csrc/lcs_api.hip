@@ -91,7 +91,7 @@ lcs_status lcs_verify_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int
   if (q == nullptr || prefix_len == nullptr || out == nullptr)
     return fail(LCS_E_ARG, "q, prefix_len and out must be non-NULL");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(LCS_E_ARG, "q and out must be 16-byte aligned");
-  if (!isfinite(scale)) return fail(LCS_E_ARG, "scale must be finite");
+  if (!isfinite(scale) || !(scale > 0.f)) return fail(LCS_E_ARG, "scale must be finite and positive");
   if (logits != nullptr && logits_ld < max_prefix_len)
     return fail(LCS_E_SHAPE, "logits_ld %lld < max_prefix_len %d", (long long)logits_ld, max_prefix_len);
   if ((long long)max_prefix_len + n_q > (long long)kv->max_pages * kv->page_size)
@@ -123,6 +123,7 @@ lcs_status lcs_verify_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int
   a.c1 = collect_row1;
   a.logits = logits;
   a.logits_ld = logits_ld;
+  a.lvec4 = (logits != nullptr && aligned(logits, 16) && logits_ld % 4 == 0) ? 1 : 0;
   a.out = out;
   a.lse = lse;
   return hip_status(lcs::attn_launch(plan, a, workspace, static_cast<hipStream_t>(stream)));
@@ -218,7 +219,7 @@ lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t 
   if (cap > 0 && (indices == nullptr || counts == nullptr))
     return fail(LCS_E_ARG, "indices and counts must be non-NULL when cap > 0");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(LCS_E_ARG, "q and out must be 16-byte aligned");
-  if (!isfinite(scale)) return fail(LCS_E_ARG, "scale must be finite");
+  if (!isfinite(scale) || !(scale > 0.f)) return fail(LCS_E_ARG, "scale must be finite and positive");
   if (tail_mask != nullptr && max_tail_len > 64)
     return fail(LCS_E_UNSUPPORTED, "a tail mask covers at most 64 tail slots (max_tail_len %d)", max_tail_len);
   if (mode == LCS_SET_BLOCK && kv->page_size % lcs::kStepTokens != 0)

@@ -54,6 +54,7 @@ struct AttnArgs {
   int32_t c0, c1;
   float* logits;
   int64_t logits_ld;
+  int32_t lvec4;   // logits rows 16-byte aligned (16-byte stores allowed)
   // split-K
   float* part;
   int32_t n_split, sps;
