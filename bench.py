@@ -19,7 +19,6 @@ microseconds are in `kernels`.  `roofline` is for the dominant kernel (verify).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -33,7 +32,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_llama8b_32k_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "long_context_self_amd", "csrc", f) for f in ("attn.hip", "lcs_internal.h")]
 
 
 def parse():
@@ -45,6 +43,8 @@ def parse():
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="run one device-to-device copy of this size first (counter calibration)")
     return p.parse_args()
 
 
@@ -66,20 +66,14 @@ def algorithmic_bytes(cfg, S_draft, tail_lens):
     return verify, select, drafts
 
 
-def kernel_hash():
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
-    return h.hexdigest()[:16]
-
-
 def traffic_record(per_launch_bytes):
     """HBM bytes per verify launch from committed rocprofv3 counter runs, if they match this source."""
     try:
         rec = json.load(open(PROFILE_TRAFFIC))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_hash():
+    from long_context_self_amd.profile_summary import kernel_source_hash
+    if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -182,6 +176,14 @@ def main():
     def draft(r, j):
         lcs.sparse_draft_attn(layers[r], qds[j], cfg.mode, idx[r], cnt[r], pl, tls[j], max_tl, scale,
                               out=dout, lse=dlse, workspace=ws_d)
+
+    if args.copy_calibration_mib > 0:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for r in range(R):       # the first iteration's sparse sets
         verify(r)

@@ -705,12 +705,19 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge split-K partials in split order.  One wave per q-row: lane s first loads the
-// (m, l) of split s, so the per-split loads are issued together rather than one
-// after another; then every lane accumulates its columns over the splits.
+// Merge split-K partials in split order.  One wave per q-row.  Lane s loads the
+// (m, l) of split s while every lane also loads its columns of the first kChunk
+// splits; later chunks are loaded one chunk ahead of their use, so the common case
+// (n_split <= kChunk) costs one memory round trip.  Split weights reach the column
+// loop through readlane.
 constexpr int kCombineRows = 4;
+constexpr int kChunk = 16;
 
-template <int D>
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+template <int D, int MODE>
 __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   const int pid = blockIdx.x;                   // (b*Hkv + g)*n_rc + rc
   const int rc = pid % a.n_rc;
@@ -722,16 +729,25 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.y * kCombineRows + (threadIdx.x >> 6);
   if (r >= nrows) return;
+  const int ns = a.n_split;                     // 2 .. kMaxSplits = 128
   const size_t pstride = (size_t)kMaxRowsPerWG * (D + 2);
-  const float* base = a.part + (size_t)pid * a.n_split * pstride;
+  const float* base = a.part + (size_t)pid * ns * pstride;
   const float* mcol = base + (size_t)kMaxRowsPerWG * D + r;
-  // splits are at most kMaxSplits = 128: two per lane
+  constexpr int CPL = D / 64;                   // columns per lane (2 or 1)
+  const float* ocol = base + (size_t)r * D + CPL * lane;
+  float cur[kChunk][CPL], nxt[kChunk][CPL];
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) cur[u][c] = ocol[(size_t)min(u, ns - 1) * pstride + c];
   float mv[2], lv[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int sp = lane + 64 * u;
-    mv[u] = (sp < a.n_split) ? mcol[sp * pstride] : -INFINITY;
-    lv[u] = (sp < a.n_split) ? mcol[sp * pstride + kMaxRowsPerWG] : 0.f;
+    const size_t o = (size_t)min(sp, ns - 1) * pstride;
+    mv[u] = mcol[o];
+    lv[u] = mcol[o + kMaxRowsPerWG];
+    if (sp >= ns) { mv[u] = -INFINITY; lv[u] = 0.f; }
   }
   float M = fmaxf(mv[0], mv[1]);
 #pragma unroll
@@ -740,39 +756,35 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   float wv[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) wv[u] = __builtin_amdgcn_exp2f(mv[u] - Ms);
-  // L = sum over splits in split order: gather the weighted l's to lane 0's order via LDS
-  __shared__ float s_w[kCombineRows][kMaxSplits];
-  __shared__ float s_l[kCombineRows][kMaxSplits];
-  const int wr = threadIdx.x >> 6;
+  // butterfly sum: every lane ends with the same, run-to-run fixed value
+  float Ls = wv[0] * lv[0] + wv[1] * lv[1];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    s_w[wr][lane + 64 * u] = wv[u];
-    s_l[wr][lane + 64 * u] = wv[u] * lv[u];
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  float Ls = 0.f;
-  for (int sp = 0; sp < a.n_split; ++sp) Ls += s_l[wr][sp];
-  constexpr int CPL = D / 64;                   // columns per lane (2 or 1)
+  for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off);
   float acc[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-  const float* ocol = base + (size_t)r * D + CPL * lane;
-  int sp = 0;
-  for (; sp + 4 <= a.n_split; sp += 4) {
-    float ov[4][CPL];
+  for (int c0 = 0; c0 < ns; c0 += kChunk) {
+    const bool more = c0 + kChunk < ns;
+    if (more) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kChunk; ++u)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) ov[u][c] = ocol[(sp + u) * pstride + c];
+        for (int c = 0; c < CPL; ++c) nxt[u][c] = ocol[(size_t)min(c0 + kChunk + u, ns - 1) * pstride + c];
+    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kChunk; ++u) {
+      const int sp = c0 + u;
+      const float w = (sp < ns) ? lane_f(sp < 64 ? wv[0] : wv[1], sp & 63) : 0.f;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] += s_w[wr][sp + u] * ov[u][c];
+      for (int c = 0; c < CPL; ++c) acc[c] += w * cur[u][c];
+    }
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) cur[u][c] = nxt[u][c];
+    }
   }
-  for (; sp < a.n_split; ++sp)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] += s_w[wr][sp] * ocol[sp * pstride + c];
   const float inv = (Ls > 0.f) ? 1.f / Ls : 0.f;
   const int rr = r0 + r;
   const int i = rr / a.G;
@@ -854,7 +866,7 @@ hipError_t launch_main_mode(const AttnPlan& p, const AttnArgs& a, hipStream_t st
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
   const int rows_wg = p.rows < kMaxRowsPerWG ? p.rows : kMaxRowsPerWG;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(a.B * a.Hkv * p.n_rc, (rows_wg + kCombineRows - 1) / kCombineRows),
+  hipLaunchKernelGGL((combine_kernel<D, MODE>), dim3(a.B * a.Hkv * p.n_rc, (rows_wg + kCombineRows - 1) / kCombineRows),
                      dim3(64 * kCombineRows), 0, stream, a);
   return hipGetLastError();
 }

@@ -1,0 +1,145 @@
+"""Short text summaries of rocprofv3 output.
+
+    python -m long_context_self_amd.profile_summary stats --csv <kernel_stats.csv | results.db> \\
+        --command "<the rocprofv3 command>" --out profiles/<kernel>_<workload>.md
+    python -m long_context_self_amd.profile_summary traffic \\
+        --fetch <counter_collection.csv | results.db of a FETCH_SIZE run> \\
+        --write <counter_collection.csv | results.db of a WRITE_SIZE run> \\
+        --copy-bytes <size of the calibration copy> --kernel <name> [--kernel <name> ...] \\
+        --algorithmic-bytes <per launch> --command-fetch "..." --command-write "..." \\
+        --out profiles/<kernel>_<workload>_traffic.json
+
+`traffic` scales each counter (KiB per dispatch) by what the same counter reads for a
+plain device-to-device copy of known size in the same run (the runtime's copy kernel),
+and sums the named kernels' dispatches into HBM bytes per call.  The JSON carries a
+hash of the kernel sources so that a later source change makes it stale.  Inputs are
+either rocprofv3's CSV files or its default SQLite database (`*_results.db`).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sqlite3
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("attn.hip", "lcs_internal.h")]
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(n: str) -> str:
+    for junk in ("lcs::(anonymous namespace)::", "(lcs::AttnArgs)", "(lcs::SelArgs, int)", "(lcs::SelArgs)",
+                 "void "):
+        n = n.replace(junk, "")
+    return n.strip()
+
+
+def stats_rows(path: str):
+    if not path.endswith(".db"):
+        return list(csv.DictReader(open(path)))
+    durs = defaultdict(list)
+    for name, d in sqlite3.connect(path).execute("select name, duration from kernels"):
+        durs[name].append(float(d))
+    grand = sum(sum(v) for v in durs.values()) or 1.0
+    return [{"Name": k, "Calls": str(len(v)), "AverageNs": sum(v) / len(v), "MinNs": min(v), "MaxNs": max(v),
+             "TotalDurationNs": sum(v), "Percentage": 100.0 * sum(v) / grand} for k, v in durs.items()]
+
+
+def stats(args) -> None:
+    rows = stats_rows(args.csv)
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = [f"# {args.title}", "", "Command (run from the repository root):", "", "```", args.command, "```", "",
+           "| kernel | calls | avg us | min us | max us | total us | % |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f | %.2f |" % (
+            short_name(r["Name"])[:70], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e3, float(r["Percentage"])))
+    if args.note:
+        out += ["", args.note]
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+
+
+def per_kernel(path: str, counter: str):
+    """kernel name -> list of counter values (KiB), one per dispatch."""
+    vals = defaultdict(list)
+    if path.endswith(".db"):
+        q = "select kernel_name, value from counters_collection where counter_name = ?"
+        for name, v in sqlite3.connect(path).execute(q, (counter,)):
+            vals[short_name(name)].append(float(v))
+        return vals
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        vals[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic(args) -> None:
+    res = {"kernel_source_hash": kernel_source_hash(), "kernels": {}, "copy_bytes": args.copy_bytes,
+           "commands": {"FETCH_SIZE": args.command_fetch, "WRITE_SIZE": args.command_write}}
+    total = 0.0
+    for counter, path in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
+        vals = per_kernel(path, counter)
+        copies = vals.get(COPY_KERNEL, [])
+        if not copies:
+            sys.exit(f"no {COPY_KERNEL} dispatch with {counter} in {path}")
+        copy_kib = max(copies)
+        factor = (args.copy_bytes / 1024.0) / copy_kib
+        res[f"{counter}_copy_kib"] = copy_kib
+        res[f"{counter}_factor"] = round(factor, 5)
+        for k in args.kernel:
+            if k not in vals:
+                sys.exit(f"kernel {k!r} has no {counter} values in {path}; have {sorted(vals)}")
+            v = vals[k]
+            avg_kib = sum(v) / len(v)
+            ent = res["kernels"].setdefault(k, {})
+            ent[f"{counter}_kib_avg"] = round(avg_kib, 1)
+            ent[f"{counter}_dispatches"] = len(v)
+            ent[f"{counter}_bytes_scaled"] = round(avg_kib * 1024.0 * factor)
+            total += avg_kib * 1024.0 * factor
+    res["hbm_bytes_per_launch"] = round(total)
+    if args.algorithmic_bytes:
+        res["algorithmic_bytes_per_launch"] = args.algorithmic_bytes
+        res["traffic_over_algorithmic"] = round(total / args.algorithmic_bytes, 4)
+    with open(args.out, "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+
+
+def main(argv=None) -> None:
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = p.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", default="rocprofv3 kernel statistics")
+    s.add_argument("--note", default="")
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--kernel", action="append", required=True)
+    t.add_argument("--algorithmic-bytes", type=int, default=0)
+    t.add_argument("--command-fetch", required=True)
+    t.add_argument("--command-write", required=True)
+    t.add_argument("--out", required=True)
+    a = p.parse_args(argv)
+    stats(a) if a.cmd == "stats" else traffic(a)
+
+
+if __name__ == "__main__":
+    main()
