@@ -173,7 +173,8 @@ lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, in
  *  tail_begin, tail_len  device int32 [B]: every row also sees the tail slots
  *               tail_begin[b] + j, j < tail_len[b] (the tokens written since the
  *               selection, the current one included), filtered by tail_mask.
- *  max_tail_len host bound on tail_len, sizes the launch.
+ *  max_tail_len host bound on tail_len, sizes the launch; larger tail_len values are
+ *               clamped to it.
  *  tail_mask    device uint64 [B][n_q] or NULL: row i sees tail slot j iff bit j
  *               is set (needs tail_len <= 64); NULL = every row sees the whole tail.
  *  out, lse     as for lcs_verify_attn.  A row that sees nothing gets out = 0

@@ -41,6 +41,9 @@
 
 #include <math.h>
 
+
+#include <type_traits>
+
 namespace lcs {
 namespace {
 
@@ -68,15 +71,29 @@ __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
 // max over the four lanes {l, l^16, l^32, l^48} (the 4 lane groups holding one MFMA
 // column) with gfx950 permlane swaps: VALU only, no LDS round trip.
 __device__ __forceinline__ float fmax2(float a, float b) { return a > b ? a : b; }
+// three-input max in one VALU op (fmaxf would first quieten every input); the
+// operands are never NaN here: masked entries are -inf, all others are finite
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float colmax4(float v) {
   const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const float a = fmax2(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  const float a = max3f(__uint_as_float(s32[0]), __uint_as_float(s32[1]), __uint_as_float(s32[1]));
   const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
-  return fmax2(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  return max3f(__uint_as_float(s16[0]), __uint_as_float(s16[1]), __uint_as_float(s16[1]));
 }
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// two floats -> packed bf16 pair (x in the low half), round to nearest even, one op
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x, y}, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) {
@@ -108,6 +125,15 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// compile-time loop: f(integral_constant<int, I>) for I in [B, E)
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 struct SeqInfo {
   int L, cnt, tb, tl, U, T;
   const int32_t* list;
@@ -125,7 +151,7 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, int g) {
     si.T = (si.L + a.n_q + kStepTokens - 1) / kStepTokens;
   } else {
     si.tb = a.tail_begin[b];
-    si.tl = max(a.tail_len[b], 0);
+    si.tl = min(max(a.tail_len[b], 0), a.max_tail_len);
     if (MODE == MODE_BLOCK) {
       const size_t o = (size_t)(b * a.Hkv + g);
       si.U = min(max(a.ucount[o], 0), a.ucap);
@@ -234,8 +260,9 @@ __device__ __forceinline__ void meta_stage_a(const AttnArgs& a, const SeqInfo& s
   for (int r = 0; r < kTokPerLane; ++r) {
     const int tok = lane + 64 * r;
     const int u = (wbase + tok / kStepTokens) * kStepTokens + (tok & (kStepTokens - 1));
-    // every lane issues (clamped into the list, or the block table when the list is empty)
-    const int32_t* src = (si.cnt > 0) ? si.list + min(max(u, 0), si.cnt - 1) : a.bt;
+    // every lane issues, clamped into the list's cap entries (the block table stands in
+    // when cap is 0); the count itself is not needed yet, so this can go out first
+    const int32_t* src = (a.cap > 0) ? si.list + min(max(u, 0), a.cap - 1) : a.bt;
     dma4(src, sidx + 64 * r);
   }
 }
@@ -322,386 +349,34 @@ __device__ __forceinline__ void step_dma(const AttnArgs& a, const int32_t* rows,
   for (int t = 0; t < 8; ++t) dma16(a.v + (size_t)max(rv[t], 0) * D + dx, slot + (2 * IPT + t) * 1024);
 }
 
-template <int D, int QT, int MODE>
-__global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
-  constexpr int KS = D / 32;                  // k-steps of the QK^T product
-  constexpr int NDMA = 2 * KS + 8;            // 16-byte DMAs per lane per step
-  constexpr int kSlot = NDMA * 1024;          // ring slot bytes per wave
-  constexpr int QCH = D / 8;                  // 16-byte chunks per Q row
-  constexpr int kPer = 4 * 8 + 2;             // merge floats per lane per q-tile
-  constexpr size_t kQBytes = (size_t)QT * 16 * D * 2;
-  constexpr size_t kWaveBytes = sizeof(WaveMeta) + 2 * (size_t)kSlot;
-  constexpr size_t kLoopBytes = kQBytes + kWaves * kWaveBytes;
-  constexpr size_t kMergeBytes = (size_t)kWaves * QT * kPer * 64 * 4;
-  constexpr size_t kSmem = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmem];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int x = lane & 15;
-  const int j = lane >> 4;
-  const int s = blockIdx.x;
-  const int g = blockIdx.y % a.Hkv;
-  const int rc = blockIdx.y / a.Hkv;
-  const int b = blockIdx.z;
-  const int r0 = rc * kMaxRowsPerWG;
-  const int nrows = min(kMaxRowsPerWG, a.rows - r0);
-
-  uint16_t* s_q = reinterpret_cast<uint16_t*>(smem_raw);
-  unsigned char* wbase_lds = smem_raw + kQBytes + (size_t)wave * kWaveBytes;
-  WaveMeta& wm = *reinterpret_cast<WaveMeta*>(wbase_lds);
-  char* ring = reinterpret_cast<char*>(wbase_lds + sizeof(WaveMeta));
-  float* s_merge = reinterpret_cast<float*>(smem_raw);
-
-  const SeqInfo si = seq_info<MODE>(a, b, g);
-  const int st0 = s * a.sps;
-  const int st1 = (s == a.n_split - 1) ? si.T : min(si.T, st0 + a.sps);
-  // contiguous per-wave step ranges
-  const int nst = max(st1 - st0, 0);
-  const int qw = (nst + kWaves - 1) / kWaves;
-  const int w0 = st0 + wave * qw;
-  const int w1 = min(st1, w0 + qw);
-
-  // Column mask of verifier/tail slot `lane`: bit i = row i sees that slot.
-  uint64_t colmask;
-  if (a.rowmask != nullptr) {
-    colmask = 0;
-    const uint64_t* rm = a.rowmask + (size_t)b * a.n_q;
-    for (int i = 0; i < a.n_q; ++i) colmask |= ((rm[i] >> lane) & 1ull) << i;
+// The same DMAs one at a time, so that a refill can be spread through the compute of
+// a step: dma_rows reads, for this lane, the cache row of each of the NDMA pieces, and
+// dma_piece issues piece n (pieces 0 .. 2*IPT-1 are K, the last 8 are V).
+template <int D>
+struct DmaGeom {
+  static constexpr int RCH = D / 8, RPI = 64 / RCH, IPT = 16 / RPI, NK = 2 * IPT, N = NK + 8;
+};
+template <int D>
+__device__ __forceinline__ void dma_rows(const int32_t* rows, int lane, int j, int (&sr)[DmaGeom<D>::N]) {
+  using G = DmaGeom<D>;
+  const int rq = lane / G::RCH;
+#pragma unroll
+  for (int n = 0; n < G::NK; ++n) sr[n] = rows[16 * (n / G::IPT) + G::RPI * (n % G::IPT) + rq];
+  const int4 rv0 = *reinterpret_cast<const int4*>(rows + 4 * j);
+  const int4 rv1 = *reinterpret_cast<const int4*>(rows + 16 + 4 * j);
+  sr[G::NK + 0] = rv0.x; sr[G::NK + 1] = rv0.y; sr[G::NK + 2] = rv0.z; sr[G::NK + 3] = rv0.w;
+  sr[G::NK + 4] = rv1.x; sr[G::NK + 5] = rv1.y; sr[G::NK + 6] = rv1.z; sr[G::NK + 7] = rv1.w;
+}
+template <int D, int n>
+__device__ __forceinline__ void dma_piece(const AttnArgs& a, const int (&sr)[DmaGeom<D>::N], char* slot, int lane,
+                                          int x) {
+  using G = DmaGeom<D>;
+  if (n < G::NK) {
+    const int tok = 16 * (n / G::IPT) + G::RPI * (n % G::IPT) + lane / G::RCH;
+    const int c = (lane % G::RCH) ^ (tok % G::RCH);
+    dma16(a.k + (size_t)max(sr[n], 0) * D + 8 * c, slot + n * 1024);
   } else {
-    colmask = (MODE == MODE_DENSE) ? (kAll << lane) : kAll;
-  }
-
-  // verifier row index of this lane's q-row in each tile (64 = padding row)
-  int rowi[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int r = 16 * qt + x;
-    rowi[qt] = (r < nrows) ? (r0 + r) / a.G : 64;
-  }
-  const bool collect = MODE == MODE_DENSE && a.logits != nullptr;
-
-  float m[QT], l[QT];
-  f32x4 O[QT][8];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    m[qt] = -INFINITY;
-    l[qt] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) O[qt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // Prologue: window-0 metadata DMAs go out together with the Q loads, so the block-table
-  // round trip overlaps the Q fetch and the Q -> LDS copy.
-  if (w0 < w1) {
-    if (MODE == MODE_LIST_SHARED) meta_stage_a<MODE>(a, si, w0, lane, wm, 0);
-    else meta_stage_b<MODE>(a, si, b, w0, w1, lane, wm, 0);
-  }
-  // Q rows of this workgroup: 16-byte chunk c of row r goes to LDS chunk c ^ (r % QCH)
-  constexpr int kQPer = (QT * 16 * QCH + 255) / 256;
-  u32x4 qv[kQPer];
-#pragma unroll
-  for (int u = 0; u < kQPer; ++u) {
-    const int e = tid + 256 * u;
-    const int r = e / QCH;
-    const int c = e - r * QCH;
-    qv[u] = u32x4{0, 0, 0, 0};
-    if (e < QT * 16 * QCH && r < nrows) {
-      const int rr = r0 + r;
-      const int i = rr / a.G;
-      const int h = g * a.G + (rr - i * a.G);
-      qv[u] = *reinterpret_cast<const u32x4*>(a.q + ((size_t)(b * a.n_q + i) * a.Hq + h) * D + 8 * c);
-    }
-  }
-  wait_vm<0>();
-  if (MODE == MODE_LIST_SHARED && w0 < w1) meta_stage_b<MODE>(a, si, b, w0, w1, lane, wm, 0);
-#pragma unroll
-  for (int u = 0; u < kQPer; ++u) {
-    const int e = tid + 256 * u;
-    const int r = e / QCH;
-    const int c = e - r * QCH;
-    if (e < QT * 16 * QCH) *reinterpret_cast<u32x4*>(s_q + (r * QCH + (c ^ (r % QCH))) * 8) = qv[u];
-  }
-  __syncthreads();   // Q in LDS
-  // Q^T B-operands of this lane (q-row x of each tile, 8 dims per k-step), kept in registers
-  u32x4 qop[QT][KS];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int r = 16 * qt + x;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int c = 4 * ks + j;
-      qop[qt][ks] = *reinterpret_cast<const u32x4*>(s_q + (r * QCH + (c ^ (r % QCH))) * 8);
-    }
-  }
-
-  if (w0 < w1) {
-    wait_vm<0>();
-    meta_stage_c<MODE>(a, si, g, w0, w1, colmask, lane, wm, 0);
-    wait_lgkm0();
-    step_dma<D>(a, wm.row[0], ring, lane, x, j);
-    if (w0 + 1 < w1) step_dma<D>(a, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
-    // software pipeline: iteration s issues S(s), then PV(s-1) from the previous
-    // iteration's registers, so the matrix core works through PV(s-1) while the VALU
-    // does softmax(s).  The first PV runs on zero P and V (adds exact zeros).
-    u32x4 vprev[8], phi[QT], plo[QT];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) vprev[t] = u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) phi[qt] = plo[qt] = u32x4{0, 0, 0, 0};
-    const float c2 = a.scale_log2;
-    for (int wb = w0, k = 0; wb < w1; wb += kMW, ++k) {
-      const int buf = k & 1;
-      const bool next_win = wb + kMW < w1;
-      const int nloc = min(kMW, w1 - wb);
-      for (int ls = 0; ls < nloc; ++ls) {
-        const int step = wb + ls;
-        char* slot = ring + ((step - w0) & 1) * kSlot;
-        // this step's DMAs are done once at most one step's worth is outstanding
-        if (step + 1 < w1) wait_vm<NDMA>();
-        else wait_vm<0>();
-        u32x4 kop[2][KS], vcur[8];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int kpos = ((4 * ks + j) ^ (x % QCH)) * 16;   // swizzled chunk of row x
-          kop[0][ks] = *reinterpret_cast<const u32x4*>(slot + x * (2 * D) + kpos);
-          kop[1][ks] = *reinterpret_cast<const u32x4*>(slot + (16 + x) * (2 * D) + kpos);
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) vcur[t] = *reinterpret_cast<const u32x4*>(slot + (2 * KS + t) * 1024 + 16 * lane);
-        const bool full = wm.full[buf][ls] != 0;
-        if (!full) {
-          // invalid slots were loaded from row 0: zero them, since a masked weight
-          // times a NaN in an unused cache slot would still poison O
-          const int32_t* rows = wm.row[buf] + ls * kStepTokens;
-          const int4 rv0 = *reinterpret_cast<const int4*>(rows + 4 * j);
-          const int4 rv1 = *reinterpret_cast<const int4*>(rows + 16 + 4 * j);
-          const int rv[8] = {rv0.x, rv0.y, rv0.z, rv0.w, rv1.x, rv1.y, rv1.z, rv1.w};
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-            if (rv[t] < 0) vcur[t] = u32x4{0, 0, 0, 0};
-        }
-        wait_lgkm0();   // the slot is in registers: it may be refilled
-        // next window's metadata, one stage per step, issued before the data DMAs
-        if (next_win) {
-          if (ls == 0) meta_stage_a<MODE>(a, si, wb + kMW, lane, wm, buf ^ 1);
-          if (ls == 1) meta_stage_b<MODE>(a, si, b, wb + kMW, w1, lane, wm, buf ^ 1);
-          if (ls == 2) meta_stage_c<MODE>(a, si, g, wb + kMW, w1, colmask, lane, wm, buf ^ 1);
-        }
-        // ---- S^T(s) = K Q^T for two 16-token tiles
-        f32x4 S[2][QT];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          S[0][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          S[1][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            S[0][qt] = mfma16(kop[0][ks], qop[qt][ks], S[0][qt]);
-            S[1][qt] = mfma16(kop[1][ks], qop[qt][ks], S[1][qt]);
-          }
-        }
-        // ---- O^T += V^T(s-1) P^T(s-1), one transposed V tile at a time
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          u32x4 vte;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t w0v = vprev[2 * w][e >> 1], w1v = vprev[2 * w + 1][e >> 1];
-            vte[w] = (e & 1) ? ((w0v >> 16) | (w1v & 0xffff0000u)) : ((w0v & 0xffffu) | (w1v << 16));
-          }
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            O[qt][e] = mfma16(vte, phi[qt], O[qt][e]);
-            O[qt][e] = mfma16(vte, plo[qt], O[qt][e]);
-          }
-        }
-
-        // ---- Collect-2-Query: scaled logits of the two collected rows, prefix columns only.
-        //      Stored before the next DMA batch is issued: stores count in vmcnt too, and
-        //      one issued after the batch would make the next step's wait drain the batch.
-        if (collect) {
-          const int p0 = step * kStepTokens + 4 * j;
-          const bool whole = a.lvec4 && step * kStepTokens + kStepTokens <= si.L;
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            const bool m0 = rowi[qt] == a.c0, m1 = rowi[qt] == a.c1;
-            if (!__any(m0 || m1)) continue;
-            const int rr = r0 + 16 * qt + x;
-            const int h = g * a.G + (rr - rowi[qt] * a.G);
-            float* base = a.logits + (size_t)(b * a.Hq + h) * 2 * a.logits_ld + p0;
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              if (!(c == 0 ? m0 : m1)) continue;
-              float* dst = base + c * a.logits_ld;
-              if (whole) {
-                *reinterpret_cast<f32x4*>(dst) = S[0][qt] * a.scale;
-                *reinterpret_cast<f32x4*>(dst + 16) = S[1][qt] * a.scale;
-              } else {
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                  for (int i = 0; i < 4; ++i)
-                    if (p0 + 16 * tt + i < si.L) dst[16 * tt + i] = S[tt][qt][i] * a.scale;
-              }
-            }
-          }
-        }
-        if (step + 2 < w1) {
-          const int ns = ls + 2;
-          const int32_t* nrows_p = (ns < kMW) ? wm.row[buf] + ns * kStepTokens
-                                              : wm.row[buf ^ 1] + (ns - kMW) * kStepTokens;
-          step_dma<D>(a, nrows_p, slot, lane, x, j);
-        }
-
-        // ---- online softmax(s) per q-tile.  The reference max m only moves when a row's
-        //      max grows by more than 2^kTau, so the O rescale (AGPR round trips) is rare;
-        //      weights stay below 2^kTau.  P goes out as bf16 hi + lo B-operands.
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          float t8[8];
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) t8[4 * tt + i] = S[tt][qt][i];
-          if (!full) {
-            const uint64_t* vr = wm.vis[buf] + ls * kStepTokens;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (((vr[16 * tt + 4 * j + i] >> rowi[qt]) & 1ull) == 0) t8[4 * tt + i] = -INFINITY;
-          }
-          const float rmax = colmax4(fmax2(fmax2(fmax2(t8[0], t8[1]), fmax2(t8[2], t8[3])),
-                                           fmax2(fmax2(t8[4], t8[5]), fmax2(t8[6], t8[7]))));
-          const float mx = rmax * c2;
-          const bool grow = mx > m[qt] + kTau;
-          if (__any(grow)) {
-            // rows that keep their reference (possibly still -inf) keep alpha = 1
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m[qt] - mx) : 1.f;
-            l[qt] *= alpha;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) O[qt][e] *= alpha;
-            m[qt] = grow ? mx : m[qt];
-          }
-          const float nms = (m[qt] == -INFINITY) ? 0.f : -m[qt];
-          float psum = 0.f;
-#pragma unroll
-          for (int u = 0; u < 8; u += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(t8[u], c2, nms));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(t8[u + 1], c2, nms));
-            psum += p0 + p1;
-            const uint32_t h0 = bf16_rne(p0), h1 = bf16_rne(p1);
-            const uint32_t l0 = bf16_rne(p0 - bf16_to_f32(h0));
-            const uint32_t l1 = bf16_rne(p1 - bf16_to_f32(h1));
-            phi[qt][u >> 1] = h0 | (h1 << 16);
-            plo[qt][u >> 1] = l0 | (l1 << 16);
-          }
-          l[qt] += psum;
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) vprev[t] = vcur[t];
-      }
-    }
-    // drain: PV of the last step
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      u32x4 vte;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t w0v = vprev[2 * w][e >> 1], w1v = vprev[2 * w + 1][e >> 1];
-        vte[w] = (e & 1) ? ((w0v >> 16) | (w1v & 0xffff0000u)) : ((w0v & 0xffffu) | (w1v << 16));
-      }
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        O[qt][e] = mfma16(vte, phi[qt], O[qt][e]);
-        O[qt][e] = mfma16(vte, plo[qt], O[qt][e]);
-      }
-    }
-  }
-
-  // full row sums (fixed order)
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    l[qt] += __shfl_xor(l[qt], 16);
-    l[qt] += __shfl_xor(l[qt], 32);
-  }
-
-  // ---- merge the 4 waves' states through LDS.  Every wave publishes (m, l, O); then
-  //      wave w merges dims {8i + 2w, 8i + 2w + 1} of every row, in wave order 0..3.
-  __syncthreads();   // every wave is done with Q, its metadata and its ring
-  {
-    float* w = s_merge + (size_t)wave * QT * kPer * 64;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[(qt * kPer + e * 4 + i) * 64 + lane] = O[qt][e][i];
-      w[(qt * kPer + 32) * 64 + lane] = m[qt];
-      w[(qt * kPer + 33) * 64 + lane] = l[qt];
-    }
-  }
-  __syncthreads();
-  const int e0 = 2 * wave;          // this wave's two O tiles (dims 32j + 8i + e0 + {0, 1})
-  float mo[QT], lo_[QT], oo[QT][2][4];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int ow = 0; ow < kWaves; ++ow) M = fmax2(M, s_merge[((size_t)ow * QT * kPer + qt * kPer + 32) * 64 + lane]);
-    const float Ms = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oo[qt][h][i] = 0.f;
-#pragma unroll
-    for (int ow = 0; ow < kWaves; ++ow) {
-      const float* w = s_merge + (size_t)ow * QT * kPer * 64;
-      const float mw = w[(qt * kPer + 32) * 64 + lane];
-      const float sc = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Ms);
-      L += sc * w[(qt * kPer + 33) * 64 + lane];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) oo[qt][h][i] += sc * w[(qt * kPer + (e0 + h) * 4 + i) * 64 + lane];
-    }
-    mo[qt] = M;
-    lo_[qt] = L;
-  }
-
-  // ---- write: lane (x, j) holds q-row x, dims 32j + 8i + e0 + {0,1} (i < 4); for d = 64
-  //      only j < 2 holds real dims.  Final output with one split, else a partial.
-  if (32 * j >= D) return;
-  const size_t pstride = (size_t)kMaxRowsPerWG * (D + 2);
-  const size_t pidx = ((size_t)(b * a.Hkv + g) * a.n_rc + rc) * a.n_split + s;
-  const int d0 = 32 * j + e0;
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int r = 16 * qt + x;
-    if (r >= nrows) continue;
-    if (a.n_split == 1) {
-      const int rr = r0 + r;
-      const int i = rr / a.G;
-      const int h = g * a.G + (rr - i * a.G);
-      const float inv = (lo_[qt] > 0.f) ? 1.f / lo_[qt] : 0.f;
-      float* op = a.out + ((size_t)(b * a.n_q + i) * a.Hq + h) * D + d0;
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        *reinterpret_cast<float2*>(op + 8 * i4) = make_float2(oo[qt][0][i4] * inv, oo[qt][1][i4] * inv);
-      if (wave == 0 && j == 0 && a.lse != nullptr)
-        a.lse[(size_t)(b * a.n_q + i) * a.Hq + h] =
-            (lo_[qt] > 0.f) ? (mo[qt] + __log2f(lo_[qt])) * kLn2 : -INFINITY;
-    } else {
-      float* pp = a.part + pidx * pstride;
-      float* op = pp + (size_t)r * D + d0;
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) *reinterpret_cast<float2*>(op + 8 * i4) = make_float2(oo[qt][0][i4], oo[qt][1][i4]);
-      if (wave == 0 && j == 0) {
-        pp[(size_t)kMaxRowsPerWG * D + r] = mo[qt];
-        pp[(size_t)kMaxRowsPerWG * D + kMaxRowsPerWG + r] = lo_[qt];
-      }
-    }
+    dma16(a.v + (size_t)max(sr[n], 0) * D + 8 * (x & (D / 8 - 1)), slot + n * 1024);
   }
 }
 
@@ -717,18 +392,15 @@ __device__ __forceinline__ float lane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-template <int D, int MODE>
-__global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
-  const int pid = blockIdx.x;                   // (b*Hkv + g)*n_rc + rc
+// Merge the split-K partials of q-row r of pair pid (= (b*Hkv + g)*n_rc + rc) in split
+// order and write its output row and lse.  One wave.
+template <int D>
+__device__ __forceinline__ void merge_row(const AttnArgs& a, int pid, int r, int lane) {
   const int rc = pid % a.n_rc;
   const int bg = pid / a.n_rc;
   const int g = bg % a.Hkv;
   const int b = bg / a.Hkv;
   const int r0 = rc * kMaxRowsPerWG;
-  const int nrows = min(kMaxRowsPerWG, a.rows - r0);
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.y * kCombineRows + (threadIdx.x >> 6);
-  if (r >= nrows) return;
   const int ns = a.n_split;                     // 2 .. kMaxSplits = 128
   const size_t pstride = (size_t)kMaxRowsPerWG * (D + 2);
   const float* base = a.part + (size_t)pid * ns * pstride;
@@ -794,6 +466,423 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   for (int c = 0; c < CPL; ++c) op[c] = acc[c] * inv;
   if (lane == 0 && a.lse != nullptr)
     a.lse[(size_t)(b * a.n_q + i) * a.Hq + h] = (Ls > 0.f) ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+}
+
+template <int D, int MODE>
+__global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
+  const int pid = blockIdx.x;                   // (b*Hkv + g)*n_rc + rc
+  const int rc = pid % a.n_rc;
+  const int nrows = min(kMaxRowsPerWG, a.rows - rc * kMaxRowsPerWG);
+  const int r = blockIdx.y * kCombineRows + (threadIdx.x >> 6);
+  if (r >= nrows) return;
+  merge_row<D>(a, pid, r, threadIdx.x & 63);
+}
+
+template <int D, int QT, int MODE>
+__global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;                  // k-steps of the QK^T product
+  constexpr int NDMA = DmaGeom<D>::N;         // 16-byte DMAs per lane per step
+  constexpr int kSlot = NDMA * 1024;          // ring slot bytes per wave
+  constexpr int QCH = D / 8;                  // 16-byte chunks per Q row
+  constexpr int kPer = 4 * 8 + 2;             // merge floats per lane per q-tile
+  constexpr size_t kQBytes = (size_t)QT * 16 * D * 2;
+  constexpr size_t kWaveBytes = sizeof(WaveMeta) + 2 * (size_t)kSlot;
+  constexpr size_t kLoopBytes = kQBytes + kWaves * kWaveBytes;
+  constexpr size_t kMergeBytes = (size_t)kWaves * QT * kPer * 64 * 4;
+  constexpr size_t kSmem = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmem];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int x = lane & 15;
+  const int j = lane >> 4;
+  const int s = blockIdx.x;
+  const int g = blockIdx.y % a.Hkv;
+  const int rc = blockIdx.y / a.Hkv;
+  const int b = blockIdx.z;
+  const int r0 = rc * kMaxRowsPerWG;
+  const int nrows = min(kMaxRowsPerWG, a.rows - r0);
+
+  uint16_t* s_q = reinterpret_cast<uint16_t*>(smem_raw);
+  unsigned char* wbase_lds = smem_raw + kQBytes + (size_t)wave * kWaveBytes;
+  WaveMeta& wm = *reinterpret_cast<WaveMeta*>(wbase_lds);
+  char* ring = reinterpret_cast<char*>(wbase_lds + sizeof(WaveMeta));
+  float* s_merge = reinterpret_cast<float*>(smem_raw);
+
+  const SeqInfo si = seq_info<MODE>(a, b, g);
+  // balanced contiguous step ranges: the n_split * kWaves waves of this (sequence, KV
+  // head) split its steps evenly (to within one step); a workgroup's waves are adjacent
+  // Token-list modes split the launch's step bound (cap + max tail) instead of the
+  // sequence's own, so that the index-list DMA can go out before the sequence's counts
+  // arrive; waves past the sequence's end then have nothing to do.
+  const long long nwv = (long long)a.n_split * kWaves;
+  const long long gwv = (long long)s * kWaves + wave;
+  const long long Tsp = (MODE == MODE_LIST_SHARED) ? (long long)a.T_max : (long long)si.T;
+  const int w0 = (int)(gwv * Tsp / nwv);
+  const int w1s = (int)((gwv + 1) * Tsp / nwv);
+  const int w1 = min(w1s, si.T);
+
+  // Column mask of verifier/tail slot `lane`: bit i = row i sees that slot.
+  uint64_t colmask;
+  if (a.rowmask != nullptr) {
+    colmask = 0;
+    const uint64_t* rm = a.rowmask + (size_t)b * a.n_q;
+    for (int i = 0; i < a.n_q; ++i) colmask |= ((rm[i] >> lane) & 1ull) << i;
+  } else {
+    colmask = (MODE == MODE_DENSE) ? (kAll << lane) : kAll;
+  }
+
+  // verifier row index of this lane's q-row in each tile (64 = padding row)
+  int rowi[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int r = 16 * qt + x;
+    rowi[qt] = (r < nrows) ? (r0 + r) / a.G : 64;
+  }
+  const bool collect = MODE == MODE_DENSE && a.logits != nullptr;
+
+  float m[QT], l[QT];
+  f32x4 O[QT][8];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m[qt] = -INFINITY;
+    l[qt] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) O[qt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // Prologue: window-0 metadata DMAs go out together with the Q loads, so the block-table
+  // round trip overlaps the Q fetch and the Q -> LDS copy.
+  if (MODE == MODE_LIST_SHARED) {
+    if (w0 < w1s) meta_stage_a<MODE>(a, si, w0, lane, wm, 0);
+  } else if (w0 < w1) {
+    meta_stage_b<MODE>(a, si, b, w0, w1, lane, wm, 0);
+  }
+  // Q rows of this workgroup: 16-byte chunk c of row r goes to LDS chunk c ^ (r % QCH)
+  constexpr int kQPer = (QT * 16 * QCH + 255) / 256;
+  u32x4 qv[kQPer];
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int e = tid + 256 * u;
+    const int r = e / QCH;
+    const int c = e - r * QCH;
+    qv[u] = u32x4{0, 0, 0, 0};
+    if (e < QT * 16 * QCH && r < nrows) {
+      const int rr = r0 + r;
+      const int i = rr / a.G;
+      const int h = g * a.G + (rr - i * a.G);
+      qv[u] = *reinterpret_cast<const u32x4*>(a.q + ((size_t)(b * a.n_q + i) * a.Hq + h) * D + 8 * c);
+    }
+  }
+  wait_vm<0>();
+  if (MODE == MODE_LIST_SHARED && w0 < w1) meta_stage_b<MODE>(a, si, b, w0, w1, lane, wm, 0);
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int e = tid + 256 * u;
+    const int r = e / QCH;
+    const int c = e - r * QCH;
+    if (e < QT * 16 * QCH) *reinterpret_cast<u32x4*>(s_q + (r * QCH + (c ^ (r % QCH))) * 8) = qv[u];
+  }
+  __syncthreads();   // Q in LDS
+  // Q^T B-operands of this lane (q-row x of each tile, 8 dims per k-step), kept in registers
+  u32x4 qop[QT][KS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int r = 16 * qt + x;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = 4 * ks + j;
+      qop[qt][ks] = *reinterpret_cast<const u32x4*>(s_q + (r * QCH + (c ^ (r % QCH))) * 8);
+    }
+  }
+
+  if (w0 < w1) {
+    wait_vm<0>();
+    meta_stage_c<MODE>(a, si, g, w0, w1, colmask, lane, wm, 0);
+    wait_lgkm0();
+    step_dma<D>(a, wm.row[0], ring, lane, x, j);
+    if (w0 + 1 < w1) step_dma<D>(a, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
+    // Software pipeline.  Iteration s waits for slot s and moves it to registers, issues
+    // the metadata stage, runs S(s) on the matrix core, stores S(s)'s collected logits,
+    // and refills slot s with step s+2 (stores count in vmcnt, so they must precede the
+    // batch that the next wait leaves outstanding).  Both ring slots are then in flight
+    // while one straight-line block runs PV(s-1) from the previous iteration's registers
+    // on the matrix core and softmax(s) on the VALU, interleaved by the scheduler.  A
+    // rescale decided by softmax(s) is applied to O right after that block, once PV(s-1)
+    // is in, so that PV(s) in the next iteration adds to O on the new reference.
+    u32x4 vprev[8], phi[QT], plo[QT];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) vprev[t] = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) phi[qt] = plo[qt] = u32x4{0, 0, 0, 0};
+    f32x4 S[2][QT];   // S^T of the current step
+    float alpha[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) alpha[qt] = 1.f;
+    bool pend = false;
+    const float c2 = a.scale_log2;
+
+    // O^T += V^T(s-1) P^T(s-1), one transposed V tile at a time; hook(e) runs after tile e
+    auto pv = [&](auto hook) {
+      static_for<0, 8>([&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        u32x4 vte;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t w0v = vprev[2 * w][e >> 1], w1v = vprev[2 * w + 1][e >> 1];
+          // even e: low halves of (w0v, w1v); odd e: high halves
+          vte[w] = __builtin_amdgcn_perm(w1v, w0v, (e & 1) ? 0x07060302u : 0x05040100u);
+        }
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          O[qt][e] = mfma16(vte, phi[qt], O[qt][e]);
+          O[qt][e] = mfma16(vte, plo[qt], O[qt][e]);
+        }
+        hook(ec);
+      });
+    };
+    auto rescale = [&]() {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) O[qt][e] *= alpha[qt];
+    };
+    // Collect-2-Query: scaled logits of the two collected rows, prefix columns only
+    auto store_logits = [&](int st) {
+      const int p0 = st * kStepTokens + 4 * j;
+      const bool whole = a.lvec4 && st * kStepTokens + kStepTokens <= si.L;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const bool m0 = rowi[qt] == a.c0, m1 = rowi[qt] == a.c1;
+        if (!__any(m0 || m1)) continue;
+        const int rr = r0 + 16 * qt + x;
+        const int h = g * a.G + (rr - rowi[qt] * a.G);
+        float* base = a.logits + (size_t)(b * a.Hq + h) * 2 * a.logits_ld + p0;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          if (!(c == 0 ? m0 : m1)) continue;
+          float* dst = base + c * a.logits_ld;
+          if (whole) {
+            *reinterpret_cast<f32x4*>(dst) = S[0][qt] * a.scale;
+            *reinterpret_cast<f32x4*>(dst + 16) = S[1][qt] * a.scale;
+          } else {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (p0 + 16 * tt + i < si.L) dst[16 * tt + i] = S[tt][qt][i] * a.scale;
+          }
+        }
+      }
+    };
+    // PV(s-1) and softmax(s).  The reference max m only moves when a row's max grows
+    // by more than 2^kTau, so the O rescale (AGPR round trips) is rare; weights stay
+    // below 2^kTau.  P goes out as bf16 hi + lo B-operands.
+    // The refill DMAs of the next-but-one step are spread over the PV tiles, so that
+    // their issue, which stalls while the memory pipeline is busy, overlaps compute.
+    // FAST: every token of the step is visible to every row and a refill is due.
+    auto block = [&](const uint64_t* vr, const int (&sr)[NDMA], char* slot, bool dma_due, auto fastc) {
+      constexpr bool FAST = decltype(fastc)::value;
+      pv([&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        static_for<e * NDMA / 8, (e + 1) * NDMA / 8>([&](auto nc) {
+          if (FAST || dma_due) dma_piece<D, decltype(nc)::value>(a, sr, slot, lane, x);
+        });
+      });
+      bool grow_any = false;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        float t8[8];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t8[4 * tt + i] = S[tt][qt][i];
+        if (!FAST) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (((vr[16 * tt + 4 * j + i] >> rowi[qt]) & 1ull) == 0) t8[4 * tt + i] = -INFINITY;
+        }
+        const float rmax = colmax4(max3f(max3f(t8[0], t8[1], t8[2]), max3f(t8[3], t8[4], t8[5]),
+                                         max3f(t8[6], t8[7], t8[7])));
+        const float mx = rmax * c2;
+        const bool grow = mx > m[qt] + kTau;
+        // rows that keep their reference (possibly still -inf) keep alpha = 1
+        alpha[qt] = grow ? __builtin_amdgcn_exp2f(m[qt] - mx) : 1.f;
+        m[qt] = grow ? mx : m[qt];
+        grow_any = grow_any || grow;
+        const float nms = (m[qt] == -INFINITY) ? 0.f : -m[qt];
+        float psum = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; u += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(t8[u], c2, nms));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(t8[u + 1], c2, nms));
+          psum += p0 + p1;
+          const uint32_t hw = pack_bf16(p0, p1);
+          phi[qt][u >> 1] = hw;
+          plo[qt][u >> 1] = pack_bf16(p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xffff0000u));
+        }
+        l[qt] = l[qt] * alpha[qt] + psum;
+      }
+      pend = __any(grow_any);
+    };
+
+    for (int wb = w0, k = 0; wb < w1; wb += kMW, ++k) {
+      const int buf = k & 1;
+      const bool next_win = wb + kMW < w1;
+      const int nloc = min(kMW, w1 - wb);
+      for (int ls = 0; ls < nloc; ++ls) {
+        const int step = wb + ls;
+        char* slot = ring + ((step - w0) & 1) * kSlot;
+        // this step's DMAs are done once at most one step's worth is outstanding
+        if (step + 1 < w1) wait_vm<NDMA>();
+        else wait_vm<0>();
+        u32x4 kop[2][KS], vcur[8];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int kpos = ((4 * ks + j) ^ (x % QCH)) * 16;   // swizzled chunk of row x
+          kop[0][ks] = *reinterpret_cast<const u32x4*>(slot + x * (2 * D) + kpos);
+          kop[1][ks] = *reinterpret_cast<const u32x4*>(slot + (16 + x) * (2 * D) + kpos);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vcur[t] = *reinterpret_cast<const u32x4*>(slot + (2 * KS + t) * 1024 + 16 * lane);
+        const bool full = wm.full[buf][ls] != 0;
+        if (!full) {
+          // invalid slots were loaded from row 0: zero them, since a masked weight
+          // times a NaN in an unused cache slot would still poison O
+          const int32_t* rows = wm.row[buf] + ls * kStepTokens;
+          const int4 rv0 = *reinterpret_cast<const int4*>(rows + 4 * j);
+          const int4 rv1 = *reinterpret_cast<const int4*>(rows + 16 + 4 * j);
+          const int rv[8] = {rv0.x, rv0.y, rv0.z, rv0.w, rv1.x, rv1.y, rv1.z, rv1.w};
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if (rv[t] < 0) vcur[t] = u32x4{0, 0, 0, 0};
+        }
+        wait_lgkm0();   // the slot is in registers: it may be refilled
+        // next window's metadata, one stage per step
+        if (next_win) {
+          if (ls == 0) meta_stage_a<MODE>(a, si, wb + kMW, lane, wm, buf ^ 1);
+          if (ls == 1) meta_stage_b<MODE>(a, si, b, wb + kMW, w1, lane, wm, buf ^ 1);
+          if (ls == 2) meta_stage_c<MODE>(a, si, g, wb + kMW, w1, colmask, lane, wm, buf ^ 1);
+        }
+        // S^T(s) = K Q^T for two 16-token tiles
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          S[0][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          S[1][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            S[0][qt] = mfma16(kop[0][ks], qop[qt][ks], S[0][qt]);
+            S[1][qt] = mfma16(kop[1][ks], qop[qt][ks], S[1][qt]);
+          }
+        }
+        if (collect) store_logits(step);
+        // cache rows of step s+2, which refills this slot (read even when no refill is
+        // due: the pointer stays inside this wave's metadata area)
+        const bool dma_due = step + 2 < w1;
+        int sr[NDMA];
+        {
+          const int ns = ls + 2;
+          dma_rows<D>((ns < kMW) ? wm.row[buf] + ns * kStepTokens : wm.row[buf ^ 1] + (ns - kMW) * kStepTokens,
+                      lane, j, sr);
+        }
+        if (full && dma_due) block(nullptr, sr, slot, true, std::true_type{});
+        else block(wm.vis[buf] + ls * kStepTokens, sr, slot, dma_due, std::false_type{});
+        if (pend) rescale();
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vprev[t] = vcur[t];
+      }
+    }
+    // drain: PV of the last step
+    pv([](auto) {});
+  }
+
+  // full row sums (fixed order)
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    l[qt] += __shfl_xor(l[qt], 16);
+    l[qt] += __shfl_xor(l[qt], 32);
+  }
+
+  // ---- merge the 4 waves' states through LDS.  Every wave publishes (m, l, O); then
+  //      wave w merges dims {8i + 2w, 8i + 2w + 1} of every row, in wave order 0..3.
+  __syncthreads();   // every wave is done with Q, its metadata and its ring
+  {
+    float* w = s_merge + (size_t)wave * QT * kPer * 64;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[(qt * kPer + e * 4 + i) * 64 + lane] = O[qt][e][i];
+      w[(qt * kPer + 32) * 64 + lane] = m[qt];
+      w[(qt * kPer + 33) * 64 + lane] = l[qt];
+    }
+  }
+  __syncthreads();
+  const int e0 = 2 * wave;          // this wave's two O tiles (dims 32j + 8i + e0 + {0, 1})
+  float mo[QT], lo_[QT], oo[QT][2][4];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int ow = 0; ow < kWaves; ++ow) M = fmax2(M, s_merge[((size_t)ow * QT * kPer + qt * kPer + 32) * 64 + lane]);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oo[qt][h][i] = 0.f;
+#pragma unroll
+    for (int ow = 0; ow < kWaves; ++ow) {
+      const float* w = s_merge + (size_t)ow * QT * kPer * 64;
+      const float mw = w[(qt * kPer + 32) * 64 + lane];
+      const float sc = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Ms);
+      L += sc * w[(qt * kPer + 33) * 64 + lane];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oo[qt][h][i] += sc * w[(qt * kPer + (e0 + h) * 4 + i) * 64 + lane];
+    }
+    mo[qt] = M;
+    lo_[qt] = L;
+  }
+
+  // ---- write: lane (x, j) holds q-row x, dims 32j + 8i + e0 + {0,1} (i < 4); for d = 64
+  //      only j < 2 holds real dims.  Final output with one split, else a partial.
+  const size_t pstride = (size_t)kMaxRowsPerWG * (D + 2);
+  const int pid = (b * a.Hkv + g) * a.n_rc + rc;
+  const size_t pidx = (size_t)pid * a.n_split + s;
+  const int d0 = 32 * j + e0;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int r = 16 * qt + x;
+    if (r >= nrows || 32 * j >= D) continue;
+    if (a.n_split == 1) {
+      const int rr = r0 + r;
+      const int i = rr / a.G;
+      const int h = g * a.G + (rr - i * a.G);
+      const float inv = (lo_[qt] > 0.f) ? 1.f / lo_[qt] : 0.f;
+      float* op = a.out + ((size_t)(b * a.n_q + i) * a.Hq + h) * D + d0;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<float2*>(op + 8 * i4) = make_float2(oo[qt][0][i4] * inv, oo[qt][1][i4] * inv);
+      if (wave == 0 && j == 0 && a.lse != nullptr)
+        a.lse[(size_t)(b * a.n_q + i) * a.Hq + h] =
+            (lo_[qt] > 0.f) ? (mo[qt] + __log2f(lo_[qt])) * kLn2 : -INFINITY;
+    } else {
+      float* pp = a.part + pidx * pstride;
+      float* op = pp + (size_t)r * D + d0;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<float2*>(op + 8 * i4) = make_float2(oo[qt][0][i4], oo[qt][1][i4]);
+      if (wave == 0 && j == 0) {
+        pp[(size_t)kMaxRowsPerWG * D + r] = mo[qt];
+        pp[(size_t)kMaxRowsPerWG * D + kMaxRowsPerWG + r] = lo_[qt];
+      }
+    }
+  }
 }
 
 // Union of the n_q rows' block lists of one (b, g), ascending, with per-block row masks
@@ -902,23 +991,20 @@ AttnPlan attn_plan(int32_t mode, int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv
   p.T_max = (int32_t)T;
   long long pairs = (long long)B * Hkv * p.n_rc;
   if (pairs < 1) pairs = 1;
-  // a split streams enough KV that its partial stays under ~4% of the bytes it reads
+  // One round of workgroups, one per CU: the start-up chain of dependent loads (sequence
+  // bounds, index list, block table) is paid once per workgroup, so fewer, longer
+  // workgroups stream more of the time.  A split still streams enough KV that its
+  // partial stays under ~4% of the bytes it reads.
   const long long partial_bytes = (long long)rows_wg * (d + 2) * 4;
   const long long step_bytes = (long long)kStepTokens * 2 * d * 2;
   long long min_steps = (partial_bytes * 25 + step_bytes - 1) / step_bytes;
   if (min_steps < kWaves) min_steps = kWaves;
-  long long ns = (kTargetWGs + pairs - 1) / pairs;
+  long long ns = kNumCUs / pairs;
   const long long ns_cap = (T + min_steps - 1) / min_steps;
   if (ns > ns_cap) ns = ns_cap;
   if (ns > kMaxSplits) ns = kMaxSplits;
   if (ns < 1) ns = 1;
-  // one workgroup per CU at a time: fill whole rounds of the 256 CUs
-  if (pairs * ns > kNumCUs) {
-    const long long whole = (pairs * ns) / kNumCUs * kNumCUs / pairs;
-    if (whole >= 1) ns = whole;
-  }
   p.n_split = (int32_t)ns;
-  p.sps = (int32_t)((T + ns - 1) / ns);
   p.part_bytes = (p.n_split > 1) ? align_up((size_t)pairs * p.n_split * kMaxRowsPerWG * (d + 2) * 4, 256) : 0;
   if (mode == MODE_BLOCK) {
     const size_t ucap = (size_t)n_q * cap;
@@ -935,8 +1021,8 @@ hipError_t attn_launch(const AttnPlan& p, AttnArgs a, void* workspace, hipStream
   char* ws = static_cast<char*>(workspace);
   a.part = p.part_bytes ? reinterpret_cast<float*>(ws) : nullptr;
   ws += p.part_bytes;
+  a.T_max = p.T_max;
   a.n_split = p.n_split;
-  a.sps = p.sps;
   a.rows = p.rows;
   a.n_rc = p.n_rc;
   if (a.mode == MODE_BLOCK) {

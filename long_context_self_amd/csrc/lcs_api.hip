@@ -249,6 +249,7 @@ lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t 
   a.indices = indices;
   a.counts = counts;
   a.cap = cap;
+  a.max_tail_len = max_tail_len;
   a.tail_begin = tail_begin;
   a.tail_len = tail_len;
   a.scale = scale;

@@ -22,7 +22,6 @@ constexpr int kStepTokens = 32;   // tokens consumed per inner step of a wave
 constexpr int kWaves = 4;         // waves per workgroup (one token stream each)
 constexpr int kMaxRowsPerWG = 64; // q-rows (n_q * G) handled by one workgroup
 constexpr int kMaxSplits = 128;   // split-K partials per (sequence, KV head, row chunk)
-constexpr int kTargetWGs = 1024;  // launch size the split policy aims for
 constexpr int kNumCUs = 256;      // MI355X compute units
 
 struct AttnArgs {
@@ -44,6 +43,7 @@ struct AttnArgs {
   int32_t cap;
   const int32_t* tail_begin;
   const int32_t* tail_len;
+  int32_t max_tail_len;   // tail_len values above it are clamped
   // block-union plan (workspace)
   const int32_t* ublk;
   const uint64_t* umask;
@@ -57,14 +57,15 @@ struct AttnArgs {
   int32_t lvec4;   // logits rows 16-byte aligned (16-byte stores allowed)
   // split-K
   float* part;
-  int32_t n_split, sps;
+  int32_t n_split;
+  int32_t T_max;   // step bound of the launch (list modes split it across waves)
   // final outputs
   float* out;
   float* lse;
 };
 
 struct AttnPlan {
-  int32_t D, QT, rows, n_rc, n_split, sps, T_max;
+  int32_t D, QT, rows, n_rc, n_split, T_max;
   size_t part_bytes, ublk_bytes, umask_bytes, ucount_bytes, total_bytes;
 };
 

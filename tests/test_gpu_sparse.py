@@ -157,3 +157,32 @@ def test_full_llama8b_32k_draft_step():
     cnt = np.array([[idx.shape[-1]]], dtype=np.int32)
     qd = synth.make_queries(cfg, kv, 1, seed=0, tag=200)
     check(cfg, kv, qd, "shared", idx, cnt, kv.prefix_len, np.array([cfg.n_q + 1], np.int32))
+
+
+@pytest.mark.parametrize("mode,B", [("shared", 1), ("per_kv_head", 1), ("shared", 8), ("per_kv_head", 8)])
+def test_workspace_garbage_and_reuse(mode, B):
+    """The workspace needs no initialisation: a workspace full of 0xFF bytes, then the same
+    workspace again (holding the previous call's partials), give results that match the
+    oracle and each other bit for bit."""
+    torch, lcs = require_gpu()
+    cfg = synth.CONFIGS["llama8b_32k"].with_(L=6000, top_k=1000, B=B)
+    kv = synth.make_paged_kv(cfg, seed=14)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=14)
+    idx, cnt = selected(cfg, kv, q, mode)
+    qd = synth.make_queries(cfg, kv, 1, seed=14, tag=300)
+    tl = np.full(cfg.B, cfg.n_q + 1, dtype=np.int32)
+    o_out, o_lse = oa.sparse_attn(qd, kv.k, kv.v, kv.block_table, cfg.page_size, mode, idx, cnt,
+                                  kv.prefix_len, tl, scale_for(cfg.d))
+    dkv = kv_dev(kv, torch, lcs)
+    nbytes = lcs.sparse_workspace_bytes(dkv, cfg.B, 1, cfg.Hq, mode, idx.shape[-1], int(tl.max()))
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        out = torch.full((cfg.B, 1, cfg.Hq, cfg.d), float("nan"), device="cuda")
+        lcs.sparse_draft_attn(dkv, bf16_dev(qd, torch), mode, i32_dev(idx, torch), i32_dev(cnt, torch),
+                              i32_dev(kv.prefix_len, torch), i32_dev(tl, torch), int(tl.max()),
+                              scale_for(cfg.d), out=out, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert np.max(np.abs(outs[0] - o_out)) <= OUT_TOL
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
