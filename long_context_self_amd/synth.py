@@ -285,9 +285,9 @@ def make_block_sets(cfg: Config, n_blocks: int, seed: int = 0) -> np.ndarray:
 def drift_critical(cfg: Config, kv: PagedKV, frac: float, seed: int, it: int) -> List[List[np.ndarray]]:
     """Move ``frac`` of each (b, g) critical set to fresh prefix positions.
 
-    Returns the new critical sets; the caller rewrites the affected K rows with
-    :func:`rewrite_keys`.  Used by the long-context loop to model critical
-    entries that change between iterations.
+    Returns the new critical sets; :func:`rewrite_keys` then redraws the K rows
+    of the positions that changed.  Models critical entries that change between
+    speculative iterations of the long-context loop.
     """
     new = []
     for b in range(cfg.B):
@@ -297,13 +297,48 @@ def drift_critical(cfg: Config, kv: PagedKV, frac: float, seed: int, it: int) ->
             cs = kv.critical[b][g]
             r = _rng(seed, 7, it, b, g)
             n_move = int(round(frac * cs.size))
-            if n_move == 0:
+            if n_move == 0 or cs.size >= L:
                 row.append(cs)
                 continue
-            keep = r.choice(cs.size, size=cs.size - n_move, replace=False)
-            kept = cs[np.sort(keep)]
-            pool = np.setdiff1d(np.arange(L), cs, assume_unique=True)
-            fresh = r.choice(pool, size=n_move, replace=False)
-            row.append(np.sort(np.concatenate([kept, fresh])).astype(np.int64))
+            keep = np.sort(r.choice(cs.size, size=cs.size - n_move, replace=False))
+            taken = set(cs.tolist())
+            fresh = []
+            while len(fresh) < n_move:          # rejection: the set is a small fraction of L
+                for p in r.integers(0, L, size=2 * n_move):
+                    if len(fresh) < n_move and int(p) not in taken:
+                        taken.add(int(p))
+                        fresh.append(int(p))
+            row.append(np.sort(np.concatenate([cs[keep], np.asarray(fresh, dtype=np.int64)])))
         new.append(row)
     return new
+
+
+def rewrite_keys(cfg: Config, kv: PagedKV, new_sets: List[List[np.ndarray]], seed: int, it: int):
+    """Redraw the K rows of positions that left or joined a critical set.
+
+    A position that leaves gets a fresh N(0, 1) key; one that joins gets a fresh
+    N(0, 1) key plus ``3 u``.  ``kv.k`` and ``kv.critical`` are updated in place.
+    Returns (rows, bits): flat row ids into ``k.reshape(-1, d)`` and the new bf16
+    rows, so that a device copy of the cache can be updated with one scatter.
+    """
+    P, d, Hkv = cfg.page_size, cfg.d, cfg.Hkv
+    rows, bits = [], []
+    for b in range(cfg.B):
+        for g in range(Hkv):
+            old, new = kv.critical[b][g], new_sets[b][g]
+            changed = np.setxor1d(old, new)
+            if changed.size == 0:
+                continue
+            x = _rng(seed, 8, it, b, g).standard_normal((changed.size, d), dtype=np.float32)
+            join = np.isin(changed, new)
+            x[join] += np.float32(3.0) * kv.u[b, g]
+            kb = f32_to_bf16_bits(x)
+            phys = kv.block_table[b, changed // P].astype(np.int64)
+            slot = changed % P
+            kv.k[phys, g, slot, :] = kb
+            rows.append((phys * Hkv + g) * P + slot)
+            bits.append(kb)
+            kv.critical[b][g] = new
+    if not rows:
+        return np.zeros(0, dtype=np.int64), np.zeros((0, d), dtype=np.uint16)
+    return np.concatenate(rows), np.concatenate(bits)

@@ -74,3 +74,33 @@ def test_tree_masks():
     assert [int(x) for x in m] == [0b1, 0b11, 0b111, 0b1111,
                                    0b10000, 0b110000, 0b1110000, 0b11110000]
     assert [int(x) for x in synth.chain_tail_masks(3)] == [1, 3, 7]
+
+
+def test_drift_and_rewrite_keys():
+    cfg = synth.CONFIGS["tiny"].with_(B=2, crit_frac=0.05)
+    kv = synth.make_paged_kv(cfg, seed=3)
+    old = [[c.copy() for c in row] for row in kv.critical]
+    k_before = kv.k.copy()
+    new = synth.drift_critical(cfg, kv, 0.2, seed=3, it=5)
+    for b in range(cfg.B):
+        for g in range(cfg.Hkv):
+            o, n = old[b][g], new[b][g]
+            assert n.size == o.size and np.all(np.diff(n) > 0)          # same size, sorted, distinct
+            assert n.min() >= 0 and n.max() < kv.prefix_len[b]
+            assert np.setdiff1d(o, n).size == int(round(0.2 * o.size))  # the moved fraction
+    rows, bits = synth.rewrite_keys(cfg, kv, new, seed=3, it=5)
+    flat_new, flat_old = kv.k.reshape(-1, cfg.d), k_before.reshape(-1, cfg.d)
+    assert np.array_equal(flat_new[rows], bits)
+    changed = np.any(flat_new != flat_old, axis=1)
+    assert set(np.nonzero(changed)[0].tolist()) <= set(rows.tolist())
+    # joined rows carry the planted direction, left rows do not
+    for b in range(cfg.B):
+        for g in range(cfg.Hkv):
+            joined = np.setdiff1d(new[b][g], old[b][g])
+            left = np.setdiff1d(old[b][g], new[b][g])
+            kf = synth.bf16_bits_to_f32(
+                kv.k[kv.block_table[b, joined // cfg.page_size], g, joined % cfg.page_size])
+            kl = synth.bf16_bits_to_f32(
+                kv.k[kv.block_table[b, left // cfg.page_size], g, left % cfg.page_size])
+            assert (kf @ kv.u[b, g]).mean() > (kl @ kv.u[b, g]).mean() + 1.5
+            assert kv.critical[b][g] is new[b][g]
