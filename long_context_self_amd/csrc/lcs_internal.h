@@ -82,8 +82,8 @@ hipError_t attn_launch(const AttnPlan& plan, AttnArgs args, void* workspace, hip
 enum SelMode : int32_t { LCS_SEL_SHARED = 0, LCS_SEL_PER_HEAD = 1, LCS_SEL_BLOCK = 2 };
 
 constexpr int kScorePos = 512;         // positions per workgroup of the score pass
-constexpr int kItemChunk = 1024;       // items per workgroup of the collect and emit passes
-constexpr int kMaxItemChunks = 16384;  // items < 2^24
+constexpr int kItemChunk = 4096;       // items per workgroup of the collect and emit passes
+constexpr int kMaxItemChunks = 4096;   // items < 2^24
 constexpr int kHistBins = 4096;        // first radix digit: top 12 bits of the key
 
 struct SelArgs {

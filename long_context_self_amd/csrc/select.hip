@@ -16,11 +16,13 @@
 //    sized read), writes an order-preserving uint32 key per item, and builds a
 //    4096-bin histogram of the top 12 key bits in LDS, flushed with one global
 //    atomic per non-empty bin.
-//  * collect_kernel finds the bin that holds the k-th item, counts items above it
-//    per 4096-item chunk and appends the bin's items as 44-bit composites
-//    (20 low key bits, then the complemented index) to a candidate list.
-//  * finalize_kernel (one workgroup per set) radix-selects the exact boundary
-//    composite among the candidates in four 11-bit LDS passes, then turns the
+//  * collect_kernel finds the bin that holds the k-th item, counts the items above
+//    it per 4096-item chunk and appends the bin's items as 44-bit composites
+//    (20 low key bits, then the complemented index) to a candidate list; each
+//    thread owns 16 consecutive items, and one scan places a workgroup's appends.
+//  * finalize_kernel (one workgroup per set) loads the candidates into LDS and
+//    radix-selects the exact boundary composite in up to four 11-bit passes,
+//    stopping once the chosen digit holds a single candidate; it then turns the
 //    per-chunk counts into output offsets.
 //  * emit_kernel rescans each chunk and writes the kept items in ascending order
 //    with a workgroup prefix sum.
@@ -94,6 +96,21 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave
   __syncthreads();
   total = tot;
   return pre + x - v;
+}
+
+constexpr int kIPT = kItemChunk / 256;   // consecutive items per thread in collect / emit
+
+// the 16 keys of items [i0, i0 + 16); i0 is a multiple of 16 below item_cap, which is a
+// multiple of 16, so the four 16-byte loads stay inside the set's key array
+__device__ __forceinline__ void load16(const uint32_t* keys, int i0, uint32_t (&k)[kIPT]) {
+#pragma unroll
+  for (int v = 0; v < kIPT / 4; ++v) {
+    const uint4 x = *reinterpret_cast<const uint4*>(keys + i0 + 4 * v);
+    k[4 * v] = x.x;
+    k[4 * v + 1] = x.y;
+    k[4 * v + 2] = x.z;
+    k[4 * v + 3] = x.w;
+  }
 }
 
 __global__ void zero_kernel(SelArgs a, int NS) {
@@ -210,14 +227,10 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
   const int tid = threadIdx.x;
   __shared__ uint32_t s_wave[4];
   __shared__ int sh_bin;
-  __shared__ uint32_t sh_above;
-  __shared__ uint64_t lq[kItemChunk];
-  __shared__ uint32_t lqn, lqbase, nab;
+  __shared__ uint32_t sh_above, lqbase;
   if (tid == 0) {
     sh_bin = 0;
     sh_above = 0;
-    lqn = 0;
-    nab = 0;
   }
   __syncthreads();
   find_bin(a, set, s_wave, &sh_bin, &sh_above);
@@ -226,34 +239,38 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
     a.thr[(size_t)set * 2 + 0] = (uint64_t)bin;
     a.thr[(size_t)set * 2 + 1] = (uint64_t)sh_above;
   }
-  const int i0 = blockIdx.x * kItemChunk;
-  const uint32_t* keys = a.keys + (size_t)set * a.item_cap;
-  uint32_t my_above = 0;
+  // this thread's kIPT consecutive items: count those above the bin, flag the bin's
+  const int i0 = blockIdx.x * kItemChunk + kIPT * tid;
+  uint32_t k[kIPT], flags = 0, n_above = 0;
+  if (i0 < w.hi && i0 + kIPT > w.lo) {
+    load16(a.keys + (size_t)set * a.item_cap, i0, k);
 #pragma unroll
-  for (int e = 0; e < kItemChunk / 256; ++e) {
-    const int it = i0 + e * 256 + tid;
-    if (it >= w.lo && it < w.hi) {
-      const uint32_t key = keys[it];
-      const int dg = (int)(key >> 20);
-      if (dg > bin) {
-        ++my_above;
-      } else if (dg == bin) {
-        const uint32_t slot = atomicAdd(&lqn, 1u);
-        lq[slot] = composite(key, it);
-      }
+    for (int e = 0; e < kIPT; ++e) {
+      if (i0 + e < w.lo || i0 + e >= w.hi) continue;
+      const int dg = (int)(k[e] >> 20);
+      n_above += dg > bin;
+      if (dg == bin) flags |= 1u << e;
     }
   }
-  atomicAdd(&nab, my_above);
-  __syncthreads();
+  // one scan of (above << 16 | candidates); both are at most kItemChunk per workgroup
+  uint32_t total;
+  const uint32_t excl = block_excl_scan<256>((n_above << 16) | __builtin_popcount(flags), s_wave, total);
   if (tid == 0) {
-    lqbase = lqn ? atomicAdd(&a.cand_count[set], lqn) : 0;
-    a.chunk_above[(size_t)set * a.n_chunks + blockIdx.x] = nab;
+    lqbase = (total & 0xFFFFu) ? atomicAdd(&a.cand_count[set], total & 0xFFFFu) : 0u;
+    a.chunk_above[(size_t)set * a.n_chunks + blockIdx.x] = total >> 16;
   }
   __syncthreads();
   uint64_t* cand = a.cand + (size_t)set * a.item_cap;
-  for (uint32_t e = tid; e < lqn; e += 256)
-    if (lqbase + e < (uint32_t)a.item_cap) cand[lqbase + e] = lq[e];
+  uint32_t pos = lqbase + (excl & 0xFFFFu);
+#pragma unroll
+  for (int e = 0; e < kIPT; ++e)
+    if (flags & (1u << e)) {
+      if (pos < (uint32_t)a.item_cap) cand[pos] = composite(k[e], i0 + e);
+      ++pos;
+    }
 }
+
+constexpr int kFinLDS = 8192;   // candidates the finalize pass holds in LDS
 
 __global__ void __launch_bounds__(1024) finalize_kernel(SelArgs a) {
   const int set = blockIdx.x;
@@ -261,20 +278,29 @@ __global__ void __launch_bounds__(1024) finalize_kernel(SelArgs a) {
   const Win w = window(a, b);
   if (w.all || a.top_k == 0) return;
   const int tid = threadIdx.x;
+  __shared__ uint64_t lc[kFinLDS];
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t cc[kMaxItemChunks];
   __shared__ uint32_t s_wave[16];
-  __shared__ uint64_t sh_prefix;
-  __shared__ uint32_t sh_rem;
+  __shared__ uint64_t sh_prefix, sh_one;
+  __shared__ uint32_t sh_rem, sh_cnt;
   const uint32_t above = (uint32_t)a.thr[(size_t)set * 2 + 1];
   const int n_c = min((int)a.cand_count[set], a.item_cap);
-  const uint64_t* cand = a.cand + (size_t)set * a.item_cap;
+  const uint64_t* gcand = a.cand + (size_t)set * a.item_cap;
+  const bool in_lds = n_c <= kFinLDS;
+  if (in_lds)
+    for (int e = tid; e < n_c; e += 1024) lc[e] = gcand[e];
+  const uint64_t* cand = in_lds ? lc : gcand;
   if (tid == 0) {
     sh_prefix = 0;
     sh_rem = (uint32_t)a.top_k - above;
   }
+  __syncthreads();
+  // the sh_rem-th largest candidate composite, 11 bits per pass; stop as soon as the
+  // chosen digit holds a single candidate
   uint64_t mask = 0;
-  for (int pass = 0; pass < 4; ++pass) {
+  int pass = 0;
+  for (; pass < 4; ++pass) {
     const int shift = 33 - 11 * pass;
     hist[tid] = 0;
     hist[tid + 1024] = 0;
@@ -296,15 +322,27 @@ __global__ void __launch_bounds__(1024) finalize_kernel(SelArgs a) {
       if (above_t + hh >= rem) {
         sh_prefix = prefix | ((uint64_t)(2 * tid + 1) << shift);
         sh_rem = rem - above_t;
+        sh_cnt = hh;
       } else {
         sh_prefix = prefix | ((uint64_t)(2 * tid) << shift);
         sh_rem = rem - above_t - hh;
+        sh_cnt = hl;
       }
     }
     mask |= (uint64_t)2047u << shift;
     __syncthreads();
+    if (sh_cnt == 1) break;
   }
-  const uint64_t cstar = sh_prefix;
+  uint64_t cstar = sh_prefix;
+  if (pass < 3) {                 // one candidate carries the chosen prefix: it is the answer
+    const uint64_t prefix = sh_prefix;
+    for (int e = tid; e < n_c; e += 1024) {
+      const uint64_t c = cand[e];
+      if ((c & mask) == prefix) sh_one = c;
+    }
+    __syncthreads();
+    cstar = sh_one;
+  }
   // per-chunk kept counts -> exclusive offsets after the sink window
   for (int c = tid; c < a.n_chunks; c += 1024) cc[c] = a.chunk_above[(size_t)set * a.n_chunks + c];
   __syncthreads();
@@ -355,16 +393,19 @@ __global__ void __launch_bounds__(256) emit_kernel(SelArgs a) {
   const uint64_t cstar = (K > 0) ? a.thr[(size_t)set * 2 + 1] : ~0ull;
   const uint32_t* keys = a.keys + (size_t)set * a.item_cap;
   __shared__ uint32_t s_wave[4];
-  constexpr int IPT = kItemChunk / 256;       // items per thread, consecutive
+  constexpr int IPT = kIPT;                   // items per thread, consecutive
   uint32_t flags = 0;
   uint32_t cnt = 0;
+  const int t0 = i0 + IPT * tid;
+  if (K > 0 && t0 < w.hi && t0 + IPT > w.lo) {
+    uint32_t k[kIPT];
+    load16(keys, t0, k);
 #pragma unroll
-  for (int e = 0; e < IPT; ++e) {
-    const int it = i0 + IPT * tid + e;
-    if (it >= w.lo && it < w.hi && K > 0) {
-      const uint32_t key = keys[it];
-      const int dg = (int)(key >> 20);
-      if (dg > bin || (dg == bin && composite(key, it) >= cstar)) {
+    for (int e = 0; e < IPT; ++e) {
+      const int it = t0 + e;
+      if (it < w.lo || it >= w.hi) continue;
+      const int dg = (int)(k[e] >> 20);
+      if (dg > bin || (dg == bin && composite(k[e], it) >= cstar)) {
         flags |= 1u << e;
         ++cnt;
       }
@@ -400,7 +441,7 @@ SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t ma
   long long items = max_len;
   if (mode == LCS_SEL_BLOCK) items = (max_len + block_size - 1) / block_size;
   if (items < 1) items = 1;
-  p.item_cap = (int32_t)align_up((size_t)items, 4);
+  p.item_cap = (int32_t)align_up((size_t)items, 16);
   p.n_chunks = (int32_t)((items + kItemChunk - 1) / kItemChunk);
   p.n_pos_chunks = (int32_t)(((long long)(max_len > 0 ? max_len : 1) + kScorePos - 1) / kScorePos);
   p.keys_bytes = align_up(NS * p.item_cap * 4, 256);
