@@ -386,7 +386,7 @@ __device__ __forceinline__ void dma_piece(const AttnArgs& a, const int (&sr)[Dma
 // (n_split <= kChunk) costs one memory round trip.  Split weights reach the column
 // loop through readlane.
 constexpr int kCombineRows = 4;
-constexpr int kChunk = 16;
+constexpr int kChunk = 32;
 
 __device__ __forceinline__ float lane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
@@ -583,7 +583,18 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
     const int c = e - r * QCH;
     if (e < QT * 16 * QCH) *reinterpret_cast<u32x4*>(s_q + (r * QCH + (c ^ (r % QCH))) * 8) = qv[u];
   }
-  __syncthreads();   // Q in LDS
+  // dense and block modes have the first window's block-table entries already: their
+  // first two K/V steps go out before the Q barrier, so the Q staging overlaps them
+  if (MODE != MODE_LIST_SHARED && w0 < w1) {
+    meta_stage_c<MODE>(a, si, g, w0, w1, colmask, lane, wm, 0);
+    wait_lgkm0();
+    step_dma<D>(a, wm.row[0], ring, lane, x, j);
+    if (w0 + 1 < w1) step_dma<D>(a, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
+  }
+  // Q in LDS.  An LDS-only barrier: __syncthreads would also wait for those DMAs.
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   // Q^T B-operands of this lane (q-row x of each tile, 8 dims per k-step), kept in registers
   u32x4 qop[QT][KS];
 #pragma unroll
@@ -597,11 +608,13 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   }
 
   if (w0 < w1) {
-    wait_vm<0>();
-    meta_stage_c<MODE>(a, si, g, w0, w1, colmask, lane, wm, 0);
-    wait_lgkm0();
-    step_dma<D>(a, wm.row[0], ring, lane, x, j);
-    if (w0 + 1 < w1) step_dma<D>(a, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
+    if (MODE == MODE_LIST_SHARED) {
+      wait_vm<0>();
+      meta_stage_c<MODE>(a, si, g, w0, w1, colmask, lane, wm, 0);
+      wait_lgkm0();
+      step_dma<D>(a, wm.row[0], ring, lane, x, j);
+      if (w0 + 1 < w1) step_dma<D>(a, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
+    }
     // Software pipeline.  Iteration s waits for slot s and moves it to registers, issues
     // the metadata stage, runs S(s) on the matrix core, stores S(s)'s collected logits,
     // and refills slot s with step s+2 (stores count in vmcnt, so they must precede the
@@ -663,8 +676,10 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
           if (!(c == 0 ? m0 : m1)) continue;
           float* dst = base + c * a.logits_ld;
           if (whole) {
-            *reinterpret_cast<f32x4*>(dst) = S[0][qt] * a.scale;
-            *reinterpret_cast<f32x4*>(dst + 16) = S[1][qt] * a.scale;
+            // streaming stores: the rows are read once, by the selector's next launch,
+            // and should not hold L2 lines that the K/V stream needs
+            __builtin_nontemporal_store(S[0][qt] * a.scale, reinterpret_cast<f32x4*>(dst));
+            __builtin_nontemporal_store(S[1][qt] * a.scale, reinterpret_cast<f32x4*>(dst + 16));
           } else {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
