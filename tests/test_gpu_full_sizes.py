@@ -1,0 +1,121 @@
+"""Full-size parity at the 64K (per-KV-head, B=4, 40/8 heads) and 128K (B=8) workloads,
+in the launch configurations the benchmark and the loop driver use.
+
+The oracle cannot evaluate these calls whole, so it checks sampled outputs one by one:
+for a sampled (sequence, row, head) it gathers the visible K/V rows itself and runs
+plain fp64 softmax attention.  Selection is checked bit for bit with the pinned-order
+CPU rule on the GPU's own logits, for a few sets.
+"""
+import numpy as np
+import pytest
+
+from long_context_self_amd import synth
+from oracle import attention as oa
+from oracle import select as osel
+
+from gpu_helpers import bf16_dev, i32_dev, kv_dev, logit_rel_err, require_gpu, scale_for
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LOGIT_TOL = 1e-3
+
+
+class Case:
+    pass
+
+
+def build(name):
+    torch, lcs = require_gpu()
+    c = Case()
+    c.cfg = synth.CONFIGS[name]
+    c.kv = synth.make_paged_kv(c.cfg, seed=0)
+    c.q = synth.make_queries(c.cfg, c.kv, c.cfg.n_q, seed=0)
+    c.qd = synth.make_queries(c.cfg, c.kv, 1, seed=0, tag=100)
+    c.dkv = kv_dev(c.kv, torch, lcs)
+    cfg = c.cfg
+    B, L = cfg.B, cfg.L
+    pl = i32_dev(c.kv.prefix_len, torch)
+    out = torch.full((B, cfg.n_q, cfg.Hq, cfg.d), float("nan"), device="cuda")
+    logits = torch.full((B, cfg.Hq, 2, L), float("nan"), device="cuda")
+    lse = torch.full((B, cfg.n_q, cfg.Hq), float("nan"), device="cuda")
+    lcs.verify_attn(c.dkv, bf16_dev(c.q, torch), pl, L, scale_for(cfg.d), cfg.collect_rows, out=out,
+                    logits=logits, lse=lse)
+    n_sets = 1 if cfg.mode == "shared" else cfg.Hkv
+    S = cfg.n_sink + cfg.top_k + cfg.n_recent
+    idx = torch.full((B, n_sets, S), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((B, n_sets), dtype=torch.int32, device="cuda")
+    lcs.select_topk(logits, pl, L, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
+                    indices=idx, counts=cnt)
+    tl = np.full(B, cfg.n_q + 1, dtype=np.int32)
+    dout = torch.full((B, 1, cfg.Hq, cfg.d), float("nan"), device="cuda")
+    dlse = torch.full((B, 1, cfg.Hq), float("nan"), device="cuda")
+    lcs.sparse_draft_attn(c.dkv, bf16_dev(c.qd, torch), cfg.mode, idx, cnt, pl, i32_dev(tl, torch),
+                          cfg.n_q + cfg.n_draft, scale_for(cfg.d), out=dout, lse=dlse)
+    torch.cuda.synchronize()
+    c.out, c.logits, c.lse = out.cpu().numpy(), logits.cpu().numpy(), lse.cpu().numpy()
+    c.idx, c.cnt, c.tl = idx.cpu().numpy(), cnt.cpu().numpy(), tl
+    c.dout, c.dlse = dout.cpu().numpy(), dlse.cpu().numpy()
+    del c.dkv
+    torch.cuda.empty_cache()
+    return c
+
+
+@pytest.fixture(scope="module", params=["qwen14b_64k", "stress_128k"])
+def case(request):
+    return build(request.param)
+
+
+def test_verify_sampled(case):
+    cfg, kv = case.cfg, case.kv
+    sc = scale_for(cfg.d)
+    qf = oa.bf16_to_f64(case.q)
+    rng = np.random.default_rng(1)
+    assert np.isfinite(case.out).all()
+    for _ in range(10):
+        b, i, h = int(rng.integers(cfg.B)), int(rng.integers(cfg.n_q)), int(rng.integers(cfg.Hq))
+        g, L = h // cfg.G, int(kv.prefix_len[b])
+        pos = np.arange(L + i + 1)
+        K = oa.paged_rows(kv.k, kv.block_table, b, g, pos, cfg.page_size)
+        V = oa.paged_rows(kv.v, kv.block_table, b, g, pos, cfg.page_size)
+        o, _, l = oa.attention_one(qf[b, i, h], K, V, sc)
+        assert np.max(np.abs(case.out[b, i, h] - o)) <= OUT_TOL
+        assert abs(case.lse[b, i, h] - l) <= 1e-3
+    for _ in range(4):                 # whole collected logit rows
+        b, h, c = int(rng.integers(cfg.B)), int(rng.integers(cfg.Hq)), int(rng.integers(2))
+        i = 0 if c == 0 else cfg.n_q - 1
+        L = int(kv.prefix_len[b])
+        K = oa.paged_rows(kv.k, kv.block_table, b, h // cfg.G, np.arange(L), cfg.page_size)
+        assert logit_rel_err(case.logits[b, h, c, :L], sc * (K @ qf[b, i, h])) <= LOGIT_TOL
+
+
+def test_select_exact_on_gpu_logits(case):
+    cfg = case.cfg
+    rng = np.random.default_rng(2)
+    n_sets = 1 if cfg.mode == "shared" else cfg.Hkv
+    for _ in range(3):
+        b, s = int(rng.integers(cfg.B)), int(rng.integers(n_sets))
+        L = int(case.kv.prefix_len[b])
+        heads = range(cfg.Hq) if cfg.mode == "shared" else range(s * cfg.G, (s + 1) * cfg.G)
+        ref = osel.topk_tokens(osel.scores_f32_pinned(case.logits, b, L, heads), L, cfg.top_k, cfg.n_sink,
+                               cfg.n_recent)
+        assert case.cnt[b, s] == ref.size
+        assert np.array_equal(case.idx[b, s, :ref.size], ref)
+
+
+def test_draft_sampled(case):
+    cfg, kv = case.cfg, case.kv
+    sc = scale_for(cfg.d)
+    qf = oa.bf16_to_f64(case.qd)
+    rng = np.random.default_rng(3)
+    assert np.isfinite(case.dout).all()
+    for _ in range(10):
+        b, h = int(rng.integers(cfg.B)), int(rng.integers(cfg.Hq))
+        g, L = h // cfg.G, int(kv.prefix_len[b])
+        sel = oa.sparse_visible_positions(cfg.mode, case.idx, case.cnt, b, 0, g, cfg.page_size, L)
+        pos = np.concatenate([sel, L + np.arange(int(case.tl[b]))])
+        K = oa.paged_rows(kv.k, kv.block_table, b, g, pos, cfg.page_size)
+        V = oa.paged_rows(kv.v, kv.block_table, b, g, pos, cfg.page_size)
+        o, _, l = oa.attention_one(qf[b, 0, h], K, V, sc)
+        assert np.max(np.abs(case.dout[b, 0, h] - o)) <= OUT_TOL
+        assert abs(case.dlse[b, 0, h] - l) <= 1e-3
