@@ -67,6 +67,11 @@ typedef enum {
   LCS_SET_BLOCK = 2        /* SSV / NSA: block ids, one block = one page              */
 } lcs_set_mode;
 
+typedef enum {
+  LCS_SCORE_LOGIT_SUM = 0,      /* Vegas: pre-softmax logits of the collected rows    */
+  LCS_SCORE_SOFTMAX_WEIGHT = 1  /* Sparse Glimpse: post-softmax weights of the rows   */
+} lcs_score_kind;
+
 typedef struct {
   const void* k;              /* device bf16 [num_pages][Hkv][page_size][d]            */
   const void* v;              /* device bf16 [num_pages][Hkv][page_size][d]            */
@@ -114,6 +119,56 @@ lcs_status lcs_verify_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int
                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Dense verify attention that collects any set of verifier rows.
+ *
+ * Vegas page, Figure 6 and its text: collecting more rows costs verification
+ * time through memory-bandwidth contention, which is why the method keeps two;
+ * Sparse Glimpse page, "Core claim": its importance signal comes from the last
+ * verification queries.  This entry point collects the rows named by a mask so
+ * that both choices, and all-row collection, can be run and measured.
+ *
+ *  collect_mask bit i set: verifier row i is collected.  With logits != NULL it
+ *               must be non-zero and name rows below n_q only (LCS_E_ARG).
+ *  logits       fp32 [B][Hq][n_c][logits_ld], n_c = popcount(collect_mask):
+ *               slot c holds the c-th collected row in ascending row order,
+ *               columns p < prefix_len[b] written, others untouched.  NULL:
+ *               nothing is collected and collect_mask is ignored.
+ * Every other argument, the workspace size and the limits are those of
+ * lcs_verify_attn, whose result this reproduces bit for bit for the two rows
+ * 0 < n_q-1 (collect_mask = 1 | 1 << (n_q-1)).
+ * ------------------------------------------------------------------------- */
+lcs_status lcs_verify_attn_rows(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q,
+                                int32_t Hq, const int32_t* prefix_len, int32_t max_prefix_len,
+                                const uint64_t* tree_mask, float scale, uint64_t collect_mask,
+                                float* out, float* logits, int64_t logits_ld, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Dense verify attention that writes per-KV-head partial scores of the two
+ * collected rows instead of their logits.
+ *
+ * Vegas page, "Core claim": the selector only needs the two rows' logits summed
+ * over the query heads.  Summing the G heads of each KV group inside the verify
+ * epilogue writes 2G times fewer bytes than the two logit rows (Figure 6 text:
+ * the collection cost is memory traffic) and leaves one row per KV head for
+ * lcs_select_topk_scores.
+ *
+ *  scores       fp32 [B][Hkv][scores_ld], scores_ld >= max_prefix_len:
+ *               scores[b][g][p] = sum over the heads h of group g, ascending, of
+ *               (l[h][row0][p] + l[h][row1][p]) in fp32 as acc = acc + (pair),
+ *               l the scaled logits lcs_verify_attn would write (bit for bit);
+ *               columns p < prefix_len[b] written, others untouched.
+ * Every other argument is that of lcs_verify_attn (logits are not written).
+ * Limits: n_q * Hq/Hkv <= 64, and Hq/Hkv <= d/32 * ceil(n_q * Hq/Hkv / 16)
+ * (the staging area); else LCS_E_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+lcs_status lcs_verify_attn_scores(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q,
+                                  int32_t Hq, const int32_t* prefix_len, int32_t max_prefix_len,
+                                  const uint64_t* tree_mask, float scale, int32_t collect_row0,
+                                  int32_t collect_row1, float* out, float* scores, int64_t scores_ld,
+                                  float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Verification-guided top-k selection.
  *
  * Vegas page, "Core claim" / "What carries the argument": the two collected
@@ -152,6 +207,55 @@ lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, in
                            lcs_set_mode mode, int32_t top_k, int32_t n_sink, int32_t n_recent,
                            int32_t block_size, int32_t* indices, int32_t* counts, int32_t cap,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Top-k selection from per-KV-head partial scores (lcs_verify_attn_scores).
+ *
+ * Rule, modes, windows, outputs and workspace (lcs_select_workspace_bytes with
+ * the model's Hq) as for lcs_select_topk, with the position score
+ *   SHARED:       sigma_p = sum over g ascending of scores[b][g][p] (fp32);
+ *   PER_KV_HEAD,
+ *   BLOCK:        sigma_p = scores[b][g][p] for the set of KV head g,
+ * so PER_KV_HEAD and BLOCK select exactly what lcs_select_topk selects on the
+ * logits, and SHARED sums the same terms grouped by KV head first.
+ *
+ *  scores       fp32 [B][Hkv][scores_ld], scores_ld >= max_prefix_len.
+ * ------------------------------------------------------------------------- */
+lcs_status lcs_select_topk_scores(const float* scores, int64_t scores_ld, int32_t B, int32_t Hkv,
+                                  const int32_t* prefix_len, int32_t max_prefix_len,
+                                  lcs_set_mode mode, int32_t top_k, int32_t n_sink, int32_t n_recent,
+                                  int32_t block_size, int32_t* indices, int32_t* counts, int32_t cap,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Top-k selection over n collected rows, scored by logits or softmax weights.
+ *
+ * The rule, modes, windows, outputs and workspace are those of lcs_select_topk;
+ * only the per-head term of sigma_p changes, for a head h with n_rows rows:
+ *   LCS_SCORE_LOGIT_SUM:      t = l[h][0][p]; t = t + l[h][c][p] for c = 1..n-1
+ *                             (Vegas page, "Core claim", extended to n rows).
+ *   LCS_SCORE_SOFTMAX_WEIGHT: t = sum over c ascending of
+ *                             expf(l[h][c][p] - lse[b][row_c][h]), row_c the
+ *                             c-th set bit of rows_mask (Sparse Glimpse page,
+ *                             "Core claim": post-softmax weights of the last
+ *                             verification queries).
+ * and sigma_p = sum over the set's heads ascending of t, in fp32.  LOGIT_SUM is
+ * bit-identical to the CPU rule in the same order (n_rows = 2 gives exactly
+ * lcs_select_topk); SOFTMAX_WEIGHT matches it to within expf's rounding.
+ *
+ *  logits       fp32 [B][Hq][n_rows][logits_ld] (lcs_verify_attn_rows layout).
+ *  n_rows       1..64.
+ *  lse, n_q, rows_mask  SOFTMAX_WEIGHT only (else ignored, may be NULL / 0):
+ *               lse fp32 [B][n_q][Hq] as written by the verify call, natural log;
+ *               rows_mask names exactly n_rows rows below n_q (LCS_E_ARG).
+ * ------------------------------------------------------------------------- */
+lcs_status lcs_select_topk_rows(const float* logits, int64_t logits_ld, int32_t n_rows,
+                                lcs_score_kind kind, const float* lse, int32_t n_q,
+                                uint64_t rows_mask, int32_t B, int32_t Hq, int32_t Hkv,
+                                const int32_t* prefix_len, int32_t max_prefix_len,
+                                lcs_set_mode mode, int32_t top_k, int32_t n_sink, int32_t n_recent,
+                                int32_t block_size, int32_t* indices, int32_t* counts, int32_t cap,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Sparse draft attention over the selected entries plus the recent tail.

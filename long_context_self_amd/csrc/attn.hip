@@ -478,7 +478,9 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   merge_row<D>(a, pid, r, threadIdx.x & 63);
 }
 
-template <int D, int QT, int MODE>
+// SC: dense verify that writes per-KV-head partial scores of the two collected rows
+// instead of their logits (the selector's per-head sum, done here, 2G times fewer bytes)
+template <int D, int QT, int MODE, bool SC = false>
 __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   constexpr int KS = D / 32;                  // k-steps of the QK^T product
   constexpr int NDMA = DmaGeom<D>::N;         // 16-byte DMAs per lane per step
@@ -533,14 +535,18 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
     colmask = (MODE == MODE_DENSE) ? (kAll << lane) : kAll;
   }
 
-  // verifier row index of this lane's q-row in each tile (64 = padding row)
-  int rowi[QT];
+  // verifier row index of this lane's q-row in each tile (64 = padding row), and the
+  // logit slot of that row (-1: not collected)
+  int rowi[QT], cslot[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int r = 16 * qt + x;
     rowi[qt] = (r < nrows) ? (r0 + r) / a.G : 64;
+    cslot[qt] = -1;
+    if (rowi[qt] < 64 && ((a.cmask >> rowi[qt]) & 1ull))
+      cslot[qt] = __popcll(a.cmask & ((1ull << rowi[qt]) - 1)) ^ a.cswap;
   }
-  const bool collect = MODE == MODE_DENSE && a.logits != nullptr;
+  const bool collect = MODE == MODE_DENSE && !SC && a.logits != nullptr;
 
   float m[QT], l[QT];
   f32x4 O[QT][8];
@@ -606,6 +612,12 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
       qop[qt][ks] = *reinterpret_cast<const u32x4*>(s_q + (r * QCH + (c ^ (r % QCH))) * 8);
     }
   }
+  // partial scores stage their logits in the Q area, free once every wave holds Q
+  if constexpr (SC) {
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
 
   if (w0 < w1) {
     if (MODE == MODE_LIST_SHARED) {
@@ -660,20 +672,21 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) O[qt][e] *= alpha[qt];
     };
-    // Collect-2-Query: scaled logits of the two collected rows, prefix columns only
+    // Collected rows (Collect-2-Query and its generalisation to any row set): scaled
+    // logits, prefix columns only
     auto store_logits = [&](int st) {
       const int p0 = st * kStepTokens + 4 * j;
       const bool whole = a.lvec4 && st * kStepTokens + kStepTokens <= si.L;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const bool m0 = rowi[qt] == a.c0, m1 = rowi[qt] == a.c1;
-        if (!__any(m0 || m1)) continue;
+        const bool mine = cslot[qt] >= 0;
+        if (!__any(mine)) continue;
         const int rr = r0 + 16 * qt + x;
         const int h = g * a.G + (rr - rowi[qt] * a.G);
-        float* base = a.logits + (size_t)(b * a.Hq + h) * 2 * a.logits_ld + p0;
+        float* base = a.logits + ((size_t)(b * a.Hq + h) * a.n_cl + max(cslot[qt], 0)) * a.logits_ld + p0;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          if (!(c == 0 ? m0 : m1)) continue;
+          if (!mine || (c == 1 && !a.cdup)) continue;
           float* dst = base + c * a.logits_ld;
           if (whole) {
             // streaming stores: the rows are read once, by the selector's next launch,
@@ -688,6 +701,34 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
                 if (p0 + 16 * tt + i < si.L) dst[16 * tt + i] = S[tt][qt][i] * a.scale;
           }
         }
+      }
+    };
+    // Partial scores: the lanes of the collected rows put their scaled logits of the
+    // step in this wave's part of the Q area as [slot c * G + head][32 tokens]; lanes
+    // 0-31 then sum one token's column over the group's heads, ascending, as
+    // acc = acc + (row0 + row1), and store 32 consecutive scores.
+    auto store_scores = [&](int st) {
+      float* sb = reinterpret_cast<float*>(smem_raw) + (size_t)wave * (kQBytes / 4 / kWaves);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const bool mine = cslot[qt] >= 0;
+        if (!__any(mine)) continue;
+        if (mine) {
+          const int hh = r0 + 16 * qt + x - rowi[qt] * a.G;
+          float* dst = sb + (cslot[qt] * a.G + hh) * kStepTokens + 4 * j;
+          *reinterpret_cast<f32x4*>(dst) = S[0][qt] * a.scale;
+          *reinterpret_cast<f32x4*>(dst + 16) = S[1][qt] * a.scale;
+          if (a.cdup) {
+            *reinterpret_cast<f32x4*>(dst + a.G * kStepTokens) = S[0][qt] * a.scale;
+            *reinterpret_cast<f32x4*>(dst + a.G * kStepTokens + 16) = S[1][qt] * a.scale;
+          }
+        }
+      }
+      const int p = st * kStepTokens + lane;
+      if (lane < kStepTokens && p < si.L) {
+        float acc = 0.f;
+        for (int hh = 0; hh < a.G; ++hh) acc = acc + (sb[hh * kStepTokens + lane] + sb[(a.G + hh) * kStepTokens + lane]);
+        a.scores[(size_t)(b * a.Hkv + g) * a.scores_ld + p] = acc;
       }
     };
     // PV(s-1) and softmax(s).  The reference max m only moves when a row's max grows
@@ -793,6 +834,7 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
           }
         }
         if (collect) store_logits(step);
+        if constexpr (SC) store_scores(step);
         // cache rows of step s+2, which refills this slot (read even when no refill is
         // due: the pointer stays inside this wave's metadata area)
         const bool dma_due = step + 2 < w1;
@@ -961,7 +1003,19 @@ __global__ void __launch_bounds__(256) block_union_kernel(AttnArgs a) {
 template <int D, int MODE>
 hipError_t launch_main_mode(const AttnPlan& p, const AttnArgs& a, hipStream_t stream) {
   dim3 grid(p.n_split, a.Hkv * p.n_rc, a.B);
-  switch (p.QT) {
+  bool launched = false;
+  if constexpr (MODE == MODE_DENSE) {
+    if (a.scores != nullptr) {
+      switch (p.QT) {
+        case 1: hipLaunchKernelGGL((attn_kernel<D, 1, MODE, true>), grid, dim3(256), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((attn_kernel<D, 2, MODE, true>), grid, dim3(256), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((attn_kernel<D, 3, MODE, true>), grid, dim3(256), 0, stream, a); break;
+        default: hipLaunchKernelGGL((attn_kernel<D, 4, MODE, true>), grid, dim3(256), 0, stream, a); break;
+      }
+      launched = true;
+    }
+  }
+  if (!launched) switch (p.QT) {
     case 1: hipLaunchKernelGGL((attn_kernel<D, 1, MODE>), grid, dim3(256), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((attn_kernel<D, 2, MODE>), grid, dim3(256), 0, stream, a); break;
     case 3: hipLaunchKernelGGL((attn_kernel<D, 3, MODE>), grid, dim3(256), 0, stream, a); break;

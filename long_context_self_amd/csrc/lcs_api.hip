@@ -73,20 +73,17 @@ size_t lcs_verify_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq, const lcs_
       .total_bytes;
 }
 
-lcs_status lcs_verify_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q, int32_t Hq,
-                           const int32_t* prefix_len, int32_t max_prefix_len, const uint64_t* tree_mask,
-                           float scale, int32_t collect_row0, int32_t collect_row1, float* out,
-                           float* logits, int64_t logits_ld, float* lse, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  lcs_status st = check_kv(kv);
-  if (st != LCS_OK) return st;
-  if ((st = check_heads(Hq, kv->Hkv)) != LCS_OK) return st;
-  if (B < 0) return fail(LCS_E_SHAPE, "B must be >= 0");
-  if (n_q < 1) return fail(LCS_E_SHAPE, "n_q must be >= 1");
-  if (n_q > 64) return fail(LCS_E_UNSUPPORTED, "n_q %d > 64 verifier rows", n_q);
-  if (max_prefix_len < 0) return fail(LCS_E_SHAPE, "max_prefix_len must be >= 0");
-  if (collect_row0 < 0 || collect_row0 >= n_q || collect_row1 < 0 || collect_row1 >= n_q)
-    return fail(LCS_E_ARG, "collect rows (%d, %d) outside [0, %d)", collect_row0, collect_row1, n_q);
+}  // extern "C"
+
+namespace {
+
+// Shared body of the two verify entry points; the collected rows arrive as the
+// kernel's (cmask, n_cl, cswap, cdup) encoding, already validated against n_q.
+lcs_status verify_impl(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q, int32_t Hq,
+                       const int32_t* prefix_len, int32_t max_prefix_len, const uint64_t* tree_mask,
+                       float scale, uint64_t cmask, int32_t n_cl, int32_t cswap, int32_t cdup, float* out,
+                       float* logits, int64_t logits_ld, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream, float* scores = nullptr, int64_t scores_ld = 0) {
   if (B == 0) return LCS_OK;   // empty batch: nothing is read or written, pointers may be NULL
   if (q == nullptr || prefix_len == nullptr || out == nullptr)
     return fail(LCS_E_ARG, "q, prefix_len and out must be non-NULL");
@@ -119,14 +116,95 @@ lcs_status lcs_verify_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int
   a.rowmask = tree_mask;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.c0 = collect_row0;
-  a.c1 = collect_row1;
+  a.cmask = (logits != nullptr) ? cmask : 0;
+  a.n_cl = n_cl;
+  a.cswap = cswap;
+  a.cdup = cdup;
   a.logits = logits;
   a.logits_ld = logits_ld;
   a.lvec4 = (logits != nullptr && aligned(logits, 16) && logits_ld % 4 == 0) ? 1 : 0;
+  a.scores = scores;
+  a.scores_ld = scores_ld;
+  if (scores != nullptr) {
+    // the partial sums need both collected rows of every head of a group in one
+    // workgroup, and their staging area (the Q tile) must hold 2G x 32 floats per wave
+    if (plan.n_rc != 1)
+      return fail(LCS_E_UNSUPPORTED, "partial scores need n_q * Hq / Hkv <= 64 rows (have %d)", plan.rows);
+    if (256LL * a.G > 8LL * plan.QT * kv->d)
+      return fail(LCS_E_UNSUPPORTED, "partial scores need Hq / Hkv <= %d at %d rows and d = %d",
+                  plan.QT * kv->d / 32, plan.rows, kv->d);
+    a.cmask = cmask;
+    a.logits = nullptr;
+  }
   a.out = out;
   a.lse = lse;
   return hip_status(lcs::attn_launch(plan, a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+lcs_status verify_checks(const lcs_paged_kv* kv, int32_t B, int32_t n_q, int32_t Hq, int32_t max_prefix_len) {
+  lcs_status st = check_kv(kv);
+  if (st != LCS_OK) return st;
+  if ((st = check_heads(Hq, kv->Hkv)) != LCS_OK) return st;
+  if (B < 0) return fail(LCS_E_SHAPE, "B must be >= 0");
+  if (n_q < 1) return fail(LCS_E_SHAPE, "n_q must be >= 1");
+  if (n_q > 64) return fail(LCS_E_UNSUPPORTED, "n_q %d > 64 verifier rows", n_q);
+  if (max_prefix_len < 0) return fail(LCS_E_SHAPE, "max_prefix_len must be >= 0");
+  return LCS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lcs_status lcs_verify_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q, int32_t Hq,
+                           const int32_t* prefix_len, int32_t max_prefix_len, const uint64_t* tree_mask,
+                           float scale, int32_t collect_row0, int32_t collect_row1, float* out,
+                           float* logits, int64_t logits_ld, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  lcs_status st = verify_checks(kv, B, n_q, Hq, max_prefix_len);
+  if (st != LCS_OK) return st;
+  if (collect_row0 < 0 || collect_row0 >= n_q || collect_row1 < 0 || collect_row1 >= n_q)
+    return fail(LCS_E_ARG, "collect rows (%d, %d) outside [0, %d)", collect_row0, collect_row1, n_q);
+  const uint64_t cmask = (1ull << collect_row0) | (1ull << collect_row1);
+  return verify_impl(kv, q, B, n_q, Hq, prefix_len, max_prefix_len, tree_mask, scale, cmask, 2,
+                     collect_row0 > collect_row1 ? 1 : 0, collect_row0 == collect_row1 ? 1 : 0, out, logits,
+                     logits_ld, lse, workspace, workspace_bytes, stream);
+}
+
+lcs_status lcs_verify_attn_scores(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q, int32_t Hq,
+                                  const int32_t* prefix_len, int32_t max_prefix_len, const uint64_t* tree_mask,
+                                  float scale, int32_t collect_row0, int32_t collect_row1, float* out,
+                                  float* scores, int64_t scores_ld, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  lcs_status st = verify_checks(kv, B, n_q, Hq, max_prefix_len);
+  if (st != LCS_OK) return st;
+  if (collect_row0 < 0 || collect_row0 >= n_q || collect_row1 < 0 || collect_row1 >= n_q)
+    return fail(LCS_E_ARG, "collect rows (%d, %d) outside [0, %d)", collect_row0, collect_row1, n_q);
+  if (B > 0 && scores == nullptr) return fail(LCS_E_ARG, "scores must be non-NULL");
+  if (B > 0 && scores_ld < max_prefix_len)
+    return fail(LCS_E_SHAPE, "scores_ld %lld < max_prefix_len %d", (long long)scores_ld, max_prefix_len);
+  const uint64_t cmask = (1ull << collect_row0) | (1ull << collect_row1);
+  return verify_impl(kv, q, B, n_q, Hq, prefix_len, max_prefix_len, tree_mask, scale, cmask, 2,
+                     collect_row0 > collect_row1 ? 1 : 0, collect_row0 == collect_row1 ? 1 : 0, out, nullptr, 0,
+                     lse, workspace, workspace_bytes, stream, scores, scores_ld);
+}
+
+lcs_status lcs_verify_attn_rows(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q, int32_t Hq,
+                                const int32_t* prefix_len, int32_t max_prefix_len, const uint64_t* tree_mask,
+                                float scale, uint64_t collect_mask, float* out, float* logits,
+                                int64_t logits_ld, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  lcs_status st = verify_checks(kv, B, n_q, Hq, max_prefix_len);
+  if (st != LCS_OK) return st;
+  if (logits != nullptr) {
+    if (collect_mask == 0) return fail(LCS_E_ARG, "collect_mask is empty but logits is not NULL");
+    if (n_q < 64 && (collect_mask >> n_q) != 0)
+      return fail(LCS_E_ARG, "collect_mask 0x%llx names rows at or above n_q = %d",
+                  (unsigned long long)collect_mask, n_q);
+  }
+  return verify_impl(kv, q, B, n_q, Hq, prefix_len, max_prefix_len, tree_mask, scale, collect_mask,
+                     __builtin_popcountll(collect_mask), 0, 0, out, logits, logits_ld, lse, workspace,
+                     workspace_bytes, stream);
 }
 
 size_t lcs_select_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, lcs_set_mode mode,
@@ -136,11 +214,15 @@ size_t lcs_select_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, lcs_set_mo
   return lcs::select_plan(B, Hq, Hkv, (int32_t)mode, max_prefix_len, block_size).total_bytes;
 }
 
-lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, int32_t Hq, int32_t Hkv,
-                           const int32_t* prefix_len, int32_t max_prefix_len, lcs_set_mode mode,
-                           int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t block_size,
-                           int32_t* indices, int32_t* counts, int32_t cap, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+lcs_status select_impl(const float* logits, int64_t logits_ld, int32_t n_rows, int32_t kind, const float* lse,
+                       int32_t n_q, uint64_t rows_mask, int32_t B, int32_t Hq, int32_t Hkv,
+                       const int32_t* prefix_len, int32_t max_prefix_len, lcs_set_mode mode, int32_t top_k,
+                       int32_t n_sink, int32_t n_recent, int32_t block_size, int32_t* indices, int32_t* counts,
+                       int32_t cap, void* workspace, size_t workspace_bytes, void* stream) {
   if (Hkv < 1) return fail(LCS_E_SHAPE, "Hkv must be >= 1");
   lcs_status st = check_heads(Hq, Hkv);
   if (st != LCS_OK) return st;
@@ -150,6 +232,7 @@ lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, in
   if (B == 0) return LCS_OK;   // empty batch: nothing is read or written, pointers may be NULL
   if (logits == nullptr || prefix_len == nullptr || indices == nullptr || counts == nullptr)
     return fail(LCS_E_ARG, "logits, prefix_len, indices and counts must be non-NULL");
+  if (kind == lcs::SCORE_SOFTMAX_WT && lse == nullptr) return fail(LCS_E_ARG, "softmax-weight scores need lse");
   if (top_k < 0 || n_sink < 0 || n_recent < 0) return fail(LCS_E_ARG, "top_k, n_sink, n_recent must be >= 0");
   if (max_prefix_len < 0) return fail(LCS_E_SHAPE, "max_prefix_len must be >= 0");
   if (max_prefix_len >= (1 << 24)) return fail(LCS_E_UNSUPPORTED, "max_prefix_len must be < 2^24");
@@ -172,6 +255,11 @@ lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, in
   lcs::SelArgs a{};
   a.logits = logits;
   a.ld = logits_ld;
+  a.n_rows = n_rows;
+  a.kind = kind;
+  a.lse = lse;
+  a.n_q = n_q;
+  a.rows_mask = rows_mask;
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -188,6 +276,52 @@ lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, in
   a.counts = counts;
   a.cap = cap;
   return hip_status(lcs::select_launch(plan, a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, int32_t Hq, int32_t Hkv,
+                           const int32_t* prefix_len, int32_t max_prefix_len, lcs_set_mode mode,
+                           int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t block_size,
+                           int32_t* indices, int32_t* counts, int32_t cap, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return select_impl(logits, logits_ld, 2, lcs::SCORE_LOGIT_SUM, nullptr, 0, 0, B, Hq, Hkv, prefix_len,
+                     max_prefix_len, mode, top_k, n_sink, n_recent, block_size, indices, counts, cap, workspace,
+                     workspace_bytes, stream);
+}
+
+lcs_status lcs_select_topk_scores(const float* scores, int64_t scores_ld, int32_t B, int32_t Hkv,
+                                  const int32_t* prefix_len, int32_t max_prefix_len, lcs_set_mode mode,
+                                  int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t block_size,
+                                  int32_t* indices, int32_t* counts, int32_t cap, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  // one score row per KV head: the selector's head loop runs over KV heads, one row each
+  return select_impl(scores, scores_ld, 1, lcs::SCORE_LOGIT_SUM, nullptr, 0, 0, B, Hkv, Hkv, prefix_len,
+                     max_prefix_len, mode, top_k, n_sink, n_recent, block_size, indices, counts, cap, workspace,
+                     workspace_bytes, stream);
+}
+
+lcs_status lcs_select_topk_rows(const float* logits, int64_t logits_ld, int32_t n_rows, lcs_score_kind kind,
+                                const float* lse, int32_t n_q, uint64_t rows_mask, int32_t B, int32_t Hq,
+                                int32_t Hkv, const int32_t* prefix_len, int32_t max_prefix_len,
+                                lcs_set_mode mode, int32_t top_k, int32_t n_sink, int32_t n_recent,
+                                int32_t block_size, int32_t* indices, int32_t* counts, int32_t cap,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_rows < 1 || n_rows > 64) return fail(LCS_E_ARG, "n_rows %d outside [1, 64]", n_rows);
+  if (kind != LCS_SCORE_LOGIT_SUM && kind != LCS_SCORE_SOFTMAX_WEIGHT)
+    return fail(LCS_E_ARG, "unknown score kind %d", (int)kind);
+  if (kind == LCS_SCORE_SOFTMAX_WEIGHT) {
+    if (n_q < 1 || n_q > 64) return fail(LCS_E_ARG, "n_q %d outside [1, 64]", n_q);
+    if (__builtin_popcountll(rows_mask) != n_rows || (n_q < 64 && (rows_mask >> n_q) != 0))
+      return fail(LCS_E_ARG, "rows_mask 0x%llx must name n_rows = %d rows below n_q = %d",
+                  (unsigned long long)rows_mask, n_rows, n_q);
+  }
+  return select_impl(logits, logits_ld, n_rows,
+                     kind == LCS_SCORE_SOFTMAX_WEIGHT ? lcs::SCORE_SOFTMAX_WT : lcs::SCORE_LOGIT_SUM, lse, n_q,
+                     rows_mask, B, Hq, Hkv, prefix_len, max_prefix_len, mode, top_k, n_sink, n_recent, block_size,
+                     indices, counts, cap, workspace, workspace_bytes, stream);
 }
 
 size_t lcs_sparse_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq, const lcs_paged_kv* kv,
@@ -254,7 +388,6 @@ lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t 
   a.tail_len = tail_len;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.c0 = a.c1 = -1;
   a.out = out;
   a.lse = lse;
   return hip_status(lcs::attn_launch(plan, a, workspace, static_cast<hipStream_t>(stream)));

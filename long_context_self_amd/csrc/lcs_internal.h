@@ -50,11 +50,18 @@ struct AttnArgs {
   const int32_t* ucount;
   int32_t ucap;
   float scale, scale_log2;
-  // Collect-2-Query (dense only)
-  int32_t c0, c1;
+  // Collected logit rows (dense only).  Verifier row i is collected iff bit i of cmask
+  // is set; it goes to slot popcount(cmask below i) of the n_cl slots per head, to the
+  // other slot of two when cswap is set, and to slots 0 and 1 when cdup is set.
+  uint64_t cmask;
+  int32_t n_cl, cswap, cdup;
   float* logits;
   int64_t logits_ld;
   int32_t lvec4;   // logits rows 16-byte aligned (16-byte stores allowed)
+  // Per-KV-head partial scores instead of logits (dense only): [B][Hkv][scores_ld],
+  // the sum over the group's heads, ascending, of (row0 + row1) logits
+  float* scores;
+  int64_t scores_ld;
   // split-K
   float* part;
   int32_t n_split;
@@ -86,9 +93,18 @@ constexpr int kItemChunk = 4096;       // items per workgroup of the collect and
 constexpr int kMaxItemChunks = 4096;   // items < 2^24
 constexpr int kHistBins = 4096;        // first radix digit: top 12 bits of the key
 
+// Position score of a set (the selection passes are identical for both):
+//   SCORE_LOGIT_SUM:   per head, the collected rows' logits summed in slot order;
+//   SCORE_SOFTMAX_WT:  per head, the rows' softmax weights exp(logit - lse) summed.
+enum ScoreKind : int32_t { SCORE_LOGIT_SUM = 0, SCORE_SOFTMAX_WT = 1 };
+
 struct SelArgs {
   const float* logits;
   int64_t ld;
+  int32_t n_rows, kind;    // logit rows per head; ScoreKind
+  const float* lse;        // SCORE_SOFTMAX_WT: [B][n_q][Hq]
+  int32_t n_q;
+  uint64_t rows_mask;      // SCORE_SOFTMAX_WT: slot c holds verifier row = c-th set bit
   int32_t B, Hq, Hkv, G, n_sets, mode;
   const int32_t* prefix_len;
   int32_t max_len;

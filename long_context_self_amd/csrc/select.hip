@@ -9,7 +9,10 @@
 //  * SSV page, NSA block selection: a block scores the max of its positions.
 //  Score of position p: sigma_p = sum over the set's heads h (ascending) of
 //  (l[h,row0,p] + l[h,row1,p]) in that fixed fp32 order; -0 is taken as +0.  Ties
-//  at the k-th place go to the smaller index; output is ascending.
+//  at the k-th place go to the smaller index; output is ascending.  With n collected
+//  rows the head term is (((l0 + l1) + l2) + ...); with softmax weights (Sparse
+//  Glimpse page, "Core claim": per-head attention weights of the last verification
+//  queries) it is the same sum of exp(l[h,c,p] - lse[h,row_c]).
 //
 // How
 //  * score_kernel streams the two logit rows of every head once (the only HBM-
@@ -26,8 +29,9 @@
 //    per-chunk counts into output offsets.
 //  * emit_kernel rescans each chunk and writes the kept items in ascending order
 //    with a workgroup prefix sum.
-//  No transcendental function and no multiply is involved, so the result is
-//  bit-identical to the same rule evaluated on the CPU in the same order.
+//  With logit sums no transcendental function and no multiply is involved, so the
+//  result is bit-identical to the same rule evaluated on the CPU in the same order;
+//  softmax weights go through expf and match the CPU rule to within its rounding.
 #include "lcs_internal.h"
 
 namespace lcs {
@@ -119,7 +123,42 @@ __global__ void zero_kernel(SelArgs a, int NS) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < NS; i += gridDim.x * blockDim.x) a.cand_count[i] = 0;
 }
 
+// Score of one head's rows at positions p, p + 1 (both < L when BOTH), into t0, t1.
+// NR2: exactly two rows (the Collect-2-Query layout), summed as one pair.
+template <int KIND, bool NR2, bool BOTH>
+__device__ __forceinline__ void head_score(const SelArgs& a, const float* hb, int b, int h, float& t0, float& t1) {
+  const int nr = NR2 ? 2 : a.n_rows;
+  if (KIND == SCORE_LOGIT_SUM) {
+    if (BOTH) {
+      float2 x = *reinterpret_cast<const float2*>(hb);
+      t0 = x.x;
+      t1 = x.y;
+      for (int c = 1; c < nr; ++c) {
+        x = *reinterpret_cast<const float2*>(hb + (size_t)c * a.ld);
+        t0 = t0 + x.x;
+        t1 = t1 + x.y;
+      }
+    } else {
+      t0 = hb[0];
+      for (int c = 1; c < nr; ++c) t0 = t0 + hb[(size_t)c * a.ld];
+      t1 = 0.f;
+    }
+  } else {
+    uint64_t rm = a.rows_mask;
+    t0 = t1 = 0.f;
+    for (int c = 0; c < nr; ++c) {
+      const int row = __builtin_ctzll(rm);
+      rm &= rm - 1;
+      const float ls = a.lse[((size_t)b * a.n_q + row) * a.Hq + h];
+      const float* rp = hb + (size_t)c * a.ld;
+      t0 = t0 + expf(rp[0] - ls);
+      if (BOTH) t1 = t1 + expf(rp[1] - ls);
+    }
+  }
+}
+
 // sigma, keys and the first-digit histogram for kScorePos positions of one set.
+template <int KIND, bool NR2>
 __global__ void __launch_bounds__(256) score_kernel(SelArgs a) {
   const int set = blockIdx.y;
   const int b = set / a.n_sets;
@@ -141,21 +180,26 @@ __global__ void __launch_bounds__(256) score_kernel(SelArgs a) {
 
   const int p = p0 + 2 * tid;          // this thread's two positions
   float acc0 = 0.f, acc1 = 0.f;
-  const float* base = a.logits + (size_t)b * a.Hq * 2 * a.ld;
+  const int nr = NR2 ? 2 : a.n_rows;
+  const float* base = a.logits + (size_t)b * a.Hq * nr * a.ld;
   if (a.vec4 && p + 1 < w.L) {
 #pragma unroll 8
     for (int hh = 0; hh < nh; ++hh) {
-      const float* r0 = base + (size_t)(h0 + hh) * 2 * a.ld + p;
-      const float2 x0 = *reinterpret_cast<const float2*>(r0);
-      const float2 x1 = *reinterpret_cast<const float2*>(r0 + a.ld);
-      acc0 = acc0 + (x0.x + x1.x);
-      acc1 = acc1 + (x0.y + x1.y);
+      float t0, t1;
+      head_score<KIND, NR2, true>(a, base + (size_t)(h0 + hh) * nr * a.ld + p, b, h0 + hh, t0, t1);
+      acc0 = acc0 + t0;
+      acc1 = acc1 + t1;
     }
   } else if (p < w.L) {
     for (int hh = 0; hh < nh; ++hh) {
-      const float* r0 = base + (size_t)(h0 + hh) * 2 * a.ld + p;
-      acc0 = acc0 + (r0[0] + r0[a.ld]);
-      if (p + 1 < w.L) acc1 = acc1 + (r0[1] + r0[a.ld + 1]);
+      const float* hb = base + (size_t)(h0 + hh) * nr * a.ld + p;
+      float t0, t1, u0, u1;
+      head_score<KIND, NR2, false>(a, hb, b, h0 + hh, t0, t1);
+      acc0 = acc0 + t0;
+      if (p + 1 < w.L) {
+        head_score<KIND, NR2, false>(a, hb + 1, b, h0 + hh, u0, u1);
+        acc1 = acc1 + u0;
+      }
     }
   }
   const uint32_t k0 = f2key(acc0), k1 = f2key(acc1);
@@ -473,7 +517,13 @@ hipError_t select_launch(const SelPlan& p, SelArgs a, void* workspace, hipStream
   hipLaunchKernelGGL(zero_kernel, dim3(min(1024, (NS * kHistBins + 255) / 256)), dim3(256), 0, stream, a, NS);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(score_kernel, dim3(p.n_pos_chunks, NS), dim3(256), 0, stream, a);
+  const dim3 sgrid(p.n_pos_chunks, NS);
+  if (a.kind == SCORE_SOFTMAX_WT)
+    hipLaunchKernelGGL((score_kernel<SCORE_SOFTMAX_WT, false>), sgrid, dim3(256), 0, stream, a);
+  else if (a.n_rows == 2)
+    hipLaunchKernelGGL((score_kernel<SCORE_LOGIT_SUM, true>), sgrid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((score_kernel<SCORE_LOGIT_SUM, false>), sgrid, dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(collect_kernel, dim3(p.n_chunks, NS), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -1,0 +1,161 @@
+"""Measurements of the scoring variants on synthetic workloads.
+
+    python -m long_context_self_amd.experiments collect-overhead --config llama8b_32k
+    python -m long_context_self_amd.experiments overlap --config llama8b_32k
+
+collect-overhead: verify latency against the number of collected logit rows (none,
+one, the two boundary rows, half, all n_q).  The Vegas page (Figure 6 and its text)
+reports that collecting more rows slows verification through memory-bandwidth
+contention and keeps two for that reason; this is the same curve for these kernels.
+Each call runs on a KV replica last touched several calls earlier, so it reads HBM.
+
+overlap: how far the selected sets of the scoring variants agree, and how many of
+the planted critical positions each one holds.  The Vegas page (Figure 7, Table 1)
+compares the boundary-row selection with one driven by every verifier row; the
+Sparse Glimpse page scores by the post-softmax weights of the last verification
+queries.  Overlap counts the top-k part only (the sink and recent windows are the
+same for every variant) against the all-row logit selection.
+
+Host orchestration only: every step runs in the library's kernels.  Inputs are the
+seeded synthetic workloads of `synth`; the numbers are properties of those inputs,
+not of any dataset.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import sys
+
+import numpy as np
+
+
+def _dev_inputs(torch, cfg, seed, replicas):
+    from . import lcs, synth
+    kv = synth.make_paged_kv(cfg, seed=seed)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=seed)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    k0, v0 = bf16(kv.k), bf16(kv.v)
+    bt = torch.from_numpy(kv.block_table).to("cuda")
+    layers = [lcs.PagedKV(k0 if r == 0 else k0.clone(), v0 if r == 0 else v0.clone(), bt) for r in range(replicas)]
+    return kv, layers, bf16(q), torch.from_numpy(kv.prefix_len).to("cuda")
+
+
+def collect_overhead(cfg, replicas: int, iters: int, seed: int = 0) -> dict:
+    import torch
+
+    from . import lcs
+    kv, layers, q, pl = _dev_inputs(torch, cfg, seed, replicas)
+    B, Hq, L, n_q = cfg.B, cfg.Hq, cfg.L, cfg.n_q
+    scale = 1.0 / math.sqrt(cfg.d)
+    sets = {"0": [], "1": [n_q - 1], "2": [0, n_q - 1], "half": list(range(0, n_q, 2)), "all": list(range(n_q))}
+    out = torch.empty((B, n_q, Hq, cfg.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, n_q, Hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lcs.verify_workspace_bytes(layers[0], B, n_q, Hq, L), dtype=torch.uint8, device="cuda")
+    res = {}
+    for name, rows in sets.items():
+        lg = (torch.empty((B, Hq, len(rows), L), dtype=torch.float32, device="cuda") if rows else None)
+
+        def call(r):
+            lcs.verify_attn_rows(layers[r], q, pl, L, scale, rows or [0], out=out, logits=lg, lse=lse,
+                                 workspace=ws, with_logits=bool(rows))
+        for r in range(replicas):
+            call(r)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            for r in range(replicas):
+                call(r)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (iters * replicas)
+        kv_bytes = 4 * B * cfg.Hkv * cfg.d * (L + n_q)
+        res[name] = {"rows": len(rows), "verify_us": round(us, 2),
+                     "logit_bytes_over_kv": round(4 * B * Hq * len(rows) * L / kv_bytes, 4)}
+        del lg
+    base = res["0"]["verify_us"]
+    for v in res.values():
+        v["overhead"] = round(v["verify_us"] / base - 1.0, 4)
+    return {"config": cfg.name, "replicas": replicas, "iters": iters, "points": res}
+
+
+def _topk_part(idx, cnt, b, s, L, cfg):
+    sel = idx[b, s, :int(cnt[b, s])]
+    return sel[(sel >= cfg.n_sink) & (sel < L - cfg.n_recent)]
+
+
+def overlap(cfg, seed: int = 0) -> dict:
+    import torch
+
+    from . import lcs
+    kv, layers, q, pl = _dev_inputs(torch, cfg, seed, 1)
+    n_q, L = cfg.n_q, cfg.L
+    scale = 1.0 / math.sqrt(cfg.d)
+    W = min(16, n_q)
+    rows_all = list(range(n_q))
+    _, lg_all, lse = lcs.verify_attn_rows(layers[0], q, pl, L, scale, rows_all)
+    variants = {
+        "all_rows_logits": (rows_all, "logits"),
+        "boundary_rows_logits": ([0, n_q - 1], "logits"),
+        "first_row_logits": ([0], "logits"),
+        "last_row_logits": ([n_q - 1], "logits"),
+        "last_W_rows_weights": (list(range(n_q - W, n_q)), "weights"),
+        "boundary_rows_weights": ([0, n_q - 1], "weights"),
+    }
+    sel = {}
+    for name, (rows, kind) in variants.items():
+        lg = lg_all[:, :, rows].contiguous()
+        idx, cnt = lcs.select_topk_rows(lg, pl, L, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent,
+                                        score=kind, lse=lse, rows=rows)
+        torch.cuda.synchronize()
+        sel[name] = (idx.cpu().numpy(), cnt.cpu().numpy())
+    n_sets = 1 if cfg.mode == "shared" else cfg.Hkv
+    ref_i, ref_c = sel["all_rows_logits"]
+    res = {}
+    for name, (idx, cnt) in sel.items():
+        ov, rec = [], []
+        for b in range(cfg.B):
+            Lb = int(kv.prefix_len[b])
+            for s in range(n_sets):
+                a = _topk_part(idx, cnt, b, s, Lb, cfg)
+                r = _topk_part(ref_i, ref_c, b, s, Lb, cfg)
+                if r.size:
+                    ov.append(np.isin(a, r).sum() / r.size)
+            for g in range(cfg.Hkv):
+                crit = kv.critical[b][g]
+                if crit.size:
+                    s = 0 if cfg.mode == "shared" else g
+                    rec.append(np.isin(crit, idx[b, s, :int(cnt[b, s])]).mean())
+        res[name] = {"rows": variants[name][0], "score": variants[name][1],
+                     "overlap_with_all_rows": round(float(np.mean(ov)), 4),
+                     "critical_recall": round(float(np.mean(rec)), 4) if rec else None}
+    blind = (cfg.n_sink + cfg.top_k + cfg.n_recent) / cfg.L
+    return {"config": cfg.name, "mode": cfg.mode, "top_k": cfg.top_k, "blind_recall": round(blind, 4),
+            "variants": res}
+
+
+def main(argv=None) -> None:
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("what", choices=["collect-overhead", "overlap"])
+    p.add_argument("--config", default="llama8b_32k")
+    p.add_argument("--replicas", type=int, default=0, help="KV copies rotated per timed call (0: sized to ~2 GB)")
+    p.add_argument("--iters", type=int, default=5)
+    p.add_argument("--seed", type=int, default=0)
+    a = p.parse_args(argv)
+    from . import synth
+    cfg = synth.CONFIGS[a.config]
+    if a.what == "collect-overhead":
+        kv_bytes = 4 * cfg.B * cfg.Hkv * cfg.d * cfg.L
+        reps = a.replicas or max(2, min(16, int(2e9 // kv_bytes)))
+        res = collect_overhead(cfg, reps, a.iters, a.seed)
+    else:
+        res = overlap(cfg, a.seed)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

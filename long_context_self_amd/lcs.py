@@ -38,13 +38,22 @@ class PagedKVDesc(ctypes.Structure):
 
 
 _i32, _i64, _sz, _p, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_u64 = ctypes.c_uint64
 _KV = ctypes.POINTER(PagedKVDesc)
 
 SIGNATURES = {
     "lcs_verify_workspace_bytes": (_sz, [_i32, _i32, _i32, _KV, _i32]),
     "lcs_verify_attn": (_i32, [_KV, _p, _i32, _i32, _i32, _p, _i32, _p, _f, _i32, _i32, _p, _p, _i64,
                               _p, _p, _sz, _p]),
+    "lcs_verify_attn_rows": (_i32, [_KV, _p, _i32, _i32, _i32, _p, _i32, _p, _f, _u64, _p, _p, _i64,
+                                   _p, _p, _sz, _p]),
+    "lcs_verify_attn_scores": (_i32, [_KV, _p, _i32, _i32, _i32, _p, _i32, _p, _f, _i32, _i32, _p, _p,
+                                     _i64, _p, _p, _sz, _p]),
     "lcs_select_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "lcs_select_topk_scores": (_i32, [_p, _i64, _i32, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p,
+                                     _i32, _p, _sz, _p]),
+    "lcs_select_topk_rows": (_i32, [_p, _i64, _i32, _i32, _p, _i32, _u64, _i32, _i32, _i32, _p, _i32, _i32,
+                                   _i32, _i32, _i32, _i32, _p, _p, _i32, _p, _sz, _p]),
     "lcs_select_topk": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                               _p, _p, _i32, _p, _sz, _p]),
     "lcs_sparse_workspace_bytes": (_sz, [_i32, _i32, _i32, _KV, _i32, _i32, _i32]),
@@ -140,6 +149,92 @@ def verify_attn(kv: PagedKV, q: torch.Tensor, prefix_len: torch.Tensor, max_pref
     return out, logits, lse
 
 
+def rows_mask(rows) -> int:
+    """Bit mask of verifier rows (ascending slots in the collected logits)."""
+    m = 0
+    for r in rows:
+        m |= 1 << int(r)
+    return m
+
+
+def verify_attn_rows(kv: PagedKV, q: torch.Tensor, prefix_len: torch.Tensor, max_prefix_len: int,
+                     scale: float, rows, tree_mask: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     with_logits: bool = True):
+    """lcs_verify_attn_rows.  rows: the verifier rows to collect (any order; slots are
+    ascending).  Returns (out, logits [B][Hq][len(rows)][ld] or None, lse)."""
+    B, n_q, Hq, d = q.shape
+    dev = q.device
+    mask = rows_mask(rows)
+    n_c = bin(mask).count("1")
+    if out is None:
+        out = torch.empty((B, n_q, Hq, d), dtype=torch.float32, device=dev)
+    if logits is None and with_logits and n_c > 0:
+        logits = torch.empty((B, Hq, n_c, max(max_prefix_len, 1)), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, n_q, Hq), dtype=torch.float32, device=dev)
+    desc = kv.desc()
+    need = load().lcs_verify_workspace_bytes(B, n_q, Hq, ctypes.byref(desc), max_prefix_len)
+    ws = _workspace(need, dev, workspace)
+    ld = logits.shape[-1] if logits is not None else 0
+    _check(load().lcs_verify_attn_rows(ctypes.byref(desc), _ptr(q), B, n_q, Hq, _ptr(prefix_len),
+                                       max_prefix_len, _ptr(tree_mask), scale, mask, _ptr(out),
+                                       _ptr(logits), ld, _ptr(lse), ws.data_ptr(), ws.numel(), _stream()))
+    return out, logits, lse
+
+
+def verify_attn_scores(kv: PagedKV, q: torch.Tensor, prefix_len: torch.Tensor, max_prefix_len: int,
+                       scale: float, collect_rows: Tuple[int, int], tree_mask: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """lcs_verify_attn_scores.  Returns (out, scores [B][Hkv][ld], lse)."""
+    B, n_q, Hq, d = q.shape
+    dev = q.device
+    Hkv = kv.k.shape[1]
+    if out is None:
+        out = torch.empty((B, n_q, Hq, d), dtype=torch.float32, device=dev)
+    if scores is None:
+        scores = torch.empty((B, Hkv, max(max_prefix_len, 1)), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, n_q, Hq), dtype=torch.float32, device=dev)
+    desc = kv.desc()
+    need = load().lcs_verify_workspace_bytes(B, n_q, Hq, ctypes.byref(desc), max_prefix_len)
+    ws = _workspace(need, dev, workspace)
+    _check(load().lcs_verify_attn_scores(ctypes.byref(desc), _ptr(q), B, n_q, Hq, _ptr(prefix_len),
+                                         max_prefix_len, _ptr(tree_mask), scale, collect_rows[0],
+                                         collect_rows[1], _ptr(out), _ptr(scores), scores.stride(1), _ptr(lse),
+                                         ws.data_ptr(), ws.numel(), _stream()))
+    return out, scores, lse
+
+
+def select_topk_scores(scores: torch.Tensor, prefix_len: torch.Tensor, max_prefix_len: int, mode: str,
+                       top_k: int, n_sink: int, n_recent: int, block_size: int = 0, cap: Optional[int] = None,
+                       indices: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, Hq: Optional[int] = None):
+    """lcs_select_topk_scores.  scores fp32 [B][Hkv][ld].  Returns (indices, counts)."""
+    B, Hkv = scores.shape[0], scores.shape[1]
+    dev = scores.device
+    n_sets = 1 if mode == "shared" else Hkv
+    if cap is None:
+        if mode == "block":
+            nb = -(-max_prefix_len // block_size)
+            cap = min(nb, -(-n_sink // block_size) + top_k + -(-n_recent // block_size) + 1)
+        else:
+            cap = min(max_prefix_len, n_sink + top_k + n_recent)
+        cap = max(cap, 1)
+    if indices is None:
+        indices = torch.full((B, n_sets, cap), -1, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.zeros((B, n_sets), dtype=torch.int32, device=dev)
+    need = load().lcs_select_workspace_bytes(B, Hq or Hkv, Hkv, SET_MODES[mode], max_prefix_len, block_size)
+    ws = _workspace(need, dev, workspace)
+    _check(load().lcs_select_topk_scores(_ptr(scores), scores.stride(1), B, Hkv, _ptr(prefix_len),
+                                         max_prefix_len, SET_MODES[mode], top_k, n_sink, n_recent, block_size,
+                                         _ptr(indices), _ptr(counts), cap, ws.data_ptr(), ws.numel(), _stream()))
+    return indices, counts
+
+
 def select_workspace_bytes(B: int, Hq: int, Hkv: int, mode: str, max_prefix_len: int,
                            block_size: int = 0) -> int:
     return load().lcs_select_workspace_bytes(B, Hq, Hkv, SET_MODES[mode], max_prefix_len, block_size)
@@ -170,6 +265,41 @@ def select_topk(logits: torch.Tensor, prefix_len: torch.Tensor, max_prefix_len: 
                                   max_prefix_len, SET_MODES[mode], top_k, n_sink, n_recent, block_size,
                                   _ptr(indices), _ptr(counts), cap, ws.data_ptr(), ws.numel(),
                                   _stream()))
+    return indices, counts
+
+
+SCORE_KINDS = {"logits": 0, "weights": 1}
+
+
+def select_topk_rows(logits: torch.Tensor, prefix_len: torch.Tensor, max_prefix_len: int, Hkv: int,
+                     mode: str, top_k: int, n_sink: int, n_recent: int, score: str = "logits",
+                     lse: Optional[torch.Tensor] = None, rows=None, block_size: int = 0,
+                     cap: Optional[int] = None, indices: Optional[torch.Tensor] = None,
+                     counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """lcs_select_topk_rows.  logits fp32 [B][Hq][n_rows][ld]; score "logits" or
+    "weights" (the latter needs lse [B][n_q][Hq] and the collected rows)."""
+    B, Hq, n_rows = logits.shape[0], logits.shape[1], logits.shape[2]
+    dev = logits.device
+    n_sets = 1 if mode == "shared" else Hkv
+    if cap is None:
+        if mode == "block":
+            nb = -(-max_prefix_len // block_size)
+            cap = min(nb, -(-n_sink // block_size) + top_k + -(-n_recent // block_size) + 1)
+        else:
+            cap = min(max_prefix_len, n_sink + top_k + n_recent)
+        cap = max(cap, 1)
+    if indices is None:
+        indices = torch.full((B, n_sets, cap), -1, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.zeros((B, n_sets), dtype=torch.int32, device=dev)
+    n_q = lse.shape[1] if lse is not None else 0
+    mask = rows_mask(rows) if rows is not None else 0
+    need = load().lcs_select_workspace_bytes(B, Hq, Hkv, SET_MODES[mode], max_prefix_len, block_size)
+    ws = _workspace(need, dev, workspace)
+    _check(load().lcs_select_topk_rows(_ptr(logits), logits.stride(2), n_rows, SCORE_KINDS[score], _ptr(lse),
+                                       n_q, mask, B, Hq, Hkv, _ptr(prefix_len), max_prefix_len,
+                                       SET_MODES[mode], top_k, n_sink, n_recent, block_size, _ptr(indices),
+                                       _ptr(counts), cap, ws.data_ptr(), ws.numel(), _stream()))
     return indices, counts
 
 

@@ -78,15 +78,16 @@ def verify_visibility(prefix_len: int, n_q: int, tail_mask: Optional[Sequence[in
 def verify_attn(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
                 block_table: np.ndarray, prefix_len: np.ndarray, page_size: int,
                 scale: float, tree_mask: Optional[np.ndarray] = None,
-                collect_rows: Tuple[int, int] = None, logits_ld: Optional[int] = None,
+                collect_rows: Sequence[int] = None, logits_ld: Optional[int] = None,
                 return_weights: bool = False):
-    """Dense verify attention over the full paged cache, plus two logit rows.
+    """Dense verify attention over the full paged cache, plus collected logit rows.
 
     q_bits: bf16 [B][n_q][Hq][d]; k_bits/v_bits: bf16 [pages][Hkv][P][d].
-    Returns (out [B][n_q][Hq][d], logits [B][Hq][2][ld], lse [B][n_q][Hq]) in
-    float64; logits hold scale*q.k of rows collect_rows for prefix columns
-    p < prefix_len[b], NaN elsewhere.  With return_weights the softmax
-    weights [b][g] -> [n_q][G][L_b+n_q] are returned as a fourth item.
+    Returns (out [B][n_q][Hq][d], logits [B][Hq][n_c][ld], lse [B][n_q][Hq]) in
+    float64; slot c of logits holds scale*q.k of row collect_rows[c] (default
+    the two rows 0 and n_q - 1, the Vegas page's Collect-2-Query pair) for
+    prefix columns p < prefix_len[b], NaN elsewhere.  With return_weights the
+    softmax weights [b][g] -> [n_q][G][L_b+n_q] are returned as a fourth item.
     """
     B, n_q, Hq, d = q_bits.shape
     Hkv = k_bits.shape[1]
@@ -97,7 +98,7 @@ def verify_attn(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
     ld = Lmax if logits_ld is None else logits_ld
     out = np.zeros((B, n_q, Hq, d))
     lse = np.zeros((B, n_q, Hq))
-    logits = np.full((B, Hq, 2, ld), np.nan)
+    logits = np.full((B, Hq, len(collect_rows), ld), np.nan)
     weights = {}
     q = bf16_to_f64(q_bits)
     for b in range(B):

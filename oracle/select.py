@@ -27,6 +27,16 @@ Selection rule (the pages are silent on these points; our readings):
 ``scores_f32_pinned`` is the same score in float32 with the summation order
 fixed (heads ascending, each pair summed first); the GPU selector must match
 it bit for bit, so the top-k on the GPU's own logits can be compared exactly.
+
+Scoring variants (rule 1 with other inputs; readings of ours):
+* n collected rows instead of two: each head contributes the sum of its n rows'
+  logits (in float32: t = l0, then t = t + l_c in slot order, then the head sum).
+  All n_q rows is the all-row collection the Vegas page's Figure 6 prices.
+* Softmax weights (Sparse Glimpse page, "Core claim" and its parameter list: the
+  per-head attention weights of the last W = 16 verification queries are the
+  importance signal): each head contributes, over its collected rows r, the
+  weight exp(l[h, r, p] - lse[h, r]) of position p.  The page gives no formula for
+  the aggregation; a plain sum over rows and over the set's heads is ours.
 """
 from __future__ import annotations
 
@@ -52,7 +62,8 @@ def scores_f64(logits: np.ndarray, b: int, L: int, heads) -> np.ndarray:
 
 
 def scores_f32_pinned(logits: np.ndarray, b: int, L: int, heads) -> np.ndarray:
-    """sigma_p in float32, pinned order: acc = 0; for h ascending: acc = acc + (l0 + l1).
+    """sigma_p in float32, pinned order: acc = 0; for h ascending: acc = acc + t_h,
+    t_h = l0 for one row, (l0 + l1) for two, (((l0 + l1) + l2) + ...) for more.
 
     Negative zero is mapped to positive zero so that the two compare and key
     identically.
@@ -60,9 +71,38 @@ def scores_f32_pinned(logits: np.ndarray, b: int, L: int, heads) -> np.ndarray:
     x = np.asarray(logits[b, :, :, :L], dtype=np.float32)
     acc = np.zeros(L, dtype=np.float32)
     for h in heads:
-        pair = (x[h, 0] + x[h, 1]).astype(np.float32)
-        acc = (acc + pair).astype(np.float32)
+        t = x[h, 0].copy()
+        for c in range(1, x.shape[1]):
+            t = (t + x[h, c]).astype(np.float32)
+        acc = (acc + t).astype(np.float32)
     acc[acc == 0] = np.float32(0.0)
+    return acc
+
+
+def partial_scores_f32(logits: np.ndarray, b: int, L: int, Hq: int, Hkv: int) -> np.ndarray:
+    """Per-KV-head partial scores [Hkv][L] in float32: row g is the pinned-order score
+    of the G query heads of group g (acc = 0; acc = acc + (l0 + l1) over its heads).
+
+    Selecting from these, the shared score is the pinned sum over g of the rows
+    (grouped association), and a KV head's set scores by its own row, which is
+    exactly its per-KV-head score on the logits.
+    """
+    G = Hq // Hkv
+    return np.stack([scores_f32_pinned(logits, b, L, range(g * G, (g + 1) * G)) for g in range(Hkv)])
+
+
+def scores_weights_f64(logits: np.ndarray, lse: np.ndarray, rows, b: int, L: int, heads) -> np.ndarray:
+    """Softmax-weight score in float64: sum over heads h and slots c of
+    exp(l[b, h, c, p] - lse[b, rows[c], h]) for p < L.
+
+    logits [B][Hq][n_rows][ld] (slot c = verifier row rows[c]); lse [B][n_q][Hq],
+    natural log, over every position the row sees.
+    """
+    x = np.asarray(logits[b, :, :, :L], dtype=np.float64)
+    acc = np.zeros(L)
+    for h in heads:
+        for c, r in enumerate(rows):
+            acc += np.exp(x[h, c] - float(lse[b, r, h]))
     return acc
 
 
@@ -110,15 +150,22 @@ def topk_blocks(sigma: np.ndarray, L: int, top_k: int, n_sink: int, n_recent: in
 
 
 def select(logits: np.ndarray, prefix_len: np.ndarray, Hkv: int, mode: str, top_k: int,
-           n_sink: int, n_recent: int, block_size: int = 0, precision: str = "f64"):
+           n_sink: int, n_recent: int, block_size: int = 0, precision: str = "f64",
+           score_kind: str = "logits", lse: np.ndarray = None, rows=None):
     """Run the selector for every (sequence, set).
 
-    logits: [B][Hq][2][ld] (the two collected rows).  Returns a list over b of
-    lists over sets of ascending int64 arrays (positions, or block ids in
-    'block' mode, where sets are per KV head).
+    logits: [B][Hq][n_rows][ld] (the collected rows; two for Collect-2-Query).
+    score_kind "weights" scores by softmax weights (needs lse [B][n_q][Hq] and the
+    verifier row of each slot, rows).  Returns a list over b of lists over sets of
+    ascending int64 arrays (positions, or block ids in 'block' mode, where sets
+    are per KV head).
     """
     B, Hq = logits.shape[0], logits.shape[1]
-    score = scores_f64 if precision == "f64" else scores_f32_pinned
+    if score_kind == "weights":
+        def score(lg, b, L, heads):
+            return scores_weights_f64(lg, lse, rows, b, L, heads)
+    else:
+        score = scores_f64 if precision == "f64" else scores_f32_pinned
     res = []
     for b in range(B):
         L = int(prefix_len[b])

@@ -69,6 +69,50 @@ def test_verify_host_errors():
     assert verify(lcs, L, kv, B=0, q=0, out=0, prefix_len=0) == lcs.LCS_OK
 
 
+def test_verify_rows_host_errors():
+    lcs, L = lib()
+    kv = fake_kv(lcs)
+
+    def vr(**kw):
+        a = dict(q=0x4000, B=1, n_q=5, Hq=4, prefix_len=0x5000, max_len=40, tree=None, scale=0.1, mask=0b10001,
+                 out=0x6000, logits=0x7000, ld=40, lse=None, ws=0x8000, wsb=1 << 20)
+        a.update(kw)
+        return L.lcs_verify_attn_rows(ctypes.byref(kv), a["q"], a["B"], a["n_q"], a["Hq"], a["prefix_len"],
+                                      a["max_len"], a["tree"], a["scale"], a["mask"], a["out"], a["logits"],
+                                      a["ld"], a["lse"], a["ws"], a["wsb"], None)
+
+    assert vr(mask=0) == lcs.LCS_E_ARG                    # logits without rows
+    assert b"collect_mask" in L.lcs_last_error()
+    assert vr(mask=1 << 5) == lcs.LCS_E_ARG               # row 5 of 5
+    assert vr(n_q=65) == lcs.LCS_E_UNSUPPORTED
+    assert vr(ld=39) == lcs.LCS_E_SHAPE
+    assert vr(wsb=0) == lcs.LCS_E_WORKSPACE
+    assert vr(B=0, q=0, out=0, prefix_len=0) == lcs.LCS_OK
+    assert lcs.rows_mask([4, 0, 2]) == 0b10101
+
+
+def test_select_rows_host_errors():
+    lcs, L = lib()
+
+    def sr(**kw):
+        a = dict(lg=0x1000, ld=100, n=3, kind=0, lse=None, n_q=0, rm=0, B=1, Hq=4, Hkv=2, pl=0x2000, maxL=100,
+                 mode=0, k=10, ns=4, nr=8, bs=0, idx=0x3000, cnt=0x4000, cap=22, ws=0x5000, wsb=1 << 24)
+        a.update(kw)
+        return L.lcs_select_topk_rows(a["lg"], a["ld"], a["n"], a["kind"], a["lse"], a["n_q"], a["rm"], a["B"],
+                                      a["Hq"], a["Hkv"], a["pl"], a["maxL"], a["mode"], a["k"], a["ns"], a["nr"],
+                                      a["bs"], a["idx"], a["cnt"], a["cap"], a["ws"], a["wsb"], None)
+
+    assert sr(n=0) == lcs.LCS_E_ARG
+    assert sr(n=65) == lcs.LCS_E_ARG
+    assert sr(kind=2) == lcs.LCS_E_ARG
+    assert sr(kind=1, lse=None, n_q=9, rm=0b111) == lcs.LCS_E_ARG          # no lse
+    assert sr(kind=1, lse=0x6000, n_q=9, rm=0b11) == lcs.LCS_E_ARG         # 2 rows named, n = 3
+    assert sr(kind=1, lse=0x6000, n_q=2, rm=0b111) == lcs.LCS_E_ARG        # row 2 of 2
+    assert sr(kind=1, lse=0x6000, n_q=9, rm=0b111, B=0) == lcs.LCS_OK
+    assert sr(cap=21) == lcs.LCS_E_SHAPE
+    assert sr(wsb=10) == lcs.LCS_E_WORKSPACE
+
+
 def test_select_host_errors():
     lcs, L = lib()
 
@@ -124,3 +168,38 @@ def test_workspace_queries_are_deterministic():
     b = L.lcs_verify_workspace_bytes(1, 9, 32, ctypes.byref(kv), 32768)
     assert a == b and a > 0
     assert L.lcs_verify_workspace_bytes(1, 9, 33, ctypes.byref(kv), 32768) == 0
+
+
+def test_scores_host_errors():
+    lcs, L = lib()
+    kv = fake_kv(lcs)
+
+    def vs(kvd=kv, **kw):
+        a = dict(q=0x4000, B=1, n_q=5, Hq=4, prefix_len=0x5000, max_len=40, tree=None, scale=0.1, r0=0, r1=4,
+                 out=0x6000, sc=0x7000, ld=40, lse=None, ws=0x8000, wsb=1 << 20)
+        a.update(kw)
+        return L.lcs_verify_attn_scores(ctypes.byref(kvd), a["q"], a["B"], a["n_q"], a["Hq"], a["prefix_len"],
+                                        a["max_len"], a["tree"], a["scale"], a["r0"], a["r1"], a["out"], a["sc"],
+                                        a["ld"], a["lse"], a["ws"], a["wsb"], None)
+
+    assert vs(sc=0) == lcs.LCS_E_ARG
+    assert vs(ld=39) == lcs.LCS_E_SHAPE
+    assert vs(r1=5) == lcs.LCS_E_ARG
+    big = fake_kv(lcs, max_pages=64, num_pages=200)
+    assert vs(big, n_q=17, Hq=8) == lcs.LCS_E_UNSUPPORTED      # 68 rows: two row chunks
+    many = fake_kv(lcs, Hkv=1, d=64)
+    assert vs(many, n_q=1, Hq=16, r1=0) == lcs.LCS_E_UNSUPPORTED   # G = 16 > d/32 * 1 tile
+    assert vs(B=0, q=0, out=0, prefix_len=0, sc=0) == lcs.LCS_OK
+
+    def ss(**kw):
+        a = dict(sc=0x1000, ld=100, B=1, Hkv=2, pl=0x2000, maxL=100, mode=0, k=10, ns=4, nr=8, bs=0,
+                 idx=0x3000, cnt=0x4000, cap=22, ws=0x5000, wsb=1 << 24)
+        a.update(kw)
+        return L.lcs_select_topk_scores(a["sc"], a["ld"], a["B"], a["Hkv"], a["pl"], a["maxL"], a["mode"], a["k"],
+                                        a["ns"], a["nr"], a["bs"], a["idx"], a["cnt"], a["cap"], a["ws"], a["wsb"],
+                                        None)
+
+    assert ss(sc=0) == lcs.LCS_E_ARG
+    assert ss(ld=99) == lcs.LCS_E_SHAPE
+    assert ss(mode=9) == lcs.LCS_E_ARG
+    assert ss(B=0) == lcs.LCS_OK

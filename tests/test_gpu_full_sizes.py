@@ -4,7 +4,8 @@ in the launch configurations the benchmark and the loop driver use.
 The oracle cannot evaluate these calls whole, so it checks sampled outputs one by one:
 for a sampled (sequence, row, head) it gathers the visible K/V rows itself and runs
 plain fp64 softmax attention.  Selection is checked bit for bit with the pinned-order
-CPU rule on the GPU's own logits, for a few sets.
+CPU rule on the GPU's own logits, for a few sets, and the fused per-KV-head partial
+scores bit for bit against the pinned sums of those logits.
 """
 import numpy as np
 import pytest
@@ -52,7 +53,11 @@ def build(name):
     dlse = torch.full((B, 1, cfg.Hq), float("nan"), device="cuda")
     lcs.sparse_draft_attn(c.dkv, bf16_dev(c.qd, torch), cfg.mode, idx, cnt, pl, i32_dev(tl, torch),
                           cfg.n_q + cfg.n_draft, scale_for(cfg.d), out=dout, lse=dlse)
+    scores = torch.full((B, cfg.Hkv, L), float("nan"), device="cuda")
+    lcs.verify_attn_scores(c.dkv, bf16_dev(c.q, torch), pl, L, scale_for(cfg.d), cfg.collect_rows,
+                           scores=scores)
     torch.cuda.synchronize()
+    c.scores = scores.cpu().numpy()
     c.out, c.logits, c.lse = out.cpu().numpy(), logits.cpu().numpy(), lse.cpu().numpy()
     c.idx, c.cnt, c.tl = idx.cpu().numpy(), cnt.cpu().numpy(), tl
     c.dout, c.dlse = dout.cpu().numpy(), dlse.cpu().numpy()
@@ -119,3 +124,12 @@ def test_draft_sampled(case):
         o, _, l = oa.attention_one(qf[b, 0, h], K, V, sc)
         assert np.max(np.abs(case.dout[b, 0, h] - o)) <= OUT_TOL
         assert abs(case.dlse[b, 0, h] - l) <= 1e-3
+
+
+def test_partial_scores_bit_exact(case):
+    """The fused partial scores equal the pinned CPU sums of the written logits."""
+    cfg = case.cfg
+    for b in range(cfg.B):
+        L = int(case.kv.prefix_len[b])
+        want = osel.partial_scores_f32(case.logits, b, L, cfg.Hq, cfg.Hkv)
+        assert np.array_equal(case.scores[b, :, :L].view(np.uint32), want.view(np.uint32)), f"b {b}"

@@ -237,3 +237,22 @@ def test_sparse_single_index_and_empty_list():
     out, lse = oa.sparse_attn(q, kv.k, kv.v, kv.block_table, cfg.page_size, "shared", idx, cnt0,
                               kv.prefix_len, np.array([0]), scale)
     assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_verify_any_row_set_matches_brute_force():
+    """Collected rows in any order and count: slot c is row rows[c], against the
+    scalar brute force."""
+    cfg = small_cfg(n_q=5)
+    kv, q = make(cfg, seed=4, lens=[29, 37])
+    scale = 1.0 / math.sqrt(cfg.d)
+    for rows in ([2], [4, 1, 3], list(range(5))):
+        _, logits, _ = oa.verify_attn(q, kv.k, kv.v, kv.block_table, kv.prefix_len, cfg.page_size, scale,
+                                      collect_rows=rows)
+        assert logits.shape[2] == len(rows)
+        for b in range(cfg.B):
+            L = int(kv.prefix_len[b])
+            for c, r in enumerate(rows):
+                for h in range(cfg.Hq):
+                    _, _, lg = brute.attend(q[b, r, h], kv.k, kv.v, kv.block_table, b, h // cfg.G,
+                                            list(range(L + r + 1)), cfg.page_size, scale)
+                    np.testing.assert_allclose(logits[b, h, c, :L], lg[:L], rtol=0, atol=1e-12)

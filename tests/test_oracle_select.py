@@ -157,3 +157,89 @@ def test_planted_critical_recall_tiny():
     crit = set(np.concatenate(kv.critical[0]).tolist())
     recall = len(crit & chosen) / len(crit)
     assert recall > 0.6
+
+
+@pytest.mark.parametrize("n_rows", [1, 3, 9])
+def test_pinned_n_rows_exact_on_small_integers(n_rows):
+    """Small integers add exactly in float32 in any order, so the pinned n-row score
+    must equal the exact integer sum over heads and rows (a dropped row, head or
+    term, or a wrong axis, changes it)."""
+    rng = np.random.default_rng(n_rows)
+    B, Hq, L = 2, 6, 50
+    lg = rng.integers(-1000, 1000, size=(B, Hq, n_rows, L)).astype(np.float32)
+    for b in range(B):
+        for heads in ([0, 1, 2, 3, 4, 5], [2, 3]):
+            exact = lg[b, heads].astype(np.int64).sum(axis=(0, 1))
+            got = osel.scores_f32_pinned(lg, b, L, heads)
+            assert np.array_equal(got.astype(np.int64), exact)
+
+
+def test_pinned_n_rows_order():
+    """Within a head the rows are summed first, left to right: (((a + b) + c)) with
+    a = 2^24, b = c = 1 gives 2^24 (each 1 is absorbed), not 2^24 + 2."""
+    lg = np.zeros((1, 1, 3, 1), dtype=np.float32)
+    lg[0, 0, :, 0] = [2.0 ** 24, 1.0, 1.0]
+    assert osel.scores_f32_pinned(lg, 0, 1, [0])[0] == np.float32(2.0 ** 24)
+    lg[0, 0, :, 0] = [1.0, 1.0, 2.0 ** 24]
+    assert osel.scores_f32_pinned(lg, 0, 1, [0])[0] == np.float32(2.0 ** 24 + 2)
+
+
+def test_weights_closed_form_uniform_keys():
+    """Every key equal: row r of a chain sees L + r + 1 positions with equal weight, so
+    each prefix position scores sum over heads and collected rows of 1/(L + r + 1)."""
+    cfg = synth.Config("w", B=2, Hq=4, Hkv=2, d=16, L=40, page_size=8, n_q=4, n_draft=3,
+                       top_k=8, n_sink=2, n_recent=3, mode="shared", crit_frac=0.0)
+    kv = synth.make_paged_kv(cfg, seed=5, lens=[40, 23])
+    kv.k[...] = kv.k[0, 0, 0, :]                        # one key row everywhere
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=5)
+    rows = [3, 0, 2]
+    _, logits, lse = oa.verify_attn(q, kv.k, kv.v, kv.block_table, kv.prefix_len, cfg.page_size, 0.25,
+                                    collect_rows=rows)
+    for b in range(cfg.B):
+        L = int(kv.prefix_len[b])
+        for heads in (list(range(cfg.Hq)), [2, 3]):
+            got = osel.scores_weights_f64(logits, lse, rows, b, L, heads)
+            want = len(heads) * sum(1.0 / (L + r + 1) for r in rows)
+            np.testing.assert_allclose(got, want, rtol=1e-12, atol=0)
+
+
+def test_weights_mass_matches_softmax_weights():
+    """Per head, the weight scores over the prefix sum to the rows' prefix mass, which
+    the attention oracle's normalised weights give independently (one minus the mass
+    on the verifier tail)."""
+    cfg = synth.Config("w", B=1, Hq=4, Hkv=2, d=16, L=33, page_size=4, n_q=5, n_draft=4,
+                       top_k=8, n_sink=2, n_recent=3, mode="shared", crit_frac=0.05)
+    kv = synth.make_paged_kv(cfg, seed=6)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=6)
+    rows = [0, 4, 2]
+    _, logits, lse, W = oa.verify_attn(q, kv.k, kv.v, kv.block_table, kv.prefix_len, cfg.page_size, 0.25,
+                                       collect_rows=rows, return_weights=True)
+    L = int(kv.prefix_len[0])
+    for h in range(cfg.Hq):
+        g, hh = divmod(h, cfg.G)
+        got = osel.scores_weights_f64(logits, lse, rows, 0, L, [h]).sum()
+        want = sum(W[(0, g)][r, hh, :L].sum() for r in rows)
+        assert abs(got - want) < 1e-12
+        assert got < len(rows)
+
+
+def test_partial_scores_group_first_association():
+    """Shared selection from per-KV-head partials sums each group first: heads
+    (2^24, 1 | 1, 1) give 2^24 + 2 grouped but 2^24 flat (every 1 absorbed in turn)."""
+    lg = np.zeros((1, 4, 2, 1), dtype=np.float32)
+    lg[0, :, 0, 0] = [2.0 ** 24, 1.0, 1.0, 1.0]
+    part = osel.partial_scores_f32(lg, 0, 1, 4, 2)
+    assert part[:, 0].tolist() == [2.0 ** 24, 2.0]
+    grouped = osel.scores_f32_pinned(part[None, :, None, :], 0, 1, [0, 1])
+    flat = osel.scores_f32_pinned(lg, 0, 1, [0, 1, 2, 3])
+    assert grouped[0] == np.float32(2.0 ** 24 + 2) and flat[0] == np.float32(2.0 ** 24)
+
+
+def test_partial_scores_exact_on_small_integers():
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, L = 2, 12, 3, 40
+    lg = rng.integers(-500, 500, size=(B, Hq, 2, L)).astype(np.float32)
+    for b in range(B):
+        part = osel.partial_scores_f32(lg, b, L, Hq, Hkv)
+        want = lg[b].astype(np.int64).reshape(Hkv, Hq // Hkv, 2, L).sum(axis=(1, 2))
+        assert np.array_equal(part.astype(np.int64), want)
