@@ -43,21 +43,27 @@ def parse():
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--scores", action="store_true",
+                   help="verify writes per-KV-head partial scores and select reads them, instead of the "
+                        "two collected logit rows")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="run one device-to-device copy of this size first (counter calibration)")
     return p.parse_args()
 
 
-def algorithmic_bytes(cfg, S_draft, tail_lens):
-    """Bytes each call must move at minimum (bf16 = 2 B, fp32 / int32 = 4 B)."""
+def algorithmic_bytes(cfg, S_draft, tail_lens, scores=False):
+    """Bytes each call must move at minimum (bf16 = 2 B, fp32 / int32 = 4 B).  With
+    scores the verify call writes one fp32 partial-score row per KV head instead of
+    two logit rows per query head, and select reads those."""
     B, Hq, Hkv, d, L, n_q = cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.L, cfg.n_q
+    collected = 4 * B * Hkv * L if scores else 8 * B * Hq * L
     verify = (4 * B * Hkv * d * (L + n_q)        # K and V of every cached position
               + 2 * B * n_q * Hq * d             # Q
               + 4 * B * n_q * Hq * d             # O (fp32)
               + 4 * B * n_q * Hq                 # lse
-              + 8 * B * Hq * L)                  # two collected logit rows (fp32)
+              + collected)                       # two collected logit rows, or partial scores (fp32)
     n_sets = 1 if cfg.mode == "shared" else Hkv
-    select = 8 * B * Hq * L + 4 * B * n_sets * S_draft + 4 * B * n_sets
+    select = collected + 4 * B * n_sets * S_draft + 4 * B * n_sets
     drafts = []
     for tl in tail_lens:
         drafts.append(4 * B * Hkv * d * (S_draft + tl)   # gathered K and V rows, all KV heads
@@ -153,7 +159,10 @@ def main():
     S = cfg.n_sink + cfg.top_k + cfg.n_recent
     outs = torch.empty((B, cfg.n_q, Hq, cfg.d), dtype=torch.float32, device=dev)
     lses = torch.empty((B, cfg.n_q, Hq), dtype=torch.float32, device=dev)
-    logits = [torch.empty((B, Hq, 2, L), dtype=torch.float32, device=dev) for _ in range(R)]
+    if args.scores:
+        logits = [torch.empty((B, cfg.Hkv, L), dtype=torch.float32, device=dev) for _ in range(R)]
+    else:
+        logits = [torch.empty((B, Hq, 2, L), dtype=torch.float32, device=dev) for _ in range(R)]
     idx = [torch.empty((B, n_sets, S), dtype=torch.int32, device=dev) for _ in range(R)]
     cnt = [torch.empty((B, n_sets), dtype=torch.int32, device=dev) for _ in range(R)]
     dout = torch.empty((B, 1, Hq, cfg.d), dtype=torch.float32, device=dev)
@@ -166,12 +175,20 @@ def main():
                        dtype=torch.uint8, device=dev)
 
     def verify(r):
-        lcs.verify_attn(layers[r], qv, pl, L, scale, cfg.collect_rows, out=outs, logits=logits[r], lse=lses,
-                        workspace=ws_v)
+        if args.scores:
+            lcs.verify_attn_scores(layers[r], qv, pl, L, scale, cfg.collect_rows, out=outs, scores=logits[r],
+                                   lse=lses, workspace=ws_v)
+        else:
+            lcs.verify_attn(layers[r], qv, pl, L, scale, cfg.collect_rows, out=outs, logits=logits[r], lse=lses,
+                            workspace=ws_v)
 
     def select(r):
-        lcs.select_topk(logits[r], pl, L, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
-                        indices=idx[r], counts=cnt[r], workspace=ws_s)
+        if args.scores:
+            lcs.select_topk_scores(logits[r], pl, L, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
+                                   indices=idx[r], counts=cnt[r], workspace=ws_s, Hq=Hq)
+        else:
+            lcs.select_topk(logits[r], pl, L, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
+                            indices=idx[r], counts=cnt[r], workspace=ws_s)
 
     def draft(r, j):
         lcs.sparse_draft_attn(layers[r], qds[j], cfg.mode, idx[r], cnt[r], pl, tls[j], max_tl, scale,
@@ -228,7 +245,7 @@ def main():
 
     s_count = int(cnt[0].min().item())
     tail_lens = [cfg.n_q + j + 1 for j in range(cfg.n_draft)]
-    vb, sb, db = algorithmic_bytes(cfg, s_count, tail_lens)
+    vb, sb, db = algorithmic_bytes(cfg, s_count, tail_lens, scores=args.scores)
     step_bytes = R * (vb + sb + sum(db))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     v_gbs = vb / (t_verify_us * 1e-6) / 1e9
@@ -253,6 +270,7 @@ def main():
         "config": {"workload": cfg.name, "B": B, "Hq": Hq, "Hkv": cfg.Hkv, "d": cfg.d, "L": L,
                    "page_size": cfg.page_size, "n_q": cfg.n_q, "n_draft": cfg.n_draft,
                    "select": f"{cfg.mode} top-{cfg.top_k}+{cfg.n_sink} sink+{cfg.n_recent} recent",
+                   "collected": "per-KV-head partial scores" if args.scores else "two logit rows",
                    "layers": R},
         "kernels": {
             "verify": {"us": round(t_verify_us, 2), "bytes": vb, "GB/s": round(v_gbs, 1),
@@ -266,7 +284,8 @@ def main():
         },
         "gamma_attn": round(gamma_attn, 4),
         "roofline": {"bound": "hbm", "achieved": round(v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(v_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_record(vb),
+                     "frac": round(v_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if args.scores else traffic_record(vb),
                      "kernel": "verify_attn (attn_kernel + split-K combine), per launch"},
     }
     if not args.no_cpu_baseline:

@@ -11,7 +11,7 @@ kernels.  Per-call times come from HIP events on the calling stream; the recall 
 the current critical positions in the selected set is a quality sanity check of the
 synthetic workload, not a parity check.
 
-    python -m long_context_self_amd.driver --config stress_128k --iters 256
+    python -m long_context_self_amd.driver --config stress_128k --iters 256 [--scores]
 """
 from __future__ import annotations
 
@@ -42,7 +42,10 @@ def recall(cfg, kv, idx: np.ndarray, cnt: np.ndarray) -> float:
     return float(np.mean(vals)) if vals else float("nan")
 
 
-def run(cfg, iters: int, drift: float = 0.1, seed: int = 0, warmup: int = 1, log=None) -> dict:
+def run(cfg, iters: int, drift: float = 0.1, seed: int = 0, warmup: int = 1, log=None,
+        scores: bool = False) -> dict:
+    """scores: verify writes per-KV-head partial scores and select reads them, instead
+    of the two collected logit rows (same selection rule, one row per KV head)."""
     import torch
 
     from . import lcs, synth
@@ -57,7 +60,10 @@ def run(cfg, iters: int, drift: float = 0.1, seed: int = 0, warmup: int = 1, log
     n_sets = 1 if cfg.mode == "shared" else cfg.Hkv
     S = cfg.n_sink + cfg.top_k + cfg.n_recent
     pl = torch.from_numpy(kv.prefix_len).to(dev)
-    logits = torch.empty((B, Hq, 2, L), dtype=torch.float32, device=dev)
+    if scores:
+        logits = torch.empty((B, cfg.Hkv, L), dtype=torch.float32, device=dev)
+    else:
+        logits = torch.empty((B, Hq, 2, L), dtype=torch.float32, device=dev)
     out = torch.empty((B, cfg.n_q, Hq, d), dtype=torch.float32, device=dev)
     dout = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=dev)
     idx = torch.empty((B, n_sets, S), dtype=torch.int32, device=dev)
@@ -79,10 +85,18 @@ def run(cfg, iters: int, drift: float = 0.1, seed: int = 0, warmup: int = 1, log
         torch.cuda.synchronize()
         e = [E() for _ in range(4)]
         e[0].record()
-        lcs.verify_attn(layer, qv, pl, L, scale, cfg.collect_rows, out=out, logits=logits, workspace=ws_v)
+        if scores:
+            lcs.verify_attn_scores(layer, qv, pl, L, scale, cfg.collect_rows, out=out, scores=logits,
+                                   workspace=ws_v)
+        else:
+            lcs.verify_attn(layer, qv, pl, L, scale, cfg.collect_rows, out=out, logits=logits, workspace=ws_v)
         e[1].record()
-        lcs.select_topk(logits, pl, L, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
-                        indices=idx, counts=cnt, workspace=ws_s)
+        if scores:
+            lcs.select_topk_scores(logits, pl, L, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
+                                   indices=idx, counts=cnt, workspace=ws_s, Hq=Hq)
+        else:
+            lcs.select_topk(logits, pl, L, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
+                            indices=idx, counts=cnt, workspace=ws_s)
         e[2].record()
         for j in range(cfg.n_draft):
             lcs.sparse_draft_attn(layer, qd[j], cfg.mode, idx, cnt, pl, tls[j], max_tl, scale, out=dout,
@@ -108,7 +122,7 @@ def run(cfg, iters: int, drift: float = 0.1, seed: int = 0, warmup: int = 1, log
             print(f"iteration {it}: verify {tv:.1f} us, select {ts:.1f} us, draft step {td / max(cfg.n_draft, 1):.1f}"
                   f" us, recall {rec['recall'][-1]:.3f}", file=log, flush=True)
     med = {k: float(np.median(v)) for k, v in rec.items() if v}
-    return {"config": cfg.name, "iters": iters, "drift": drift, "median": med,
+    return {"config": cfg.name, "iters": iters, "drift": drift, "scores": scores, "median": med,
             "recall_first": rec["recall"][0] if rec["recall"] else None,
             "recall_last": rec["recall"][-1] if rec["recall"] else None,
             "gamma_attn": med["draft_us"] / med["verify_us"] if rec["verify_us"] else None}
@@ -120,10 +134,11 @@ def main(argv=None) -> None:
     p.add_argument("--iters", type=int, default=256)
     p.add_argument("--drift", type=float, default=0.1)
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--scores", action="store_true", help="per-KV-head partial scores instead of logit rows")
     a = p.parse_args(argv)
     from . import synth
     t0 = time.time()
-    res = run(synth.CONFIGS[a.config], a.iters, a.drift, a.seed, log=sys.stderr)
+    res = run(synth.CONFIGS[a.config], a.iters, a.drift, a.seed, log=sys.stderr, scores=a.scores)
     res["wall_s"] = round(time.time() - t0, 1)
     print(json.dumps(res), flush=True)
 

@@ -11,12 +11,12 @@ from gpu_helpers import require_gpu
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("mode", ["shared", "per_kv_head"])
-def test_driver_loop_with_drift(mode):
+@pytest.mark.parametrize("mode,scores", [("shared", False), ("per_kv_head", False), ("shared", True)])
+def test_driver_loop_with_drift(mode, scores):
     require_gpu()
     from long_context_self_amd import driver
     cfg = synth.CONFIGS["llama8b_32k"].with_(L=8192, top_k=512, crit_frac=0.01, mode=mode)
-    res = driver.run(cfg, iters=6, drift=0.1, seed=1)
+    res = driver.run(cfg, iters=6, drift=0.1, seed=1, scores=scores)
     med = res["median"]
     for key in ("verify_us", "select_us", "draft_us", "iter_us"):
         assert math.isfinite(med[key]) and med[key] > 0
