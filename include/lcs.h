@@ -159,7 +159,7 @@ lcs_status lcs_verify_attn_rows(const lcs_paged_kv* kv, const void* q, int32_t B
  *               l the scaled logits lcs_verify_attn would write (bit for bit);
  *               columns p < prefix_len[b] written, others untouched.
  * Every other argument is that of lcs_verify_attn (logits are not written).
- * Limits: n_q * Hq/Hkv <= 64, and Hq/Hkv <= d/32 * ceil(n_q * Hq/Hkv / 16)
+ * Limits: n_q * Hq/Hkv <= 48, and Hq/Hkv <= d/32 * ceil(n_q * Hq/Hkv / 16)
  * (the staging area); else LCS_E_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 lcs_status lcs_verify_attn_scores(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q,

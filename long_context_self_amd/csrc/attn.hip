@@ -1009,8 +1009,7 @@ hipError_t launch_main_mode(const AttnPlan& p, const AttnArgs& a, hipStream_t st
       switch (p.QT) {
         case 1: hipLaunchKernelGGL((attn_kernel<D, 1, MODE, true>), grid, dim3(256), 0, stream, a); break;
         case 2: hipLaunchKernelGGL((attn_kernel<D, 2, MODE, true>), grid, dim3(256), 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((attn_kernel<D, 3, MODE, true>), grid, dim3(256), 0, stream, a); break;
-        default: hipLaunchKernelGGL((attn_kernel<D, 4, MODE, true>), grid, dim3(256), 0, stream, a); break;
+        default: hipLaunchKernelGGL((attn_kernel<D, 3, MODE, true>), grid, dim3(256), 0, stream, a); break;
       }
       launched = true;
     }
@@ -1018,8 +1017,7 @@ hipError_t launch_main_mode(const AttnPlan& p, const AttnArgs& a, hipStream_t st
   if (!launched) switch (p.QT) {
     case 1: hipLaunchKernelGGL((attn_kernel<D, 1, MODE>), grid, dim3(256), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((attn_kernel<D, 2, MODE>), grid, dim3(256), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((attn_kernel<D, 3, MODE>), grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((attn_kernel<D, 4, MODE>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((attn_kernel<D, 3, MODE>), grid, dim3(256), 0, stream, a); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;

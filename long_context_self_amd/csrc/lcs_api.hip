@@ -129,7 +129,8 @@ lcs_status verify_impl(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t
     // the partial sums need both collected rows of every head of a group in one
     // workgroup, and their staging area (the Q tile) must hold 2G x 32 floats per wave
     if (plan.n_rc != 1)
-      return fail(LCS_E_UNSUPPORTED, "partial scores need n_q * Hq / Hkv <= 64 rows (have %d)", plan.rows);
+      return fail(LCS_E_UNSUPPORTED, "partial scores need n_q * Hq / Hkv <= %d rows (have %d)", lcs::kMaxRowsPerWG,
+                  plan.rows);
     if (256LL * a.G > 8LL * plan.QT * kv->d)
       return fail(LCS_E_UNSUPPORTED, "partial scores need Hq / Hkv <= %d at %d rows and d = %d",
                   plan.QT * kv->d / 32, plan.rows, kv->d);

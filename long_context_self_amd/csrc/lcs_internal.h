@@ -20,7 +20,8 @@ enum AttnMode : int32_t {
 
 constexpr int kStepTokens = 32;   // tokens consumed per inner step of a wave
 constexpr int kWaves = 4;         // waves per workgroup (one token stream each)
-constexpr int kMaxRowsPerWG = 64; // q-rows (n_q * G) handled by one workgroup
+constexpr int kMaxRowsPerWG = 48; // q-rows (n_q * G) handled by one workgroup: three 16-row
+                                  // tiles, the most whose accumulators fit one wave's registers
 constexpr int kMaxSplits = 128;   // split-K partials per (sequence, KV head, row chunk)
 constexpr int kNumCUs = 256;      // MI355X compute units
 

@@ -186,7 +186,7 @@ def test_scores_host_errors():
     assert vs(ld=39) == lcs.LCS_E_SHAPE
     assert vs(r1=5) == lcs.LCS_E_ARG
     big = fake_kv(lcs, max_pages=64, num_pages=200)
-    assert vs(big, n_q=17, Hq=8) == lcs.LCS_E_UNSUPPORTED      # 68 rows: two row chunks
+    assert vs(big, n_q=13, Hq=8) == lcs.LCS_E_UNSUPPORTED      # 52 rows: two row chunks
     many = fake_kv(lcs, Hkv=1, d=64)
     assert vs(many, n_q=1, Hq=16, r1=0) == lcs.LCS_E_UNSUPPORTED   # G = 16 > d/32 * 1 tile
     assert vs(B=0, q=0, out=0, prefix_len=0, sc=0) == lcs.LCS_OK

@@ -74,7 +74,7 @@ def test_reduced_configs(name, L, B):
 
 
 def test_ragged_tree_mask_many_rows():
-    # 8 tree rows x G=8 -> 64 rows per workgroup (four 16-row MFMA tiles)
+    # 8 tree rows x G=8 -> 64 rows: a 48-row and a 16-row chunk
     cfg = synth.Config("t", B=3, Hq=16, Hkv=2, d=128, L=300, page_size=16, n_q=8, n_draft=0,
                        top_k=8, n_sink=0, n_recent=0, mode="shared", crit_frac=0.02)
     kv = synth.make_paged_kv(cfg, seed=4, lens=[300, 17, 0])
