@@ -2,6 +2,7 @@
 
     python -m long_context_self_amd.experiments collect-overhead --config llama8b_32k
     python -m long_context_self_amd.experiments overlap --config llama8b_32k
+    python -m long_context_self_amd.experiments row-scaling --config llama8b_32k
 
 collect-overhead: verify latency against the number of collected logit rows (none,
 one, the two boundary rows, half, all n_q).  The Vegas page (Figure 6 and its text)
@@ -15,6 +16,9 @@ compares the boundary-row selection with one driven by every verifier row; the
 Sparse Glimpse page scores by the post-softmax weights of the last verification
 queries.  Overlap counts the top-k part only (the sink and recent windows are the
 same for every variant) against the all-row logit selection.
+
+row-scaling: verify latency against the number of verifier rows, up to 64 (trees of
+many drafts, SSV page), on the workload's shapes.
 
 Host orchestration only: every step runs in the library's kernels.  Inputs are the
 seeded synthetic workloads of `synth`; the numbers are properties of those inputs,
@@ -83,6 +87,41 @@ def collect_overhead(cfg, replicas: int, iters: int, seed: int = 0) -> dict:
     return {"config": cfg.name, "replicas": replicas, "iters": iters, "points": res}
 
 
+def row_scaling(cfg, replicas: int, iters: int, n_qs=(9, 16, 17, 33, 64), seed: int = 0) -> dict:
+    """Verify latency against the number of verifier rows (trees of up to 64 drafts),
+    the two boundary rows collected, on the workload's shapes with n_q replaced."""
+    import torch
+
+    from . import lcs
+    res = {}
+    for n_q in n_qs:
+        c = cfg.with_(n_q=n_q, n_draft=n_q - 1)
+        kv, layers, q, pl = _dev_inputs(torch, c, seed, replicas)
+        B, Hq, L = c.B, c.Hq, c.L
+        scale = 1.0 / math.sqrt(c.d)
+        out = torch.empty((B, n_q, Hq, c.d), dtype=torch.float32, device="cuda")
+        lg = torch.empty((B, Hq, 2, L), dtype=torch.float32, device="cuda")
+        ws = torch.empty(lcs.verify_workspace_bytes(layers[0], B, n_q, Hq, L), dtype=torch.uint8, device="cuda")
+
+        def call(r):
+            lcs.verify_attn(layers[r], q, pl, L, scale, (0, n_q - 1), out=out, logits=lg, workspace=ws)
+        for r in range(replicas):
+            call(r)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            for r in range(replicas):
+                call(r)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (iters * replicas)
+        res[str(n_q)] = {"rows_per_kv_group": n_q * c.G, "verify_us": round(us, 2)}
+        del layers, kv, lg, out, ws
+        torch.cuda.empty_cache()
+    return {"config": cfg.name, "replicas": replicas, "iters": iters, "points": res}
+
+
 def _topk_part(idx, cnt, b, s, L, cfg):
     sel = idx[b, s, :int(cnt[b, s])]
     return sel[(sel >= cfg.n_sink) & (sel < L - cfg.n_recent)]
@@ -140,7 +179,7 @@ def overlap(cfg, seed: int = 0) -> dict:
 
 def main(argv=None) -> None:
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    p.add_argument("what", choices=["collect-overhead", "overlap"])
+    p.add_argument("what", choices=["collect-overhead", "overlap", "row-scaling"])
     p.add_argument("--config", default="llama8b_32k")
     p.add_argument("--replicas", type=int, default=0, help="KV copies rotated per timed call (0: sized to ~2 GB)")
     p.add_argument("--iters", type=int, default=5)
@@ -148,10 +187,12 @@ def main(argv=None) -> None:
     a = p.parse_args(argv)
     from . import synth
     cfg = synth.CONFIGS[a.config]
+    kv_bytes = 4 * cfg.B * cfg.Hkv * cfg.d * cfg.L
+    reps = a.replicas or max(2, min(16, int(2e9 // kv_bytes)))
     if a.what == "collect-overhead":
-        kv_bytes = 4 * cfg.B * cfg.Hkv * cfg.d * cfg.L
-        reps = a.replicas or max(2, min(16, int(2e9 // kv_bytes)))
         res = collect_overhead(cfg, reps, a.iters, a.seed)
+    elif a.what == "row-scaling":
+        res = row_scaling(cfg, reps, a.iters, seed=a.seed)
     else:
         res = overlap(cfg, a.seed)
     print(json.dumps(res), flush=True)

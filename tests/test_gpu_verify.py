@@ -92,6 +92,36 @@ def test_row_chunks_beyond_64():
     check(cfg, kv, q)
 
 
+@pytest.mark.parametrize("n_q,G,d,tree,lens", [
+    (17, 4, 128, False, [700, 333]),     # 68 rows: chunks of 48 and 20
+    (33, 4, 128, True, [650]),           # 132 rows: three chunks
+    (64, 4, 128, False, [900, 1]),       # 256 rows: six chunks, the last of 16
+    (50, 4, 64, True, [513]),            # 200 rows at d = 64: five chunks
+])
+def test_large_tree_verify(n_q, G, d, tree, lens):
+    """Dense verify with many verifier rows (SSV page: trees of up to 64 drafts) over
+    several 48-row chunks; parity with the oracle, tree masks and ragged lengths."""
+    Hkv = 2
+    cfg = synth.Config("t", B=len(lens), Hq=G * Hkv, Hkv=Hkv, d=d, L=max(lens), page_size=16, n_q=n_q, n_draft=0,
+                       top_k=8, n_sink=0, n_recent=0, mode="shared", crit_frac=0.02)
+    kv = synth.make_paged_kv(cfg, seed=n_q, lens=lens)
+    q = synth.make_queries(cfg, kv, n_q, seed=n_q)
+    tm = None
+    if tree:
+        rng = np.random.default_rng(n_q)
+        # random ancestor sets: row i sees itself and a random subset of rows j < i
+        tm = np.zeros((cfg.B, n_q), dtype=np.uint64)
+        for b in range(cfg.B):
+            for i in range(n_q):
+                bits = (rng.random(i) < 0.3).astype(np.uint64)
+                m = 1 << i
+                for jj in np.nonzero(bits)[0]:
+                    m |= 1 << int(jj)
+                tm[b, i] = np.uint64(m)
+    err = check(cfg, kv, q, tree=tm)
+    print(f"n_q {n_q} G {G} d {d}: out max-abs err {err:.3e}")
+
+
 def test_v_ones_gives_ones():
     cfg = synth.CONFIGS["llama8b_32k"].with_(L=1000)
     kv = synth.make_paged_kv(cfg, seed=2)
