@@ -2,6 +2,8 @@
 
     python -m long_context_self_amd.profile_summary stats --csv <kernel_stats.csv | results.db> \\
         --command "<the rocprofv3 command>" --out profiles/<kernel>_<workload>.md
+    python -m long_context_self_amd.profile_summary counters --db <results.db> [--db ...] \\
+        --kernel <name> [--kernel ...] --command "..." [--command ...] --out profiles/<...>.md
     python -m long_context_self_amd.profile_summary traffic \\
         --fetch <counter_collection.csv | results.db of a FETCH_SIZE run> \\
         --write <counter_collection.csv | results.db of a WRITE_SIZE run> \\
@@ -27,7 +29,9 @@ import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("attn.hip", "lcs_internal.h")]
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("attn.hip", "select.hip", "lcs_internal.h")]
+SIMDS = 256 * 4          # MI355X: 256 compute units of 4 SIMDs
+XCDS = 8                 # GRBM_GUI_ACTIVE as collected per dispatch is the sum over the 8 XCDs
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -119,6 +123,42 @@ def traffic(args) -> None:
         fh.write("\n")
 
 
+def counters(args) -> None:
+    """Per-dispatch averages of every counter in one or more --pmc databases for the named
+    kernels, with the derived MFMA busy fraction, MFMA bf16 flops and LDS bank-conflict
+    rate where their inputs were collected."""
+    per = defaultdict(dict)
+    for path in args.db:
+        rows = sqlite3.connect(path).execute("select kernel_name, counter_name, value from counters_collection")
+        acc = defaultdict(list)
+        for name, cn, v in rows:
+            acc[(short_name(name), cn)].append(float(v))
+        for (k, cn), v in acc.items():
+            if k in args.kernel:
+                per[k][cn] = sum(v) / len(v)
+    out = ["# " + args.title, "", "Commands (run from the repository root):", ""]
+    out += ["```"] + list(args.command) + ["```", ""]
+    out += ["| kernel | counter | per dispatch |", "|---|---|---:|"]
+    for k in args.kernel:
+        for cn in sorted(per.get(k, {})):
+            out.append(f"| `{k}` | {cn} | {per[k][cn]:.4g} |")
+    out += ["", "| kernel | MFMA busy (% of SIMD cycles) | MFMA bf16 GFLOP | LDS bank conflicts / LDS cycles |",
+            "|---|---:|---:|---:|"]
+    for k in args.kernel:
+        c = per.get(k, {})
+        busy = (100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / XCDS * SIMDS)
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE") else None)
+        fl = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e9 if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c else None
+        lds = (c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]
+               if c.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in c else None)
+        f = lambda x, fmt: "—" if x is None else fmt % x  # noqa: E731
+        out.append(f"| `{k}` | {f(busy, '%.1f')} | {f(fl, '%.3f')} | {f(lds, '%.4f')} |")
+    if args.note:
+        out += ["", args.note]
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+
+
 def main(argv=None) -> None:
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -137,8 +177,15 @@ def main(argv=None) -> None:
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--db", action="append", required=True)
+    c.add_argument("--kernel", action="append", required=True)
+    c.add_argument("--command", action="append", required=True)
+    c.add_argument("--title", default="rocprofv3 counters")
+    c.add_argument("--note", default="")
+    c.add_argument("--out", required=True)
     a = p.parse_args(argv)
-    stats(a) if a.cmd == "stats" else traffic(a)
+    {"stats": stats, "traffic": traffic, "counters": counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
