@@ -89,6 +89,31 @@ def test_ties_and_ragged(mode):
     assert_exact(idx, cnt, cpu_rule(lg, lens, Hkv, mode, k, 5, 33, bs))
 
 
+@pytest.mark.parametrize("mode", ["shared", "per_kv_head", "block"])
+def test_one_bin_holds_every_candidate(mode):
+    """All scores equal: the whole pool lands in one first-digit bin, more candidates
+    than the finalize pass holds in LDS, and ties go to the smaller index."""
+    lens = np.array([60000, 33333], dtype=np.int32)
+    lg = np.full((2, 4, 2, 60000), 0.75, dtype=np.float32)
+    bs = 16 if mode == "block" else 0
+    k = 300 if mode == "block" else 5000
+    idx, cnt = gpu_select(lg, lens, 2, mode, k, 4, 64, bs)
+    assert_exact(idx, cnt, cpu_rule(lg, lens, 2, mode, k, 4, 64, bs))
+
+
+@pytest.mark.parametrize("mode", ["shared", "per_kv_head"])
+def test_sets_around_64k_items(mode):
+    """Sets just above and at 2^16 items (many 4096-item chunks, a ragged last chunk)
+    give the CPU rule's result."""
+    rng = np.random.default_rng(6)
+    lens = np.array([70001, 65536, 1000], dtype=np.int32)
+    lg = rng.standard_normal((3, 4, 2, 70004)).astype(np.float32)
+    idx, cnt = gpu_select(lg, lens, 2, mode, 3000, 4, 64)
+    assert_exact(idx, cnt, cpu_rule(lg, lens, 2, mode, 3000, 4, 64))
+    idx2, cnt2 = gpu_select(lg[1:, :, :, :65536].copy(), lens[1:], 2, mode, 3000, 4, 64)
+    assert_exact(idx2, cnt2, cpu_rule(lg[1:, :, :, :65536], lens[1:], 2, mode, 3000, 4, 64))
+
+
 @pytest.mark.parametrize("mode", ["shared", "block"])
 def test_short_context_keeps_everything(mode):
     rng = np.random.default_rng(4)
