@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_llama8b_32k_traffic.json")
+TRAFFIC_WORKLOAD = "llama8b_32k"   # the workload those counter runs measured
 
 
 def parse():
@@ -285,7 +286,7 @@ def main():
         "gamma_attn": round(gamma_attn, 4),
         "roofline": {"bound": "hbm", "achieved": round(v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(v_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None if args.scores else traffic_record(vb),
+                     "traffic": traffic_record(vb) if (args.config == TRAFFIC_WORKLOAD and not args.scores) else None,
                      "kernel": "verify_attn (attn_kernel + split-K combine), per launch"},
     }
     if not args.no_cpu_baseline:

@@ -951,50 +951,65 @@ __global__ void __launch_bounds__(256) block_union_kernel(AttnArgs a) {
   const int g = bg % a.Hkv;
   const int b = bg / a.Hkv;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   __shared__ uint32_t mlo[kPlanChunk];
   __shared__ uint32_t mhi[kPlanChunk];
-  __shared__ uint32_t tsum[256];
+  __shared__ uint32_t wsum[4];
+  __shared__ int32_t scnt[64];
   int32_t* ub = const_cast<int32_t*>(a.ublk) + (size_t)bg * a.ucap;
   uint64_t* um = const_cast<uint64_t*>(a.umask) + (size_t)bg * a.ucap;
   int total = 0;
   for (int base = 0; base < a.max_pages; base += kPlanChunk) {
-    for (int e = tid; e < kPlanChunk; e += 256) mlo[e] = mhi[e] = 0;
+    const int span = min(kPlanChunk, a.max_pages - base);     // block ids of this chunk
+    for (int e = tid; e < span; e += 256) mlo[e] = mhi[e] = 0;
     __syncthreads();
-    for (int i = 0; i < a.n_q && a.cap > 0; ++i) {
-      const size_t o = (size_t)(b * a.n_q + i) * a.Hkv + g;
-      const int cnt = min(max(a.counts[o], 0), a.cap);
-      const int32_t* lst = a.indices + o * a.cap;
-      for (int e = tid; e < cnt; e += 256) {
-        const int blk = lst[e];
-        if (blk >= base && blk < base + kPlanChunk && blk < a.max_pages) {
-          if (i < 32) atomicOr(&mlo[blk - base], 1u << i);
-          else atomicOr(&mhi[blk - base], 1u << (i - 32));
-        }
+    // every (row, entry) pair at once, so that the list loads do not wait on each other
+    if (tid < a.n_q) scnt[tid] = min(max(a.counts[(size_t)(b * a.n_q + tid) * a.Hkv + g], 0), a.cap);
+    __syncthreads();
+    const int n_ent = a.n_q * a.cap;
+    for (int f = tid; f < n_ent; f += 256) {
+      const int i = f / a.cap, e = f - i * a.cap;
+      if (e >= scnt[i]) continue;
+      const int blk = a.indices[((size_t)(b * a.n_q + i) * a.Hkv + g) * a.cap + e];
+      if (blk >= base && blk < base + span) {
+        if (i < 32) atomicOr(&mlo[blk - base], 1u << i);
+        else atomicOr(&mhi[blk - base], 1u << (i - 32));
       }
     }
     __syncthreads();
-    // ascending compaction: thread t owns ids [16t, 16t + 16)
+    // ascending compaction: thread t owns ids [16t, 16t + 16) of the chunk; an exclusive
+    // scan of the per-thread counts (wave shuffles, then the four wave totals)
     uint32_t c = 0;
-    for (int e = 0; e < 16; ++e) c += (mlo[16 * tid + e] | mhi[16 * tid + e]) != 0;
-    tsum[tid] = c;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const uint32_t v = (tid >= off) ? tsum[tid - off] : 0;
-      __syncthreads();
-      tsum[tid] += v;
-      __syncthreads();
-    }
-    uint32_t w = total + tsum[tid] - c;
     for (int e = 0; e < 16; ++e) {
       const int id = 16 * tid + e;
+      c += (id < span) && ((mlo[id] | mhi[id]) != 0);
+    }
+    uint32_t x = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    uint32_t pre = 0, chunk_total = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pre += (i < w) ? wsum[i] : 0u;
+      chunk_total += wsum[i];
+    }
+    uint32_t pos = total + pre + x - c;
+    for (int e = 0; e < 16; ++e) {
+      const int id = 16 * tid + e;
+      if (id >= span) break;
       const uint64_t msk = ((uint64_t)mhi[id] << 32) | mlo[id];
-      if (msk != 0 && (int)w < a.ucap) {
-        ub[w] = base + id;
-        um[w] = msk;
-        ++w;
+      if (msk != 0 && (int)pos < a.ucap) {
+        ub[pos] = base + id;
+        um[pos] = msk;
+        ++pos;
       }
     }
-    total += tsum[255];
+    total += chunk_total;
     __syncthreads();
   }
   if (tid == 0) const_cast<int32_t*>(a.ucount)[bg] = min(total, a.ucap);

@@ -3,6 +3,7 @@
     python -m long_context_self_amd.experiments collect-overhead --config llama8b_32k
     python -m long_context_self_amd.experiments overlap --config llama8b_32k
     python -m long_context_self_amd.experiments row-scaling --config llama8b_32k
+    python -m long_context_self_amd.experiments block-merge --config nsa_16k
 
 collect-overhead: verify latency against the number of collected logit rows (none,
 one, the two boundary rows, half, all n_q).  The Vegas page (Figure 6 and its text)
@@ -19,6 +20,9 @@ same for every variant) against the all-row logit selection.
 
 row-scaling: verify latency against the number of verifier rows, up to 64 (trees of
 many drafts, SSV page), on the workload's shapes.
+
+block-merge: SSV block mode (section 4.2 of the SSV page): the tree's rows in one call,
+which loads the union of their block sets once, against each row alone.
 
 Host orchestration only: every step runs in the library's kernels.  Inputs are the
 seeded synthetic workloads of `synth`; the numbers are properties of those inputs,
@@ -122,6 +126,71 @@ def row_scaling(cfg, replicas: int, iters: int, n_qs=(9, 16, 17, 33, 64), seed: 
     return {"config": cfg.name, "replicas": replicas, "iters": iters, "points": res}
 
 
+def block_merge(cfg, replicas: int, iters: int, seed: int = 0) -> dict:
+    """SSV block mode: the n_q tree rows in one call (the union of their block sets loaded
+    once) against each row alone (n_q calls, every row's blocks loaded for it)."""
+    import torch
+
+    from . import lcs, synth
+    kv = synth.make_paged_kv(cfg, seed=seed)
+    nblk = cfg.L // cfg.page_size
+    sets = synth.make_block_sets(cfg, nblk, seed=seed)
+    q_np = synth.make_queries(cfg, kv, cfg.n_q, seed=seed)
+    tm_np = np.stack([synth.tree_tail_masks(cfg.n_q, cfg.tree_branches)] * cfg.B)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    k0, v0 = bf16(kv.k), bf16(kv.v)
+    bt = torch.from_numpy(kv.block_table).to("cuda")
+    layers = [lcs.PagedKV(k0 if r == 0 else k0.clone(), v0 if r == 0 else v0.clone(), bt) for r in range(replicas)]
+    B, n_q, Hq, d = cfg.B, cfg.n_q, cfg.Hq, cfg.d
+    q = bf16(q_np)
+    idx = torch.from_numpy(sets).to("cuda")
+    cnt = torch.full((B, n_q, cfg.Hkv), cfg.blocks_per_row, dtype=torch.int32, device="cuda")
+    tb = torch.from_numpy(kv.prefix_len).to("cuda")
+    tl = torch.full((B,), n_q, dtype=torch.int32, device="cuda")
+    tm = torch.from_numpy(tm_np.view(np.int64)).to("cuda")
+    scale = 1.0 / math.sqrt(d)
+    rows = [(q[:, i:i + 1].contiguous(), idx[:, i:i + 1].contiguous(), cnt[:, i:i + 1].contiguous(),
+             tm[:, i:i + 1].contiguous()) for i in range(n_q)]
+    out = torch.empty((B, n_q, Hq, d), dtype=torch.float32, device="cuda")
+    out1 = torch.empty((B, 1, Hq, d), dtype=torch.float32, device="cuda")
+
+    def merged(r):
+        lcs.sparse_draft_attn(layers[r], q, "block", idx, cnt, tb, tl, n_q, scale, tail_mask=tm, out=out)
+
+    def unmerged(r):
+        for qi, ii, ci, ti in rows:
+            lcs.sparse_draft_attn(layers[r], qi, "block", ii, ci, tb, tl, n_q, scale, tail_mask=ti, out=out1)
+
+    res = {}
+    for name, fn in (("merged", merged), ("unmerged", unmerged)):
+        for r in range(replicas):
+            fn(r)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            for r in range(replicas):
+                fn(r)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = {"us": round(e0.elapsed_time(e1) * 1e3 / (iters * replicas), 2)}
+    # algorithmic K/V bytes: the union of the rows' blocks per (b, g) when merged, every
+    # row's own blocks when not (the tail of n_q tokens is read in both)
+    P = cfg.page_size
+    union = sum(len(np.unique(sets[b, :, g])) for b in range(B) for g in range(cfg.Hkv))
+    per_row = int(B * cfg.Hkv * n_q * cfg.blocks_per_row)
+    tail = B * cfg.Hkv * n_q
+    res["merged"]["kv_bytes"] = 4 * d * (P * union + tail)
+    res["unmerged"]["kv_bytes"] = 4 * d * (P * per_row + n_q * tail)
+    for v in res.values():
+        v["GB/s"] = round(v["kv_bytes"] / (v["us"] * 1e3), 1)
+    res["mean_union_blocks"] = round(union / (B * cfg.Hkv), 2)
+    return {"config": cfg.name, "replicas": replicas, "iters": iters, "points": res}
+
+
 def _topk_part(idx, cnt, b, s, L, cfg):
     sel = idx[b, s, :int(cnt[b, s])]
     return sel[(sel >= cfg.n_sink) & (sel < L - cfg.n_recent)]
@@ -179,7 +248,7 @@ def overlap(cfg, seed: int = 0) -> dict:
 
 def main(argv=None) -> None:
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    p.add_argument("what", choices=["collect-overhead", "overlap", "row-scaling"])
+    p.add_argument("what", choices=["collect-overhead", "overlap", "row-scaling", "block-merge"])
     p.add_argument("--config", default="llama8b_32k")
     p.add_argument("--replicas", type=int, default=0, help="KV copies rotated per timed call (0: sized to ~2 GB)")
     p.add_argument("--iters", type=int, default=5)
@@ -193,6 +262,8 @@ def main(argv=None) -> None:
         res = collect_overhead(cfg, reps, a.iters, a.seed)
     elif a.what == "row-scaling":
         res = row_scaling(cfg, reps, a.iters, seed=a.seed)
+    elif a.what == "block-merge":
+        res = block_merge(cfg, reps, a.iters, seed=a.seed)
     else:
         res = overlap(cfg, a.seed)
     print(json.dumps(res), flush=True)
