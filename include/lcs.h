@@ -16,6 +16,14 @@
  *    ("overlap-aware grouped-query execution", section 4.2 exact merged
  *    schedule, per-row causal masks at absolute positions).  -> lcs_sparse_draft_attn
  *
+ * Variants of the first two calls:
+ *  - any set of collected rows, and selection over n rows by summed logits or
+ *    by post-softmax weights (Vegas Figure 6 and Figure 7; Sparse Glimpse "Core
+ *    claim")  -> lcs_verify_attn_rows, lcs_select_topk_rows
+ *  - the head sum of the two rows done per KV head in the verify epilogue, one
+ *    score row per KV head handed to the selector  -> lcs_verify_attn_scores,
+ *    lcs_select_topk_scores
+ *
  * Conventions common to every call
  *  - Every pointer argument is DEVICE memory owned by the caller, except the
  *    lcs_paged_kv struct itself (host memory, read during the call only).

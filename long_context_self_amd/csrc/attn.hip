@@ -5,8 +5,10 @@
 // What is computed
 //  * Vegas page, "The pith" / "Core claim": verification is full attention of the
 //    k+1 verifier rows over the whole KV cache; the pre-softmax logits of the first
-//    draft row and the bonus row are written out (Figure 6 caption,
-//    "Collect-2-Query": two rows only, so the side traffic stays constant in k).
+//    draft row and the bonus row are written out (Figure 6 caption: two rows only,
+//    so the side traffic stays constant in k).  The same kernel also collects any
+//    other set of rows, or sums the two rows over each KV group's heads and writes
+//    one score row per KV head instead.
 //  * Vegas page, "The pith": drafting attends to the selected prefix entries only.
 //  * SSV page, section 4.2 (exact merged-schedule variant) and Figure 5: grouped
 //    verifier rows with different block sets load each shared block once; each row
@@ -40,7 +42,6 @@
 #include "lcs_internal.h"
 
 #include <math.h>
-
 
 #include <type_traits>
 

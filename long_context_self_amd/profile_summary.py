@@ -24,6 +24,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sqlite3
 import sys
 from collections import defaultdict
@@ -35,11 +36,19 @@ XCDS = 8                 # GRBM_GUI_ACTIVE as collected per dispatch is the sum 
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and whitespace: edits to comments leave the
+    kernels, and so the counters taken on them, unchanged."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
