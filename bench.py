@@ -30,7 +30,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0   # the peak line every fraction is taken against (metrics.HBM_PEAK_GBS)
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_llama8b_32k_traffic.json")
 TRAFFIC_WORKLOAD = "llama8b_32k"   # the workload those counter runs measured
 
@@ -53,24 +53,10 @@ def parse():
 
 
 def algorithmic_bytes(cfg, S_draft, tail_lens, scores=False):
-    """Bytes each call must move at minimum (bf16 = 2 B, fp32 / int32 = 4 B).  With
-    scores the verify call writes one fp32 partial-score row per KV head instead of
-    two logit rows per query head, and select reads those."""
-    B, Hq, Hkv, d, L, n_q = cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.L, cfg.n_q
-    collected = 4 * B * Hkv * L if scores else 8 * B * Hq * L
-    verify = (4 * B * Hkv * d * (L + n_q)        # K and V of every cached position
-              + 2 * B * n_q * Hq * d             # Q
-              + 4 * B * n_q * Hq * d             # O (fp32)
-              + 4 * B * n_q * Hq                 # lse
-              + collected)                       # two collected logit rows, or partial scores (fp32)
-    n_sets = 1 if cfg.mode == "shared" else Hkv
-    select = collected + 4 * B * n_sets * S_draft + 4 * B * n_sets
-    drafts = []
-    for tl in tail_lens:
-        drafts.append(4 * B * Hkv * d * (S_draft + tl)   # gathered K and V rows, all KV heads
-                      + 4 * B * n_sets * S_draft          # index list
-                      + 2 * B * Hq * d + 4 * B * Hq * d + 4 * B * Hq)
-    return verify, select, drafts
+    """Bytes each call must move at minimum (long_context_self_amd.metrics)."""
+    from long_context_self_amd import metrics
+    return (metrics.verify_bytes(cfg, scores), metrics.select_bytes(cfg, S_draft, scores),
+            [metrics.draft_bytes(cfg, S_draft, tl) for tl in tail_lens])
 
 
 def traffic_record(per_launch_bytes):

@@ -4,6 +4,7 @@
     python -m long_context_self_amd.experiments overlap --config llama8b_32k
     python -m long_context_self_amd.experiments row-scaling --config llama8b_32k
     python -m long_context_self_amd.experiments block-merge --config nsa_16k
+    python -m long_context_self_amd.experiments latency --config llama8b_32k
 
 collect-overhead: verify latency against the number of collected logit rows (none,
 one, the two boundary rows, half, all n_q).  The Vegas page (Figure 6 and its text)
@@ -23,6 +24,9 @@ many drafts, SSV page), on the workload's shapes.
 
 block-merge: SSV block mode (section 4.2 of the SSV page): the tree's rows in one call,
 which loads the union of their block sets once, against each row alone.
+
+latency: p10 / p50 / p90 of every call over 100 calls, each after a 512 MiB cache
+flush, with GB/s against the 8 TB/s peak and against a measured device copy.
 
 Host orchestration only: every step runs in the library's kernels.  Inputs are the
 seeded synthetic workloads of `synth`; the numbers are properties of those inputs,
@@ -191,6 +195,97 @@ def block_merge(cfg, replicas: int, iters: int, seed: int = 0) -> dict:
     return {"config": cfg.name, "replicas": replicas, "iters": iters, "points": res}
 
 
+def latency(cfg, calls: int = 100, warmup: int = 10, flush_mib: int = 512, seed: int = 0,
+            flush: str = "read") -> dict:
+    """p10 / p50 / p90 latency of each call under a cold-cache protocol: before every
+    timed call a 512 MiB scratch buffer passes through the caches (outside the timed
+    events), which evicts the 256 MB Infinity Cache and the L2s.  flush "read" reads a
+    clean buffer; "write" writes it, which leaves the caches full of dirty lines that
+    the timed call then pays to write back.  GB/s is the call's algorithmic bytes over
+    its p50, against the 8 TB/s peak and against a measured device copy."""
+    import torch
+
+    from . import lcs, metrics, synth
+    kv, layers, q, pl = _dev_inputs(torch, cfg, seed, 1)
+    layer = layers[0]
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    qd = bf16(synth.make_queries(cfg, kv, 1, seed=seed, tag=100))
+    B, Hq, L, d = cfg.B, cfg.Hq, cfg.L, cfg.d
+    scale = 1.0 / math.sqrt(d)
+    n_sets = 1 if cfg.mode == "shared" else cfg.Hkv
+    S = cfg.n_sink + cfg.top_k + cfg.n_recent
+    tail = cfg.n_q + 1
+    out = torch.empty((B, cfg.n_q, Hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, cfg.n_q, Hq), dtype=torch.float32, device="cuda")
+    lg = torch.empty((B, Hq, 2, L), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, n_sets, S), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, n_sets), dtype=torch.int32, device="cuda")
+    dout = torch.empty((B, 1, Hq, d), dtype=torch.float32, device="cuda")
+    tl = torch.full((B,), tail, dtype=torch.int32, device="cuda")
+    ws_v = torch.empty(lcs.verify_workspace_bytes(layer, B, cfg.n_q, Hq, L), dtype=torch.uint8, device="cuda")
+    ws_s = torch.empty(lcs.select_workspace_bytes(B, Hq, cfg.Hkv, cfg.mode, L), dtype=torch.uint8, device="cuda")
+    ws_d = torch.empty(lcs.sparse_workspace_bytes(layer, B, 1, Hq, cfg.mode, S, tail), dtype=torch.uint8,
+                       device="cuda")
+    calls_fn = {
+        "verify": lambda: lcs.verify_attn(layer, q, pl, L, scale, cfg.collect_rows, out=out, logits=lg, lse=lse,
+                                          workspace=ws_v),
+        "select": lambda: lcs.select_topk(lg, pl, L, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
+                                          indices=idx, counts=cnt, workspace=ws_s),
+        "draft_step": lambda: lcs.sparse_draft_attn(layer, qd, cfg.mode, idx, cnt, pl, tl, tail, scale, out=dout,
+                                                    workspace=ws_d),
+    }
+    scratch = torch.ones(flush_mib << 17, dtype=torch.int64, device="cuda")
+    sink = torch.empty((), dtype=torch.int64, device="cuda")
+
+    def do_flush(c):
+        if flush == "write":
+            scratch.fill_(c)
+        else:
+            torch.sum(scratch, dim=0, out=sink)
+    for c in range(3):          # the buffer's own first writes leave the caches first
+        do_flush(c)
+    # measured streaming bandwidth: a device copy of 1 GiB (read + write)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    res = {}
+    for name, fn in calls_fn.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = []
+        for c in range(calls):
+            do_flush(c)
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            z.record()
+            ev.append((a, z))
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(z) * 1e3 for a, z in ev])
+        p10, p50, p90 = (float(np.percentile(us, x)) for x in (10, 50, 90))
+        nbytes = {"verify": metrics.verify_bytes(cfg), "select": metrics.select_bytes(cfg, S),
+                  "draft_step": metrics.draft_bytes(cfg, S, tail)}[name]
+        gbs = nbytes / (p50 * 1e3)
+        res[name] = {"p10_us": round(p10, 2), "p50_us": round(p50, 2), "p90_us": round(p90, 2), "bytes": nbytes,
+                     "GB/s_p50": round(gbs, 1), "frac_8TBps": round(gbs / metrics.HBM_PEAK_GBS, 4),
+                     "frac_copy": round(gbs / copy_gbs, 4)}
+    return {"config": cfg.name, "calls": calls, "warmup": warmup, "flush_MiB": flush_mib, "flush": flush,
+            "copy_GBps": round(copy_gbs, 1), "calls_us": res}
+
+
 def _topk_part(idx, cnt, b, s, L, cfg):
     sel = idx[b, s, :int(cnt[b, s])]
     return sel[(sel >= cfg.n_sink) & (sel < L - cfg.n_recent)]
@@ -248,11 +343,12 @@ def overlap(cfg, seed: int = 0) -> dict:
 
 def main(argv=None) -> None:
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    p.add_argument("what", choices=["collect-overhead", "overlap", "row-scaling", "block-merge"])
+    p.add_argument("what", choices=["collect-overhead", "overlap", "row-scaling", "block-merge", "latency"])
     p.add_argument("--config", default="llama8b_32k")
     p.add_argument("--replicas", type=int, default=0, help="KV copies rotated per timed call (0: sized to ~2 GB)")
     p.add_argument("--iters", type=int, default=5)
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--flush", choices=["read", "write"], default="read", help="latency: how the caches are flushed")
     a = p.parse_args(argv)
     from . import synth
     cfg = synth.CONFIGS[a.config]
@@ -264,6 +360,8 @@ def main(argv=None) -> None:
         res = row_scaling(cfg, reps, a.iters, seed=a.seed)
     elif a.what == "block-merge":
         res = block_merge(cfg, reps, a.iters, seed=a.seed)
+    elif a.what == "latency":
+        res = latency(cfg, seed=a.seed, flush=a.flush)
     else:
         res = overlap(cfg, a.seed)
     print(json.dumps(res), flush=True)
