@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--oracle-timing", action="store_true",
+                   help="only time the fp64 oracle per call on every workload (host cores, no GPU)")
     p.add_argument("--scores", action="store_true",
                    help="verify writes per-KV-head partial scores and select reads them, instead of the "
                         "two collected logit rows")
@@ -112,8 +114,68 @@ def cpu_baseline(cfg, kv, q, qd, idx, budget_s):
                       f"verify + shared select + {cfg.n_draft} draft steps, fp64 NumPy, {dt:.1f} s"}
 
 
+def oracle_timing():
+    """The fp64 oracle timed per call on every workload (host cores only, no GPU): one
+    (sequence, KV head) sample of each call, scaled to the whole call."""
+    from long_context_self_amd import synth
+    from oracle import attention as oa
+    from oracle import select as osel
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    res = {}
+    for name in ("tiny", "llama8b_32k", "qwen14b_64k", "nsa_16k", "stress_128k"):
+        cfg = synth.CONFIGS[name].with_(B=1)            # one sequence of the workload
+        full = synth.CONFIGS[name]
+        kv = synth.make_paged_kv(cfg, seed=0)
+        q = synth.make_queries(cfg, kv, cfg.n_q, seed=0)[:, :, :cfg.G]
+        k1, v1 = kv.k[:, :1], kv.v[:, :1]                # one KV head
+        scale = 1.0 / math.sqrt(cfg.d)
+        pairs = full.B * full.Hkv
+        rec = {}
+        if cfg.mode == "block":
+            nblk = cfg.L // cfg.page_size
+            sets = synth.make_block_sets(cfg, nblk, seed=0)[:, :, :1]
+            cnt = np.full((1, cfg.n_q, 1), cfg.blocks_per_row, dtype=np.int32)
+            tm = synth.tree_tail_masks(cfg.n_q, cfg.tree_branches)[None]
+            t0 = time.perf_counter()
+            oa.sparse_attn(q, k1, v1, kv.block_table, cfg.page_size, "block", sets, cnt, kv.prefix_len,
+                           np.full(1, cfg.n_q, np.int32), scale, tail_mask=tm)
+            rec["block_sparse_s"] = round((time.perf_counter() - t0) * pairs, 4)
+        else:
+            t0 = time.perf_counter()
+            _, lg, _ = oa.verify_attn(q, k1, v1, kv.block_table, kv.prefix_len, cfg.page_size, scale)
+            rec["verify_s"] = round((time.perf_counter() - t0) * pairs, 4)
+            heads = full.Hq if full.mode == "shared" else cfg.G
+            lg_full = np.repeat(lg, heads // cfg.G, axis=1)  # stand-in rows for the set's other heads
+            t0 = time.perf_counter()
+            sel = osel.select(lg_full, kv.prefix_len, 1, "shared", cfg.top_k, cfg.n_sink, cfg.n_recent)
+            n_sets = 1 if full.mode == "shared" else full.Hkv
+            rec["select_s"] = round((time.perf_counter() - t0) * full.B * n_sets, 4)
+            i_, c_ = osel.pack(sel, max(a.size for r in sel for a in r))
+            qd = synth.make_queries(cfg, kv, 1, seed=0, tag=100)[:, :, :cfg.G]
+            t0 = time.perf_counter()
+            oa.sparse_attn(qd, k1, v1, kv.block_table, cfg.page_size, "shared", i_, c_, kv.prefix_len,
+                           np.full(1, cfg.n_q + 1, np.int32), scale)
+            rec["draft_step_s"] = round((time.perf_counter() - t0) * pairs, 4)
+            rec["iteration_s"] = round(rec["verify_s"] + rec["select_s"] + full.n_draft * rec["draft_step_s"], 4)
+        n_sets_all = full.B * (1 if full.mode == "shared" else full.Hkv)
+        rec["sample"] = (f"one sequence x one KV head of {name}: attention scaled x{pairs} (sequences x KV "
+                         f"heads), select x{n_sets_all} (sequences x sets)")
+        res[name] = rec
+        print(f"{name}: {rec}", file=sys.stderr, flush=True)
+        del kv
+    print(json.dumps({"oracle_timing": res, "cores": int(threads), "kind": "oracle", "precision": "fp64"}),
+          flush=True)
+
+
 def main():
     args = parse()
+    if args.oracle_timing:
+        oracle_timing()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the multi-GPU "
               "sharding of this path is described in the design notes, not built).", file=sys.stderr)
