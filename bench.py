@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--refresh-every", type=int, default=1,
+                   help="SSV refresh/reuse schedule: select on every R-th layer only; the layers between "
+                        "reuse the nearest preceding refresh layer's sets")
     p.add_argument("--oracle-timing", action="store_true",
                    help="only time the fp64 oracle per call on every workload (host cores, no GPU)")
     p.add_argument("--scores", action="store_true",
@@ -239,8 +242,12 @@ def main():
             lcs.select_topk(logits[r], pl, L, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
                             indices=idx[r], counts=cnt[r], workspace=ws_s)
 
+    RF = max(1, args.refresh_every)
+    refresh = [r for r in range(R) if r % RF == 0]       # layers that derive their own sets
+
     def draft(r, j):
-        lcs.sparse_draft_attn(layers[r], qds[j], cfg.mode, idx[r], cnt[r], pl, tls[j], max_tl, scale,
+        rs = r - r % RF                                  # reuse layers take the refresh layer's sets
+        lcs.sparse_draft_attn(layers[r], qds[j], cfg.mode, idx[rs], cnt[rs], pl, tls[j], max_tl, scale,
                               out=dout, lse=dlse, workspace=ws_d)
 
     if args.copy_calibration_mib > 0:
@@ -269,7 +276,7 @@ def main():
         for r in range(R):
             verify(r)
         e2 = E(); e2.record(); ev.append(("verify", e2))
-        for r in range(R):
+        for r in refresh:
             select(r)
         e3 = E(); e3.record(); ev.append(("select", e3))
         return ev
@@ -290,12 +297,12 @@ def main():
     n_draft_calls = args.steps * cfg.n_draft * R
     t_draft_us = phase_ms["draft"] * 1e3 / n_draft_calls
     t_verify_us = phase_ms["verify"] * 1e3 / (args.steps * R)
-    t_select_us = phase_ms["select"] * 1e3 / (args.steps * R)
+    t_select_us = phase_ms["select"] * 1e3 / (args.steps * len(refresh))
 
     s_count = int(cnt[0].min().item())
     tail_lens = [cfg.n_q + j + 1 for j in range(cfg.n_draft)]
     vb, sb, db = algorithmic_bytes(cfg, s_count, tail_lens, scores=args.scores)
-    step_bytes = R * (vb + sb + sum(db))
+    step_bytes = R * (vb + sum(db)) + len(refresh) * sb
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     v_gbs = vb / (t_verify_us * 1e-6) / 1e9
     s_gbs = sb / (t_select_us * 1e-6) / 1e9
@@ -320,6 +327,7 @@ def main():
                    "page_size": cfg.page_size, "n_q": cfg.n_q, "n_draft": cfg.n_draft,
                    "select": f"{cfg.mode} top-{cfg.top_k}+{cfg.n_sink} sink+{cfg.n_recent} recent",
                    "collected": "per-KV-head partial scores" if args.scores else "two logit rows",
+                   "refresh_every": RF,
                    "layers": R},
         "kernels": {
             "verify": {"us": round(t_verify_us, 2), "bytes": vb, "GB/s": round(v_gbs, 1),
