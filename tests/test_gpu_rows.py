@@ -95,6 +95,20 @@ def test_select_logit_sum_n_rows_bit_exact(mode):
             assert np.array_equal(gi[b, s, :r.size], r), f"{mode} b{b} s{s}"
 
 
+@pytest.mark.parametrize("row", [0, 8])
+def test_select_single_row_bit_exact(row):
+    """One collected row: the head sum of that row's logits, bit-exact."""
+    cfg = synth.CONFIGS["llama8b_32k"].with_(L=5000, B=1, top_k=500)
+    torch, lcs, kv, q, dkv, dq, pl = setup(cfg, 14)
+    _, lg, _ = lcs.verify_attn_rows(dkv, dq, pl, cfg.L, scale_for(cfg.d), [row])
+    idx, cnt = lcs.select_topk_rows(lg, pl, cfg.L, cfg.Hkv, "shared", cfg.top_k, cfg.n_sink, cfg.n_recent)
+    torch.cuda.synchronize()
+    ref = osel.select(lg.cpu().numpy(), kv.prefix_len, cfg.Hkv, "shared", cfg.top_k, cfg.n_sink, cfg.n_recent,
+                      precision="f32")[0][0]
+    assert cnt.cpu().numpy()[0, 0] == ref.size
+    assert np.array_equal(idx.cpu().numpy()[0, 0, :ref.size], ref)
+
+
 def test_select_rows_two_equals_select_topk():
     cfg = synth.CONFIGS["llama8b_32k"].with_(L=5000, B=1, top_k=600)
     torch, lcs, kv, q, dkv, dq, pl = setup(cfg, 9)
