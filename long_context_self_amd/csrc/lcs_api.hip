@@ -149,6 +149,7 @@ lcs_status verify_checks(const lcs_paged_kv* kv, int32_t B, int32_t n_q, int32_t
   if (B < 0) return fail(LCS_E_SHAPE, "B must be >= 0");
   if (n_q < 1) return fail(LCS_E_SHAPE, "n_q must be >= 1");
   if (n_q > 64) return fail(LCS_E_UNSUPPORTED, "n_q %d > 64 verifier rows", n_q);
+  if (Hq / kv->Hkv > 64) return fail(LCS_E_UNSUPPORTED, "Hq / Hkv = %d > 64 query heads per KV head", Hq / kv->Hkv);
   if (max_prefix_len < 0) return fail(LCS_E_SHAPE, "max_prefix_len must be >= 0");
   return LCS_OK;
 }

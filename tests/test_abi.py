@@ -57,6 +57,7 @@ def test_verify_host_errors():
     assert verify(lcs, L, kv, Hq=3) == lcs.LCS_E_SHAPE
     assert verify(lcs, L, kv, n_q=65) == lcs.LCS_E_UNSUPPORTED
     assert verify(lcs, L, kv, n_q=0) == lcs.LCS_E_SHAPE
+    assert verify(lcs, L, fake_kv(lcs, Hkv=1), Hq=65) == lcs.LCS_E_UNSUPPORTED    # G = 65
     assert verify(lcs, L, kv, q=0) == lcs.LCS_E_ARG
     assert verify(lcs, L, kv, q=0x4002) == lcs.LCS_E_ARG          # misaligned
     assert verify(lcs, L, kv, r1=5) == lcs.LCS_E_ARG
