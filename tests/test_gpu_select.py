@@ -153,3 +153,18 @@ def test_full_stress_128k_shape():
         ref = osel.topk_tokens(osel.scores_f32_pinned(lg, b, cfg.L, range(cfg.Hq)), cfg.L,
                                cfg.top_k, cfg.n_sink, cfg.n_recent)
         assert cnt[b, 0] == ref.size and np.array_equal(idx[b, 0, :ref.size], ref)
+
+
+@pytest.mark.parametrize("maxlen", [262144, 262160, 300001])
+def test_sets_at_and_beyond_one_workgroup(maxlen):
+    """Sets of 2^18 items and just above (64 and 65 chunks of 4096 items, a ragged last
+    chunk), with random scores and with every pool item in one first-digit bin (far more
+    candidates than LDS holds), give the CPU rule's result."""
+    rng = np.random.default_rng(9)
+    lens = np.array([maxlen, maxlen - 4097], dtype=np.int32)
+    lg = rng.standard_normal((2, 2, 2, maxlen)).astype(np.float32)
+    idx, cnt = gpu_select(lg, lens, 1, "shared", 9000, 4, 64)
+    assert_exact(idx, cnt, cpu_rule(lg, lens, 1, "shared", 9000, 4, 64))
+    flat = np.full((2, 2, 2, maxlen), -0.5, dtype=np.float32)
+    idx, cnt = gpu_select(flat, lens, 1, "shared", 9000, 4, 64)
+    assert_exact(idx, cnt, cpu_rule(flat, lens, 1, "shared", 9000, 4, 64))

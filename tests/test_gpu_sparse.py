@@ -186,3 +186,33 @@ def test_workspace_garbage_and_reuse(mode, B):
         outs.append(out.cpu().numpy())
     assert np.max(np.abs(outs[0] - o_out)) <= OUT_TOL
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+
+
+@pytest.mark.parametrize("name,L,B,mode", [("llama8b_32k", 6000, 1, "shared"),
+                                           ("qwen14b_64k", 7000, 2, "per_kv_head")])
+def test_any_workspace_contents(name, L, B, mode):
+    """The workspace is scratch: whatever it held before (random bytes, the partials of
+    earlier calls, zeros), every call gives the same bits, and they match the oracle."""
+    torch, lcs = require_gpu()
+    cfg = synth.CONFIGS[name]
+    cfg = cfg.with_(B=B, L=L, top_k=min(cfg.top_k, L // 4))
+    kv = synth.make_paged_kv(cfg, seed=21, lens=[L - 29 * b for b in range(B)])
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=21)
+    idx, cnt = selected(cfg, kv, q, mode)
+    qd = synth.make_queries(cfg, kv, 1, seed=21, tag=100)
+    tl = np.full(B, cfg.n_q + 1, dtype=np.int32)
+    o_out, _ = oa.sparse_attn(qd, kv.k, kv.v, kv.block_table, cfg.page_size, mode, idx, cnt,
+                              kv.prefix_len, tl, scale_for(cfg.d))
+    dkv = kv_dev(kv, torch, lcs)
+    args = (dkv, bf16_dev(qd, torch), mode, i32_dev(idx, torch), i32_dev(cnt, torch),
+            i32_dev(kv.prefix_len, torch), i32_dev(tl, torch), int(tl.max()), scale_for(cfg.d))
+    need = lcs.sparse_workspace_bytes(dkv, B, 1, cfg.Hq, mode, idx.shape[-1], int(tl.max()))
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda", generator=gen)
+    outs = [lcs.sparse_draft_attn(*args, workspace=ws)[0].cpu().numpy() for _ in range(20)]
+    ws.zero_()
+    outs.append(lcs.sparse_draft_attn(*args, workspace=ws)[0].cpu().numpy())
+    outs.append(lcs.sparse_draft_attn(*args)[0].cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    assert np.max(np.abs(outs[0] - o_out)) <= OUT_TOL
