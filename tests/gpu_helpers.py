@@ -41,6 +41,8 @@ def logit_rel_err(g: np.ndarray, o: np.ndarray) -> float:
     """max |g - o| / max(|o|, rms(o over the row)) over the last axis (logit tolerance reading)."""
     o = np.asarray(o, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
+    if o.size == 0:
+        return 0.0       # an empty prefix has no logits to compare
     rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True))
     den = np.maximum(np.abs(o), rms)
     den = np.where(den > 0, den, 1.0)
