@@ -12,7 +12,9 @@
         --out profiles/<kernel>_<workload>_traffic.json
 
 `traffic` scales each counter (KiB per dispatch) by what the same counter reads for a
-plain device-to-device copy of known size in the same run (the runtime's copy kernel),
+plain device-to-device copy of known size in the same run (the runtime's copy kernel;
+the last dispatch of it at least a quarter the size of the largest, since the per-layer
+KV replicas made before the calibration copy are copies too),
 and sums the named kernels' dispatches into HBM bytes per call.  The JSON carries a
 hash of the kernel sources so that a later source change makes it stale.  Inputs are
 either rocprofv3's CSV files or its default SQLite database (`*_results.db`).
@@ -89,7 +91,7 @@ def per_kernel(path: str, counter: str):
     """kernel name -> list of counter values (KiB), one per dispatch."""
     vals = defaultdict(list)
     if path.endswith(".db"):
-        q = "select kernel_name, value from counters_collection where counter_name = ?"
+        q = "select kernel_name, value from counters_collection where counter_name = ? order by dispatch_id"
         for name, v in sqlite3.connect(path).execute(q, (counter,)):
             vals[short_name(name)].append(float(v))
         return vals
@@ -109,7 +111,9 @@ def traffic(args) -> None:
         copies = vals.get(COPY_KERNEL, [])
         if not copies:
             sys.exit(f"no {COPY_KERNEL} dispatch with {counter} in {path}")
-        copy_kib = max(copies)
+        # bench.py makes its calibration copy after the per-layer KV replicas (also copies,
+        # and larger than it at 128K x 8), so it is the last large copy dispatch
+        copy_kib = [c for c in copies if c >= 0.25 * max(copies)][-1]
         factor = (args.copy_bytes / 1024.0) / copy_kib
         res[f"{counter}_copy_kib"] = copy_kib
         res[f"{counter}_factor"] = round(factor, 5)
