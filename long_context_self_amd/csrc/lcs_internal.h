@@ -119,14 +119,13 @@ struct SelArgs {
   uint32_t* cand_count;  // [NS]
   uint64_t* cand;        // [NS][item_cap]
   uint32_t* chunk_above; // [NS][n_chunks]
-  uint32_t* chunk_off;   // [NS][n_chunks]
   uint64_t* thr;         // [NS][2]
   int32_t item_cap, n_chunks, n_pos_chunks;
 };
 
 struct SelPlan {
   int32_t n_sets, item_cap, n_chunks, n_pos_chunks;
-  size_t keys_bytes, hist_bytes, cc_bytes, cand_bytes, ca_bytes, co_bytes, thr_bytes, total_bytes;
+  size_t keys_bytes, hist_bytes, cc_bytes, cand_bytes, ca_bytes, thr_bytes, total_bytes;
 };
 
 SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t max_len,

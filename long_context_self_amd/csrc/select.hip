@@ -23,12 +23,12 @@
 //    it per 4096-item chunk and appends the bin's items as 44-bit composites
 //    (20 low key bits, then the complemented index) to a candidate list; each
 //    thread owns 16 consecutive items, and one scan places a workgroup's appends.
-//  * finalize_kernel (one workgroup per set) loads the candidates into LDS and
+//  * finish_kernel (one workgroup per chunk) loads the candidates into LDS and
 //    radix-selects the exact boundary composite in up to four 11-bit passes,
-//    stopping once the chosen digit holds a single candidate; it then turns the
-//    per-chunk counts into output offsets.
-//  * emit_kernel rescans each chunk and writes the kept items in ascending order
-//    with a workgroup prefix sum.
+//    stopping once the chosen digit holds a single candidate.  Every chunk does this
+//    itself, which costs less than a separate launch.  It then derives its output
+//    offset from the earlier chunks' counts and candidates, and writes its kept
+//    items in ascending order with a workgroup prefix sum.
 //  With logit sums no transcendental function and no multiply is involved, so the
 //  result is bit-identical to the same rule evaluated on the CPU in the same order;
 //  softmax weights go through expf and match the CPU rule to within its rounding.
@@ -314,154 +314,137 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
     }
 }
 
-constexpr int kFinLDS = 8192;   // candidates the finalize pass holds in LDS
+constexpr int kFinLDS = 8192;      // candidates a workgroup holds in LDS
+constexpr int kFinIPT = kItemChunk / 1024;   // consecutive items per thread in finish
 
-__global__ void __launch_bounds__(1024) finalize_kernel(SelArgs a) {
-  const int set = blockIdx.x;
-  const int b = set / a.n_sets;
-  const Win w = window(a, b);
-  if (w.all || a.top_k == 0) return;
-  const int tid = threadIdx.x;
-  __shared__ uint64_t lc[kFinLDS];
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t cc[kMaxItemChunks];
-  __shared__ uint32_t s_wave[16];
-  __shared__ uint64_t sh_prefix, sh_one;
-  __shared__ uint32_t sh_rem, sh_cnt;
-  const uint32_t above = (uint32_t)a.thr[(size_t)set * 2 + 1];
-  const int n_c = min((int)a.cand_count[set], a.item_cap);
-  const uint64_t* gcand = a.cand + (size_t)set * a.item_cap;
-  const bool in_lds = n_c <= kFinLDS;
-  if (in_lds)
-    for (int e = tid; e < n_c; e += 1024) lc[e] = gcand[e];
-  const uint64_t* cand = in_lds ? lc : gcand;
-  if (tid == 0) {
-    sh_prefix = 0;
-    sh_rem = (uint32_t)a.top_k - above;
-  }
-  __syncthreads();
-  // the sh_rem-th largest candidate composite, 11 bits per pass; stop as soon as the
-  // chosen digit holds a single candidate
-  uint64_t mask = 0;
-  int pass = 0;
-  for (; pass < 4; ++pass) {
-    const int shift = 33 - 11 * pass;
-    hist[tid] = 0;
-    hist[tid + 1024] = 0;
-    __syncthreads();
-    const uint64_t prefix = sh_prefix;
-    const uint32_t rem = sh_rem;
-    for (int e = tid; e < n_c; e += 1024) {
-      const uint64_t c = cand[e];
-      if ((c & mask) == prefix) atomicAdd(&hist[(c >> shift) & 2047u], 1u);
-    }
-    __syncthreads();
-    // the digit holding the rem-th largest remaining composite (suffix sums over bins)
-    const uint32_t hl = hist[2 * tid], hh = hist[2 * tid + 1];
-    const uint32_t c = hl + hh;
-    uint32_t total;
-    const uint32_t excl = block_excl_scan<1024>(c, s_wave, total);
-    const uint32_t above_t = total - excl - c;
-    if (above_t < rem && above_t + c >= rem) {
-      if (above_t + hh >= rem) {
-        sh_prefix = prefix | ((uint64_t)(2 * tid + 1) << shift);
-        sh_rem = rem - above_t;
-        sh_cnt = hh;
-      } else {
-        sh_prefix = prefix | ((uint64_t)(2 * tid) << shift);
-        sh_rem = rem - above_t - hh;
-        sh_cnt = hl;
-      }
-    }
-    mask |= (uint64_t)2047u << shift;
-    __syncthreads();
-    if (sh_cnt == 1) break;
-  }
-  uint64_t cstar = sh_prefix;
-  if (pass < 3) {                 // one candidate carries the chosen prefix: it is the answer
-    const uint64_t prefix = sh_prefix;
-    for (int e = tid; e < n_c; e += 1024) {
-      const uint64_t c = cand[e];
-      if ((c & mask) == prefix) sh_one = c;
-    }
-    __syncthreads();
-    cstar = sh_one;
-  }
-  // per-chunk kept counts -> exclusive offsets after the sink window
-  for (int c = tid; c < a.n_chunks; c += 1024) cc[c] = a.chunk_above[(size_t)set * a.n_chunks + c];
-  __syncthreads();
-  for (int e = tid; e < n_c; e += 1024) {
-    const uint64_t c = cand[e];
-    if (c >= cstar) {
-      const int item = (int)(kItemMask - (uint32_t)(c & kItemMask));
-      atomicAdd(&cc[item / kItemChunk], 1u);
-    }
-  }
-  __syncthreads();
-  constexpr int per = kMaxItemChunks / 1024;
-  uint32_t loc[per];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int e = 0; e < per; ++e) {
-    const int c = per * tid + e;
-    loc[e] = (c < a.n_chunks) ? cc[c] : 0u;
-    sum += loc[e];
-  }
-  uint32_t total;
-  uint32_t run = (uint32_t)w.lo + block_excl_scan<1024>(sum, s_wave, total);
-  uint32_t* off = a.chunk_off + (size_t)set * a.n_chunks;
-#pragma unroll
-  for (int e = 0; e < per; ++e) {
-    const int c = per * tid + e;
-    if (c < a.n_chunks) off[c] = run;
-    run += loc[e];
-  }
-  if (tid == 0) a.thr[(size_t)set * 2 + 1] = cstar;
-}
-
-__global__ void __launch_bounds__(256) emit_kernel(SelArgs a) {
+// Boundary and output of one 4096-item chunk (one workgroup per chunk and set).  Every
+// chunk's workgroup finds the exact boundary composite itself: the radix passes over
+// the first-digit bin's candidates cost less than one more launch.  It then places its
+// kept items after the sink window, the kept items of the chunks before it (their items
+// above the bin, counted by collect, and their candidates at or above the boundary) and
+// the kept items before it in this chunk.
+__global__ void __launch_bounds__(1024) finish_kernel(SelArgs a) {
   const int set = blockIdx.y;
   const int b = set / a.n_sets;
   const Win w = window(a, b);
   const int tid = threadIdx.x;
-  const int i0 = blockIdx.x * kItemChunk;
+  const int c0 = blockIdx.x * kItemChunk;          // first item of this chunk
   int32_t* out = a.indices + (size_t)set * a.cap;
   if (w.all) {
-    for (int it = i0 + tid; it < min(w.n, i0 + kItemChunk); it += 256)
+    for (int it = c0 + tid; it < min(w.n, c0 + kItemChunk); it += 1024)
       if (it < a.cap) out[it] = it;
     if (blockIdx.x == 0 && tid == 0) a.counts[set] = min(w.n, a.cap);
     return;
   }
   const int K = a.top_k;
-  const int bin = (K > 0) ? (int)a.thr[(size_t)set * 2 + 0] : 0;
-  const uint64_t cstar = (K > 0) ? a.thr[(size_t)set * 2 + 1] : ~0ull;
-  const uint32_t* keys = a.keys + (size_t)set * a.item_cap;
-  __shared__ uint32_t s_wave[4];
-  constexpr int IPT = kIPT;                   // items per thread, consecutive
-  uint32_t flags = 0;
-  uint32_t cnt = 0;
-  const int t0 = i0 + IPT * tid;
-  if (K > 0 && t0 < w.hi && t0 + IPT > w.lo) {
-    uint32_t k[kIPT];
-    load16(keys, t0, k);
+  __shared__ uint64_t lc[kFinLDS];
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t s_wave[16];
+  __shared__ uint64_t sh_prefix, sh_one;
+  __shared__ uint32_t sh_rem, sh_cnt;
+  // this thread's kFinIPT consecutive items (t0 is a multiple of 4 below item_cap, a
+  // multiple of 16, so the 16-byte load stays inside the set's keys); they do not depend
+  // on the boundary, so they are loaded first
+  const int t0 = c0 + kFinIPT * tid;
+  uint4 kq = make_uint4(0u, 0u, 0u, 0u);
+  if (K > 0 && t0 < w.hi && t0 + kFinIPT > w.lo)
+    kq = *reinterpret_cast<const uint4*>(a.keys + (size_t)set * a.item_cap + t0);
+  int bin = 0;
+  uint64_t cstar = ~0ull;
+  uint32_t base = (uint32_t)w.lo;
+  if (K > 0) {
+    bin = (int)a.thr[(size_t)set * 2 + 0];
+    const uint32_t above = (uint32_t)a.thr[(size_t)set * 2 + 1];
+    const int n_c = min((int)a.cand_count[set], a.item_cap);
+    const uint64_t* gcand = a.cand + (size_t)set * a.item_cap;
+    const bool in_lds = n_c <= kFinLDS;
+    if (in_lds)
+      for (int e = tid; e < n_c; e += 1024) lc[e] = gcand[e];
+    const uint64_t* cand = in_lds ? lc : gcand;
+    if (tid == 0) {
+      sh_prefix = 0;
+      sh_rem = (uint32_t)K - above;
+    }
+    __syncthreads();
+    // the sh_rem-th largest candidate composite, 11 bits per pass; stop as soon as the
+    // chosen digit holds a single candidate
+    uint64_t mask = 0;
+    int pass = 0;
+    for (; pass < 4; ++pass) {
+      const int shift = 33 - 11 * pass;
+      hist[tid] = 0;
+      hist[tid + 1024] = 0;
+      __syncthreads();
+      const uint64_t prefix = sh_prefix;
+      const uint32_t rem = sh_rem;
+      for (int e = tid; e < n_c; e += 1024) {
+        const uint64_t cv = cand[e];
+        if ((cv & mask) == prefix) atomicAdd(&hist[(cv >> shift) & 2047u], 1u);
+      }
+      __syncthreads();
+      // the digit holding the rem-th largest remaining composite (suffix sums over bins)
+      const uint32_t hl = hist[2 * tid], hh = hist[2 * tid + 1];
+      const uint32_t c = hl + hh;
+      uint32_t total;
+      const uint32_t excl = block_excl_scan<1024>(c, s_wave, total);
+      const uint32_t above_t = total - excl - c;
+      if (above_t < rem && above_t + c >= rem) {
+        if (above_t + hh >= rem) {
+          sh_prefix = prefix | ((uint64_t)(2 * tid + 1) << shift);
+          sh_rem = rem - above_t;
+          sh_cnt = hh;
+        } else {
+          sh_prefix = prefix | ((uint64_t)(2 * tid) << shift);
+          sh_rem = rem - above_t - hh;
+          sh_cnt = hl;
+        }
+      }
+      mask |= (uint64_t)2047u << shift;
+      __syncthreads();
+      if (sh_cnt == 1) break;
+    }
+    cstar = sh_prefix;
+    if (pass < 3) {                 // one candidate carries the chosen prefix: it is the answer
+      const uint64_t prefix = sh_prefix;
+      for (int e = tid; e < n_c; e += 1024) {
+        const uint64_t cv = cand[e];
+        if ((cv & mask) == prefix) sh_one = cv;
+      }
+      __syncthreads();
+      cstar = sh_one;
+    }
+    // kept items of the chunks before this one
+    uint32_t part = 0;
+    for (int c = tid; c < (int)blockIdx.x; c += 1024) part += a.chunk_above[(size_t)set * a.n_chunks + c];
+    for (int e = tid; e < n_c; e += 1024) {
+      const uint64_t cv = cand[e];
+      const int item = (int)(kItemMask - (uint32_t)(cv & kItemMask));
+      part += (cv >= cstar && item < c0) ? 1u : 0u;
+    }
+    uint32_t before;
+    block_excl_scan<1024>(part, s_wave, before);
+    base += before;
+  }
+  const uint32_t kk[kFinIPT] = {kq.x, kq.y, kq.z, kq.w};
+  uint32_t flags = 0, cnt = 0;
+  if (K > 0) {
 #pragma unroll
-    for (int e = 0; e < IPT; ++e) {
+    for (int e = 0; e < kFinIPT; ++e) {
       const int it = t0 + e;
       if (it < w.lo || it >= w.hi) continue;
-      const int dg = (int)(k[e] >> 20);
-      if (dg > bin || (dg == bin && composite(k[e], it) >= cstar)) {
+      const int dg = (int)(kk[e] >> 20);
+      if (dg > bin || (dg == bin && composite(kk[e], it) >= cstar)) {
         flags |= 1u << e;
         ++cnt;
       }
     }
   }
   uint32_t total;
-  uint32_t pos = ((K > 0) ? a.chunk_off[(size_t)set * a.n_chunks + blockIdx.x] : (uint32_t)w.lo) +
-                 block_excl_scan<256>(cnt, s_wave, total);
+  uint32_t pos = base + block_excl_scan<1024>(cnt, s_wave, total);
 #pragma unroll
-  for (int e = 0; e < IPT; ++e) {
-    const int it = i0 + IPT * tid + e;
-    if (it >= w.n) break;
+  for (int e = 0; e < kFinIPT; ++e) {
+    const int it = t0 + e;
+    if (it >= w.n) continue;
     if (it < w.lo) {
       if (it < a.cap) out[it] = it;
     } else if (it >= w.hi) {
@@ -493,10 +476,9 @@ SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t ma
   p.cc_bytes = align_up(NS * 4, 256);
   p.cand_bytes = align_up(NS * p.item_cap * 8, 256);
   p.ca_bytes = align_up(NS * p.n_chunks * 4, 256);
-  p.co_bytes = align_up(NS * p.n_chunks * 4, 256);
   p.thr_bytes = align_up(NS * 2 * 8, 256);
   p.total_bytes = p.keys_bytes + p.hist_bytes + p.cc_bytes + p.cand_bytes + p.ca_bytes +
-                  p.co_bytes + p.thr_bytes;
+                  p.thr_bytes;
   return p;
 }
 
@@ -507,7 +489,6 @@ hipError_t select_launch(const SelPlan& p, SelArgs a, void* workspace, hipStream
   a.cand_count = reinterpret_cast<uint32_t*>(ws); ws += p.cc_bytes;
   a.cand = reinterpret_cast<uint64_t*>(ws); ws += p.cand_bytes;
   a.chunk_above = reinterpret_cast<uint32_t*>(ws); ws += p.ca_bytes;
-  a.chunk_off = reinterpret_cast<uint32_t*>(ws); ws += p.co_bytes;
   a.thr = reinterpret_cast<uint64_t*>(ws);
   a.n_sets = p.n_sets;
   a.item_cap = p.item_cap;
@@ -527,9 +508,7 @@ hipError_t select_launch(const SelPlan& p, SelArgs a, void* workspace, hipStream
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(collect_kernel, dim3(p.n_chunks, NS), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(finalize_kernel, dim3(NS), dim3(1024), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(emit_kernel, dim3(p.n_chunks, NS), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(finish_kernel, dim3(p.n_chunks, NS), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
