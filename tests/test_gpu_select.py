@@ -168,3 +168,24 @@ def test_sets_at_and_beyond_one_workgroup(maxlen):
     flat = np.full((2, 2, 2, maxlen), -0.5, dtype=np.float32)
     idx, cnt = gpu_select(flat, lens, 1, "shared", 9000, 4, 64)
     assert_exact(idx, cnt, cpu_rule(flat, lens, 1, "shared", 9000, 4, 64))
+
+
+def test_full_llama8b_32k_shape():
+    """The Llama-3-8B-shaped workload at its full size (32K, 32 query heads, top-2048 + 4
+    sink + 64 recent): bit-exact against the pinned-order CPU rule on the GPU's own
+    logits, and at least 99 % overlap with the selection the fp64 oracle makes from its
+    own logits."""
+    cfg = synth.CONFIGS["llama8b_32k"]
+    kv = synth.make_paged_kv(cfg, seed=0)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=0)
+    glog = gpu_logits(cfg, kv, q)
+    idx, cnt = gpu_select(glog, kv.prefix_len, cfg.Hkv, "shared", cfg.top_k, cfg.n_sink, cfg.n_recent)
+    assert_exact(idx, cnt, cpu_rule(glog, kv.prefix_len, cfg.Hkv, "shared", cfg.top_k, cfg.n_sink,
+                                     cfg.n_recent))
+    _, olog, _ = oa.verify_attn(q, kv.k, kv.v, kv.block_table, kv.prefix_len, cfg.page_size,
+                                scale_for(cfg.d))
+    ref = osel.select(olog, kv.prefix_len, cfg.Hkv, "shared", cfg.top_k, cfg.n_sink, cfg.n_recent)[0][0]
+    got = set(idx[0, 0, :cnt[0, 0]].tolist())
+    overlap = len(got & set(ref.tolist())) / ref.size
+    assert cnt[0, 0] == ref.size == cfg.n_sink + cfg.top_k + cfg.n_recent
+    assert overlap >= 0.99, f"overlap {overlap}"
