@@ -92,7 +92,7 @@ def test_ties_and_ragged(mode):
 @pytest.mark.parametrize("mode", ["shared", "per_kv_head", "block"])
 def test_one_bin_holds_every_candidate(mode):
     """All scores equal: the whole pool lands in one first-digit bin, more candidates
-    than the finalize pass holds in LDS, and ties go to the smaller index."""
+    than a workgroup holds in LDS, and ties go to the smaller index."""
     lens = np.array([60000, 33333], dtype=np.int32)
     lg = np.full((2, 4, 2, 60000), 0.75, dtype=np.float32)
     bs = 16 if mode == "block" else 0
