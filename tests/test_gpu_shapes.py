@@ -61,3 +61,33 @@ def test_verify_select_draft(case):
             tl = np.full(c2.B, n_q + j + 1, dtype=np.int32)
             _, _, e = sparse_check(c2, kv, qd, mode, sidx, scnt, kv.prefix_len, tl)
             print(f"{case} {mode} draft {j}: max-abs {e:.2e}")
+
+
+# (page_size, Hq, Hkv, d, n_q, tree branches, blocks per row, shared blocks, prefix lengths)
+BLOCK_CASES = [
+    (32, 4, 2, 64, 4, 2, 3, 1, [1000, 937]),
+    (128, 16, 2, 128, 8, 2, 4, 2, [3000]),
+    (64, 8, 8, 128, 6, 3, 5, 3, [2500, 1999]),
+]
+
+
+@pytest.mark.parametrize("case", BLOCK_CASES, ids=lambda c: f"P{c[0]}-G{c[1] // c[2]}-d{c[3]}-nq{c[4]}")
+def test_block_mode_shapes(case):
+    """SSV block mode beyond the 16K workload's shape: head dim 64, 32- and 128-token
+    blocks, one query head per KV head, and 64 q-rows per KV head (two row chunks),
+    each with a tree over the verifier rows.  Blocks are drawn below the shorter
+    prefix rounded up to a block, so a listed block can end past a prefix."""
+    require_gpu()
+    page, Hq, Hkv, d, n_q, br, kb, core, lens = case
+    cfg = synth.Config("block", B=len(lens), Hq=Hq, Hkv=Hkv, d=d, L=max(lens), page_size=page, n_q=n_q,
+                       n_draft=0, top_k=kb, n_sink=0, n_recent=0, mode="block", crit_frac=0.0,
+                       blocks_per_row=kb, core_blocks=core, tree_branches=br)
+    kv = synth.make_paged_kv(cfg, seed=41, lens=lens)
+    nblk = (min(lens) + page - 1) // page          # every listed block lies below each prefix
+    sets = synth.make_block_sets(cfg, nblk, seed=41)
+    cnt = np.full((cfg.B, n_q, Hkv), kb, dtype=np.int32)
+    q = synth.make_queries(cfg, kv, n_q, seed=41)
+    tm = np.stack([synth.tree_tail_masks(n_q, br)] * cfg.B)
+    tl = np.full(cfg.B, n_q, dtype=np.int32)
+    _, _, e = sparse_check(cfg, kv, q, "block", sets, cnt, kv.prefix_len, tl, tm)
+    print(f"{case}: block mode max-abs {e:.2e}")
