@@ -189,3 +189,16 @@ def test_full_llama8b_32k_shape():
     overlap = len(got & set(ref.tolist())) / ref.size
     assert cnt[0, 0] == ref.size == cfg.n_sink + cfg.top_k + cfg.n_recent
     assert overlap >= 0.99, f"overlap {overlap}"
+
+
+def test_largest_accepted_set():
+    """max_prefix_len = 2^24 - 1, the largest the ABI accepts: item indices fill the 24
+    bits of the composites and the grid spans all 4096 chunks.  Bit-exact against the CPU
+    rule on the same scores."""
+    L = (1 << 24) - 1
+    rng = np.random.default_rng(10)
+    lg = rng.standard_normal((1, 1, 2, L), dtype=np.float32)
+    lens = np.array([L], dtype=np.int32)
+    idx, cnt = gpu_select(lg, lens, 1, "shared", 5000, 4, 64)
+    assert_exact(idx, cnt, cpu_rule(lg, lens, 1, "shared", 5000, 4, 64))
+    assert idx[0, 0, cnt[0, 0] - 1] == L - 1
