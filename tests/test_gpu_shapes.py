@@ -1,10 +1,11 @@
 """GPU parity over the shapes the ABI accepts beyond the five workloads: page sizes below
-the 16-token MFMA tile (1, 2, 4, 8) and above it (128, 256), one query head per KV head
-(G = 1) up to 16, a single verifier row (n_q = 1), head dim 64 in every call, prefixes
-of one token, and row sets split over two 48-row chunks.  Each case runs verify,
-select and single-token draft steps against the fp64 oracle, with the tolerances of
-the other GPU tests (outputs 1e-2 max-abs, logits 1e-3 relative, selection bit-exact
-against the pinned-order CPU rule on the GPU's own logits)."""
+the 16-token MFMA tile (1, 2, 4, 8) and above it (128, 256, and the largest, 1024), one
+query head per KV head (G = 1) up to the largest, 64, a single verifier row (n_q = 1),
+head dim 64 in every call, prefixes of one token, and row sets split over two or three
+48-row chunks.  Each case runs verify, select and single-token draft steps against the
+fp64 oracle, with the tolerances of the other GPU tests (outputs 1e-2 max-abs, logits
+1e-3 relative, selection bit-exact against the pinned-order CPU rule on the GPU's own
+logits)."""
 import numpy as np
 import pytest
 
@@ -27,6 +28,7 @@ CASES = [
     (8, 4, 4, 64, 5, [1000, 999]),
     (128, 16, 2, 128, 1, [700]),
     (256, 4, 2, 64, 2, [1500, 1, 513]),
+    (1024, 64, 1, 64, 2, [3000, 1025]),      # largest page and G the ABI accepts: 3 row chunks
 ]
 
 
