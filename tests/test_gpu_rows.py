@@ -157,3 +157,28 @@ def test_select_softmax_weights_valid(mode, rows):
             assert np.all(sig[pool[kept]] >= kth - eps)
             assert np.all(sig[pool[~kept]] <= kth + eps)
             assert np.isin(r, got).mean() >= 0.99
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_collect_all_64_rows(G):
+    """The most verifier rows a call takes (n_q = 64), every one collected: the row mask
+    uses all 64 bits and slot 63 is the last; logits of every row against the fp64
+    oracle, and outputs equal to those of the two-row call.  G = 4 splits the 256 q-rows
+    of a KV head over six row chunks."""
+    Hkv = 2
+    cfg = synth.Config("rows64", B=2, Hq=G * Hkv, Hkv=Hkv, d=64, L=700, page_size=16, n_q=64, n_draft=0,
+                       top_k=64, n_sink=4, n_recent=16, mode="shared", crit_frac=0.01)
+    torch, lcs, kv, q, dkv, dq, pl = setup(cfg, 9, lens=[700, 333])
+    rows = list(range(64))
+    out, lg, lse = lcs.verify_attn_rows(dkv, dq, pl, 700, scale_for(cfg.d), rows)
+    out2, _, lse2 = lcs.verify_attn(dkv, dq, pl, 700, scale_for(cfg.d), (0, 63))
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    _, o_lg, _ = oa.verify_attn(q, kv.k, kv.v, kv.block_table, kv.prefix_len, cfg.page_size, scale_for(cfg.d),
+                                collect_rows=rows)
+    g = lg.cpu().numpy()
+    assert g.shape[2] == 64
+    for b in range(cfg.B):
+        L = int(kv.prefix_len[b])
+        e = logit_rel_err(g[b, :, :, :L], o_lg[b, :, :, :L])
+        assert e <= LOGIT_TOL, f"b {b}: logit rel err {e}"
