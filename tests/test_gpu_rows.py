@@ -163,8 +163,9 @@ def test_select_softmax_weights_valid(mode, rows):
 def test_collect_all_64_rows(G):
     """The most verifier rows a call takes (n_q = 64), every one collected: the row mask
     uses all 64 bits and slot 63 is the last; logits of every row against the fp64
-    oracle, and outputs equal to those of the two-row call.  G = 4 splits the 256 q-rows
-    of a KV head over six row chunks."""
+    oracle, outputs equal to those of the two-row call, and selection over the 64 rows'
+    summed logits bit-exact against the pinned-order CPU rule.  G = 4 splits the 256
+    q-rows of a KV head over six row chunks."""
     Hkv = 2
     cfg = synth.Config("rows64", B=2, Hq=G * Hkv, Hkv=Hkv, d=64, L=700, page_size=16, n_q=64, n_draft=0,
                        top_k=64, n_sink=4, n_recent=16, mode="shared", crit_frac=0.01)
@@ -182,3 +183,12 @@ def test_collect_all_64_rows(G):
         L = int(kv.prefix_len[b])
         e = logit_rel_err(g[b, :, :, :L], o_lg[b, :, :, :L])
         assert e <= LOGIT_TOL, f"b {b}: logit rel err {e}"
+    # selection over all 64 rows by their summed logits, in the pinned row order
+    for mode in ("shared", "per_kv_head"):
+        idx, cnt = lcs.select_topk_rows(lg, pl, 700, cfg.Hkv, mode, cfg.top_k, cfg.n_sink, cfg.n_recent)
+        torch.cuda.synchronize()
+        ref = osel.select(g, kv.prefix_len, cfg.Hkv, mode, cfg.top_k, cfg.n_sink, cfg.n_recent, precision="f32")
+        gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+        for b in range(cfg.B):
+            for s_, r in enumerate(ref[b]):
+                assert gc[b, s_] == r.size and np.array_equal(gi[b, s_, :r.size], r), f"{mode} b{b} s{s_}"
