@@ -24,5 +24,9 @@ Sparse Speculative Verification for Efficient LLM Inference*.
 
 Pinning status: every public function is pinned by a non-GPU test against
 something other than itself (brute force, a library routine, closed forms,
-invariants or pairwise enumeration); see ``tests/test_oracle_*.py``.
+invariants or pairwise enumeration); see ``tests/test_oracle_*.py``.  That
+includes ``attention.attention_one`` (brute force, a verify row, closed form),
+``attention.sparse_attn`` with a different list per KV head (brute force) and
+``select.select`` in block mode (rank enumeration over each group's block
+maxima).
 """

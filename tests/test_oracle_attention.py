@@ -256,3 +256,78 @@ def test_verify_any_row_set_matches_brute_force():
                     _, _, lg = brute.attend(q[b, r, h], kv.k, kv.v, kv.block_table, b, h // cfg.G,
                                             list(range(L + r + 1)), cfg.page_size, scale)
                     np.testing.assert_allclose(logits[b, h, c, :L], lg[:L], rtol=0, atol=1e-12)
+
+
+def test_attention_one_matches_brute_and_verify_row():
+    """attention_one (the checker of every sampled full-size comparison) against the
+    scalar brute force on the same gathered rows, and against one row of verify_attn:
+    output, weights and lse.  A dropped scale, an unshifted exponent or a wrong lse
+    fails here."""
+    cfg = small_cfg(B=1, n_q=3)
+    kv, q = make(cfg, seed=12)
+    scale = 1.0 / math.sqrt(cfg.d)
+    out, _, lse, W = oa.verify_attn(q, kv.k, kv.v, kv.block_table, kv.prefix_len, cfg.page_size, scale,
+                                    return_weights=True)
+    L = cfg.L
+    for i in range(cfg.n_q):
+        vis = np.arange(L + i + 1)
+        for h in range(cfg.Hq):
+            g = h // cfg.G
+            K = oa.paged_rows(kv.k, kv.block_table, 0, g, vis, cfg.page_size)
+            V = oa.paged_rows(kv.v, kv.block_table, 0, g, vis, cfg.page_size)
+            o, p, l = oa.attention_one(oa.bf16_to_f64(q[0, i, h]), K, V, scale)
+            bo, bl, blg = brute.attend(q[0, i, h], kv.k, kv.v, kv.block_table, 0, g, vis.tolist(),
+                                       cfg.page_size, scale)
+            np.testing.assert_allclose(o, bo, rtol=0, atol=1e-12)
+            assert abs(l - bl) < 1e-12
+            # weights: exp(logit - lse) from the brute-force logits, summing to 1
+            np.testing.assert_allclose(p, np.exp(np.asarray(blg) - bl), rtol=0, atol=1e-12)
+            assert abs(p.sum() - 1.0) < 1e-12
+            # and the same row of the dense verify
+            np.testing.assert_allclose(o, out[0, i, h], rtol=0, atol=1e-12)
+            assert abs(l - lse[0, i, h]) < 1e-12
+            np.testing.assert_allclose(p, W[(0, g)][i, h - g * cfg.G, :L + i + 1], rtol=0, atol=1e-12)
+
+
+def test_attention_one_scale_and_shift():
+    """Closed forms: two keys whose logits differ by s give weights (1, e^-s)/(1 + e^-s);
+    the lse is the larger logit plus log(1 + e^-s), whatever the common offset."""
+    q = np.array([1.0, 0.0])
+    K = np.array([[500.0, 0.0], [496.0, 0.0]])
+    V = np.array([[1.0, 0.0], [0.0, 1.0]])
+    o, p, l = oa.attention_one(q, K, V, 0.5)        # logits 250 and 248
+    w = math.exp(-2.0)
+    np.testing.assert_allclose(p, [1 / (1 + w), w / (1 + w)], rtol=1e-15)
+    np.testing.assert_allclose(o, [1 / (1 + w), w / (1 + w)], rtol=1e-15)
+    assert abs(l - (250.0 + math.log1p(w))) < 1e-12
+
+
+def test_sparse_per_kv_head_distinct_lists_match_brute_force():
+    """Per-KV-head sets with a different list for every KV head: head h must read the
+    list of its own group h // G, not the first group's."""
+    cfg = small_cfg(B=2, Hq=6, Hkv=3, L=40, n_q=2)
+    kv, q = make(cfg, seed=13, lens=[40, 33])
+    scale = 1.0 / math.sqrt(cfg.d)
+    rng = np.random.default_rng(5)
+    cap = 9
+    idx = np.full((cfg.B, cfg.Hkv, cap), -1, dtype=np.int32)
+    cnt = np.zeros((cfg.B, cfg.Hkv), dtype=np.int32)
+    for b in range(cfg.B):
+        L = int(kv.prefix_len[b])
+        for g in range(cfg.Hkv):
+            n = 3 + 2 * g                                       # every group a different size
+            idx[b, g, :n] = np.sort(rng.choice(L, size=n, replace=False))
+            cnt[b, g] = n
+        assert len({tuple(idx[b, g, :cnt[b, g]]) for g in range(cfg.Hkv)}) == cfg.Hkv
+    tl = np.array([2, 1], dtype=np.int32)
+    out, lse = oa.sparse_attn(q, kv.k, kv.v, kv.block_table, cfg.page_size, "per_kv_head", idx, cnt,
+                              kv.prefix_len, tl, scale)
+    for b in range(cfg.B):
+        tb = int(kv.prefix_len[b])
+        for i in range(cfg.n_q):
+            for h in range(cfg.Hq):
+                g = h // cfg.G
+                vis = idx[b, g, :cnt[b, g]].tolist() + [tb + j for j in range(int(tl[b]))]
+                o, l, _ = brute.attend(q[b, i, h], kv.k, kv.v, kv.block_table, b, g, vis, cfg.page_size, scale)
+                np.testing.assert_allclose(out[b, i, h], o, rtol=0, atol=1e-12)
+                assert abs(lse[b, i, h] - l) < 1e-12

@@ -243,3 +243,33 @@ def test_partial_scores_exact_on_small_integers():
         part = osel.partial_scores_f32(lg, b, L, Hq, Hkv)
         want = lg[b].astype(np.int64).reshape(Hkv, Hq // Hkv, 2, L).sum(axis=(1, 2))
         assert np.array_equal(part.astype(np.int64), want)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_select_block_mode_per_group_matches_rank_enumeration(seed):
+    """select(mode='block') end to end: one block set per (sequence, KV head), each scored
+    by the max over its block of the group's own head sum (math.fsum over the G heads'
+    two rows), kept by rank enumeration between the sink and recent windows.  Summing the
+    wrong heads (all heads, or group 0's for every set) fails here."""
+    rng = np.random.default_rng(200 + seed)
+    B, Hq, Hkv, bs = 2, 6, 3, 8
+    G = Hq // Hkv
+    lens = [int(rng.integers(60, 120)), int(rng.integers(60, 120))]
+    ld = max(lens)
+    # small integers: many ties between blocks, and group sums that differ per group
+    lg = rng.integers(-3, 4, size=(B, Hq, 2, ld)).astype(np.float64)
+    k, ns, nr = 3, 5, 11
+    got = osel.select(lg, np.array(lens), Hkv, "block", k, ns, nr, block_size=bs)
+    for b in range(B):
+        L = lens[b]
+        nb = (L + bs - 1) // bs
+        sb = (ns + bs - 1) // bs
+        rb = (L - nr) // bs
+        for g in range(Hkv):
+            sig = [math.fsum(lg[b, h, c, p] for h in range(g * G, (g + 1) * G) for c in range(2))
+                   for p in range(L)]
+            beta = [max(sig[c * bs:min(L, c * bs + bs)]) for c in range(nb)]
+            ref = list(range(sb)) + brute.topk_by_rank(beta, sb, rb, k) + list(range(rb, nb))
+            assert got[b][g].tolist() == sorted(ref), (b, g)
+    # the groups really select differently on these inputs (so the test can tell them apart)
+    assert any(got[b][0].tolist() != got[b][g].tolist() for b in range(B) for g in range(1, Hkv))
