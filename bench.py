@@ -1,7 +1,9 @@
 """Benchmark of the verify / select / sparse-draft attention path on one MI355X.
 
 One step is one speculative decode iteration of the attention hot path of an
-n-layer model (default: the Llama-3-8B-shaped layer at 32K context, 32 layers):
+n-layer model.  The default workload is the largest one-GPU configuration, the
+long-context stress shape (8 sequences of 131072 tokens, 32 query / 8 KV heads,
+head dim 128, draft length 8, shared top-4096 + 4 sink + 64 recent), over 4 layers:
 
     for each of the k draft steps:  sparse_draft_attn on every layer
     for every layer:                verify_attn (k+1 rows, two logit rows collected)
@@ -13,8 +15,10 @@ separated by the other layers' traffic (several GB) and read HBM, not the
 
 Prints one JSON line.  `value` is the achieved algorithmic HBM bandwidth of the
 whole step (bytes the method must move / step time); the per-call latencies in
-microseconds are in `kernels`.  `roofline` is for the dominant kernel (verify).
-`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload.
+microseconds and their fractions of the 8 TB/s peak are in `kernels`.  `roofline`
+is for the call with the largest share of the step's time.  `secondary` repeats the
+per-call measurement on the Llama-3-8B-shaped layer at 32K context (32 layers).
+`cpu_baseline` times the fp64 oracle on a bounded sample of the main workload.
 """
 from __future__ import annotations
 
@@ -31,8 +35,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # the peak line every fraction is taken against (metrics.HBM_PEAK_GBS)
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_llama8b_32k_traffic.json")
-TRAFFIC_WORKLOAD = "llama8b_32k"   # the workload those counter runs measured
+DEFAULT_CONFIG = "stress_128k"
+DEFAULT_LAYERS = {"stress_128k": 4, "qwen14b_64k": 4, "llama8b_32k": 32, "tiny": 4}
+SECONDARY_CONFIG = "llama8b_32k"
+
+
+def traffic_file(workload: str, call: str) -> str:
+    """Committed counter-traffic summary of one call on one workload (rocprofv3 runs)."""
+    return os.path.join(ROOT, "profiles", f"{call}_{workload}_traffic.json")
 
 
 def parse():
@@ -40,8 +50,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", default="llama8b_32k")
-    p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--config", default=DEFAULT_CONFIG)
+    p.add_argument("--layers", type=int, default=0,
+                   help="layers (KV replicas); 0 = the workload's default (4 at 128K x 8, 32 at 32K)")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="skip the secondary per-call measurement on the 32K workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--refresh-every", type=int, default=1,
@@ -64,10 +77,11 @@ def algorithmic_bytes(cfg, S_draft, tail_lens, scores=False):
             [metrics.draft_bytes(cfg, S_draft, tl) for tl in tail_lens])
 
 
-def traffic_record(per_launch_bytes):
-    """HBM bytes per verify launch from committed rocprofv3 counter runs, if they match this source."""
+def traffic_record(workload: str, call: str):
+    """HBM bytes per call from committed rocprofv3 counter runs of this workload, if
+    they were taken on the current kernel source (else None)."""
     try:
-        rec = json.load(open(PROFILE_TRAFFIC))
+        rec = json.load(open(traffic_file(workload, call)))
     except (OSError, ValueError):
         return None
     from long_context_self_amd.profile_summary import kernel_source_hash
@@ -76,9 +90,13 @@ def traffic_record(per_launch_bytes):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, kv, q, qd, idx, budget_s):
-    """fp64 oracle on a bounded sample: one KV head of one layer per round (verify for
-    its G heads, the shared select over all heads' rows, and k draft steps)."""
+def cpu_baseline(cfg, budget_s):
+    """fp64 oracle on a bounded sample of the workload: rounds of one sequence and one KV
+    head of one layer (verify for its G query heads, the set's select, and the k draft
+    steps), on inputs drawn like the workload's.  The select leg needs every query head's
+    two rows for a shared set; the sample has G heads, so their rows stand in for the
+    other groups' (replicated), which costs the same work as the real rows."""
+    from long_context_self_amd import synth
     from oracle import attention as oa
     from oracle import select as osel
     try:
@@ -86,35 +104,39 @@ def cpu_baseline(cfg, kv, q, qd, idx, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    one = cfg.with_(B=1, Hkv=1, Hq=cfg.G)            # one sequence, one KV group
+    kv = synth.make_paged_kv(one, seed=0)
+    q = synth.make_queries(one, kv, one.n_q, seed=0)
+    qd = [synth.make_queries(one, kv, 1, seed=0, tag=100 + j) for j in range(one.n_draft)]
     scale = 1.0 / math.sqrt(cfg.d)
-    G = cfg.G
-    # one KV group: a 1-KV-head view of the cache and G query heads
-    k1 = kv.k[:, :1]
-    v1 = kv.v[:, :1]
-    q1 = q[:, :, :G]
+    n_sets = 1 if cfg.mode == "shared" else cfg.Hkv
+    heads = cfg.Hq if cfg.mode == "shared" else cfg.G
     bytes_done = 0
     rounds = 0
     t0 = time.perf_counter()
     while True:
-        _, lg, _ = oa.verify_attn(q1, k1, v1, kv.block_table, kv.prefix_len, cfg.page_size, scale)
-        full_lg = np.repeat(lg, cfg.Hkv, axis=1)   # stand-in rows for the other heads' scores
-        sel = osel.select(full_lg, kv.prefix_len, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent)
+        _, lg, _ = oa.verify_attn(q, kv.k, kv.v, kv.block_table, kv.prefix_len, one.page_size, scale)
+        full_lg = np.repeat(lg, heads // cfg.G, axis=1)   # stand-in rows for the set's other heads
+        sel = osel.select(full_lg, kv.prefix_len, 1, "shared", cfg.top_k, cfg.n_sink, cfg.n_recent)
         i_, c_ = osel.pack(sel, max(a.size for r in sel for a in r))
         for j in range(cfg.n_draft):
-            tl = np.full(cfg.B, cfg.n_q + j + 1, dtype=np.int32)
-            oa.sparse_attn(qd[j][:, :, :G], k1, v1, kv.block_table, cfg.page_size, cfg.mode,
-                           i_, c_, kv.prefix_len, tl, scale)
+            tl = np.full(1, cfg.n_q + j + 1, dtype=np.int32)
+            oa.sparse_attn(qd[j], kv.k, kv.v, kv.block_table, one.page_size, "shared", i_, c_,
+                           kv.prefix_len, tl, scale)
         S = int(c_[0, 0])
         v_b, s_b, d_b = algorithmic_bytes(cfg, S, [cfg.n_q + j + 1 for j in range(cfg.n_draft)])
-        bytes_done += (v_b + sum(d_b)) / cfg.Hkv + s_b
+        pairs = cfg.B * cfg.Hkv
+        bytes_done += (v_b + sum(d_b)) / pairs + s_b / (cfg.B * n_sets)
         rounds += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": round(bytes_done / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{rounds} rounds of one KV head (G={G} query heads) of one {cfg.name} layer: "
-                      f"verify + shared select + {cfg.n_draft} draft steps, fp64 NumPy, {dt:.1f} s"}
+            "sample": f"{rounds} rounds of one sequence x one KV head (G={cfg.G} query heads) of one "
+                      f"{cfg.name} layer: verify, the set's select (the G heads' logit rows replicated to "
+                      f"stand in for the set's {heads} heads), {cfg.n_draft} draft steps; fp64 NumPy, "
+                      f"{dt:.1f} s; bytes counted as that share of the workload's algorithmic bytes"}
 
 
 def oracle_timing():
@@ -174,24 +196,18 @@ def oracle_timing():
           flush=True)
 
 
-def main():
-    args = parse()
-    if args.oracle_timing:
-        oracle_timing()
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the multi-GPU "
-              "sharding of this path is described in the design notes, not built).", file=sys.stderr)
-        sys.exit(2)
+def measure(cfg, R, steps, warmup, scores=False, refresh_every=1, copy_calibration_mib=0, log=None):
+    """Time `steps` bench steps of workload cfg over R layers on the GPU.  Returns the
+    per-call latencies (us, HIP events on the calling stream), the algorithmic bytes and
+    the step time."""
     import torch
 
     from long_context_self_amd import lcs, synth
 
-    cfg = synth.CONFIGS[args.config]
     assert cfg.mode in ("shared", "per_kv_head"), "bench covers the token-set workloads"
     dev = "cuda"
-    torch.cuda.set_device(0)
     scale = 1.0 / math.sqrt(cfg.d)
+    t_setup = time.perf_counter()
     kv = synth.make_paged_kv(cfg, seed=0)
     q = synth.make_queries(cfg, kv, cfg.n_q, seed=0)
     qd = [synth.make_queries(cfg, kv, 1, seed=0, tag=100 + j) for j in range(cfg.n_draft)]
@@ -201,17 +217,17 @@ def main():
 
     k0, v0 = bf16(kv.k), bf16(kv.v)
     bt = torch.from_numpy(kv.block_table).to(dev)
-    R = args.layers
+    pl = torch.from_numpy(kv.prefix_len).to(dev)
+    del kv
     layers = [lcs.PagedKV(k0 if r == 0 else k0.clone(), v0 if r == 0 else v0.clone(), bt) for r in range(R)]
     qv = bf16(q)
     qds = [bf16(x) for x in qd]
-    pl = torch.from_numpy(kv.prefix_len).to(dev)
     B, Hq, L = cfg.B, cfg.Hq, cfg.L
     n_sets = 1 if cfg.mode == "shared" else cfg.Hkv
     S = cfg.n_sink + cfg.top_k + cfg.n_recent
     outs = torch.empty((B, cfg.n_q, Hq, cfg.d), dtype=torch.float32, device=dev)
     lses = torch.empty((B, cfg.n_q, Hq), dtype=torch.float32, device=dev)
-    if args.scores:
+    if scores:
         logits = [torch.empty((B, cfg.Hkv, L), dtype=torch.float32, device=dev) for _ in range(R)]
     else:
         logits = [torch.empty((B, Hq, 2, L), dtype=torch.float32, device=dev) for _ in range(R)]
@@ -227,7 +243,7 @@ def main():
                        dtype=torch.uint8, device=dev)
 
     def verify(r):
-        if args.scores:
+        if scores:
             lcs.verify_attn_scores(layers[r], qv, pl, L, scale, cfg.collect_rows, out=outs, scores=logits[r],
                                    lse=lses, workspace=ws_v)
         else:
@@ -235,14 +251,14 @@ def main():
                             workspace=ws_v)
 
     def select(r):
-        if args.scores:
+        if scores:
             lcs.select_topk_scores(logits[r], pl, L, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
                                    indices=idx[r], counts=cnt[r], workspace=ws_s, Hq=Hq)
         else:
             lcs.select_topk(logits[r], pl, L, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
                             indices=idx[r], counts=cnt[r], workspace=ws_s)
 
-    RF = max(1, args.refresh_every)
+    RF = max(1, refresh_every)
     refresh = [r for r in range(R) if r % RF == 0]       # layers that derive their own sets
 
     def draft(r, j):
@@ -250,8 +266,8 @@ def main():
         lcs.sparse_draft_attn(layers[r], qds[j], cfg.mode, idx[rs], cnt[rs], pl, tls[j], max_tl, scale,
                               out=dout, lse=dlse, workspace=ws_d)
 
-    if args.copy_calibration_mib > 0:
-        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    if copy_calibration_mib > 0:
+        src = torch.empty(copy_calibration_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
@@ -262,11 +278,14 @@ def main():
         verify(r)
         select(r)
     torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    if log:
+        print(f"{cfg.name}: set up {R} layers in {setup_s:.1f} s", file=log, flush=True)
 
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     phase_ms = {"draft": 0.0, "verify": 0.0, "select": 0.0}
 
-    def step(timed):
+    def step():
         ev = []
         e0 = E(); e0.record(); ev.append(("start", e0))
         for j in range(cfg.n_draft):
@@ -281,35 +300,81 @@ def main():
         e3 = E(); e3.record(); ev.append(("select", e3))
         return ev
 
-    for _ in range(args.warmup):
-        step(False)
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
     events = []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        events.append(step(True))
+    for _ in range(steps):
+        events.append(step())
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for ev in events:
         for (_, a), (name, b) in zip(ev[:-1], ev[1:]):
             phase_ms[name] += a.elapsed_time(b)
-    ms_per_step = wall * 1e3 / args.steps
-    n_draft_calls = args.steps * cfg.n_draft * R
-    t_draft_us = phase_ms["draft"] * 1e3 / n_draft_calls
-    t_verify_us = phase_ms["verify"] * 1e3 / (args.steps * R)
-    t_select_us = phase_ms["select"] * 1e3 / (args.steps * len(refresh))
-
+    ms_per_step = wall * 1e3 / steps
+    t_draft_us = phase_ms["draft"] * 1e3 / (steps * cfg.n_draft * R)
+    t_verify_us = phase_ms["verify"] * 1e3 / (steps * R)
+    t_select_us = phase_ms["select"] * 1e3 / (steps * len(refresh))
     s_count = int(cnt[0].min().item())
     tail_lens = [cfg.n_q + j + 1 for j in range(cfg.n_draft)]
-    vb, sb, db = algorithmic_bytes(cfg, s_count, tail_lens, scores=args.scores)
+    vb, sb, db = algorithmic_bytes(cfg, s_count, tail_lens, scores=scores)
     step_bytes = R * (vb + sum(db)) + len(refresh) * sb
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    v_gbs = vb / (t_verify_us * 1e-6) / 1e9
-    s_gbs = sb / (t_select_us * 1e-6) / 1e9
-    d_gbs = (sum(db) / len(db)) / (t_draft_us * 1e-6) / 1e9
-    flops_verify = 4 * B * Hq * cfg.n_q * (L + cfg.n_q) * cfg.d
-    gamma_attn = t_draft_us / t_verify_us
+    del layers, k0, v0
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms_per_step, "step_bytes": step_bytes, "us": {"verify": t_verify_us,
+            "select": t_select_us, "draft_step": t_draft_us},
+            "bytes": {"verify": vb, "select": sb, "draft_step": int(sum(db) / len(db))},
+            "share": {"verify": phase_ms["verify"], "select": phase_ms["select"], "draft": phase_ms["draft"]},
+            "selected": s_count, "R": R, "refresh": len(refresh), "RF": RF, "setup_s": setup_s}
 
+
+def kernel_table(cfg, m):
+    """Per-call latency, algorithmic bytes and fraction of the 8 TB/s peak."""
+    res = {}
+    for name in ("verify", "select", "draft_step"):
+        us, by = m["us"][name], m["bytes"][name]
+        gbs = by / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 2), "bytes": by, "GB/s": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    flops_verify = 4 * cfg.B * cfg.Hq * cfg.n_q * (cfg.L + cfg.n_q) * cfg.d
+    res["verify"]["TFLOP/s"] = round(flops_verify / (m["us"]["verify"] * 1e-6) / 1e12, 2)
+    res["draft_step"]["selected"] = m["selected"]
+    return res
+
+
+# the kernels behind each call, as rocprofv3 names them
+CALL_KERNELS = {"verify": "attn_kernel (dense verify) + combine_kernel",
+                "select": "zero_kernel + score_kernel + collect_kernel + finish_kernel",
+                "draft_step": "attn_kernel (shared token list) + combine_kernel"}
+
+
+def main():
+    args = parse()
+    if args.oracle_timing:
+        oracle_timing()
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the multi-GPU "
+              "sharding of this path is described in the design notes, not built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from long_context_self_amd import synth
+
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[args.config]
+    R = args.layers or DEFAULT_LAYERS.get(cfg.name, 4)
+    m = measure(cfg, R, args.steps, args.warmup, scores=args.scores, refresh_every=args.refresh_every,
+                copy_calibration_mib=args.copy_calibration_mib, log=sys.stderr)
+    kern = kernel_table(cfg, m)
+    value = m["step_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
+    # the call with the largest share of the step's time carries the roofline
+    share = {"verify": m["share"]["verify"], "select": m["share"]["select"], "draft_step": m["share"]["draft"]}
+    dom = max(share, key=share.get)
+    traffic = None
+    if not args.scores and args.refresh_every == 1:
+        traffic = traffic_record(cfg.name, dom)
     result = {
         "metric": "draft-step & verify-step attention latency (us), achieved HBM GB/s vs peak",
         "value": round(value, 2),
@@ -317,36 +382,33 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(m["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": B, "Hq": Hq, "Hkv": cfg.Hkv, "d": cfg.d, "L": L,
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d, "L": cfg.L,
                    "page_size": cfg.page_size, "n_q": cfg.n_q, "n_draft": cfg.n_draft,
                    "select": f"{cfg.mode} top-{cfg.top_k}+{cfg.n_sink} sink+{cfg.n_recent} recent",
                    "collected": "per-KV-head partial scores" if args.scores else "two logit rows",
-                   "refresh_every": RF,
-                   "layers": R},
-        "kernels": {
-            "verify": {"us": round(t_verify_us, 2), "bytes": vb, "GB/s": round(v_gbs, 1),
-                       "frac_hbm_peak": round(v_gbs / HBM_PEAK_GBS, 4),
-                       "TFLOP/s": round(flops_verify / (t_verify_us * 1e-6) / 1e12, 2)},
-            "select": {"us": round(t_select_us, 2), "bytes": sb, "GB/s": round(s_gbs, 1),
-                       "frac_hbm_peak": round(s_gbs / HBM_PEAK_GBS, 4)},
-            "draft_step": {"us": round(t_draft_us, 2), "bytes": int(sum(db) / len(db)),
-                           "GB/s": round(d_gbs, 1), "frac_hbm_peak": round(d_gbs / HBM_PEAK_GBS, 4),
-                           "selected": s_count},
-        },
-        "gamma_attn": round(gamma_attn, 4),
-        "roofline": {"bound": "hbm", "achieved": round(v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(v_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_record(vb) if (args.config == TRAFFIC_WORKLOAD and not args.scores) else None,
-                     "kernel": "verify_attn (attn_kernel + split-K combine), per launch"},
+                   "refresh_every": m["RF"], "layers": R},
+        "kernels": kern,
+        "step_share": {k: round(v / sum(share.values()), 4) for k, v in share.items()},
+        "gamma_attn": round(m["us"]["draft_step"] / m["us"]["verify"], 4),
+        "roofline": {"bound": "hbm", "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": kern[dom]["frac_hbm_peak"], "traffic": traffic,
+                     "kernel": f"{dom}: {CALL_KERNELS[dom]}, per call",
+                     "algorithmic_bytes": kern[dom]["bytes"]},
     }
+    if not args.no_secondary and args.config != SECONDARY_CONFIG:
+        c2 = synth.CONFIGS[SECONDARY_CONFIG]
+        m2 = measure(c2, DEFAULT_LAYERS[SECONDARY_CONFIG], args.steps, args.warmup, log=sys.stderr)
+        result["secondary"] = {"workload": c2.name, "layers": m2["R"], "ms_per_step": round(m2["ms_per_step"], 4),
+                               "value_GB/s": round(m2["step_bytes"] / (m2["ms_per_step"] * 1e-3) / 1e9, 2),
+                               "kernels": kernel_table(c2, m2)}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, kv, q, qd, None, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -1059,8 +1059,10 @@ hipError_t launch_main(const AttnPlan& p, const AttnArgs& a, hipStream_t stream)
 }  // namespace
 
 AttnPlan attn_plan(int32_t mode, int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d,
-                   int32_t page_size, int32_t max_prefix_len, int32_t cap, int32_t max_tail_len) {
+                   int32_t page_size, int32_t max_prefix_len, int32_t cap, int32_t max_tail_len,
+                   int32_t cus) {
   AttnPlan p{};
+  const long long ncu = cus > 0 ? cus : kDefaultCUs;
   p.D = d;
   const int G = Hq / Hkv;
   p.rows = n_q * G;
@@ -1088,15 +1090,15 @@ AttnPlan attn_plan(int32_t mode, int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv
   const long long step_bytes = (long long)kStepTokens * 2 * d * 2;
   long long min_steps = (partial_bytes * 25 + step_bytes - 1) / step_bytes;
   if (min_steps < kWaves) min_steps = kWaves;
-  const long long target = (mode == MODE_DENSE) ? 4LL * kNumCUs : (long long)kNumCUs;
+  const long long target = (mode == MODE_DENSE) ? 4LL * ncu : ncu;
   long long ns = target / pairs;
   const long long ns_cap = (T + min_steps - 1) / min_steps;
   if (ns > ns_cap) ns = ns_cap;
   if (ns > kMaxSplits) ns = kMaxSplits;
   if (ns < 1) ns = 1;
   // whole rounds of the CUs
-  if (pairs * ns > kNumCUs) {
-    const long long whole = (pairs * ns) / kNumCUs * kNumCUs / pairs;
+  if (pairs * ns > ncu) {
+    const long long whole = (pairs * ns) / ncu * ncu / pairs;
     if (whole >= 1) ns = whole;
   }
   p.n_split = (int32_t)ns;

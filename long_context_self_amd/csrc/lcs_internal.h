@@ -23,7 +23,7 @@ constexpr int kWaves = 4;         // waves per workgroup (one token stream each)
 constexpr int kMaxRowsPerWG = 48; // q-rows (n_q * G) handled by one workgroup: three 16-row
                                   // tiles, the most whose accumulators fit one wave's registers
 constexpr int kMaxSplits = 128;   // split-K partials per (sequence, KV head, row chunk)
-constexpr int kNumCUs = 256;      // MI355X compute units
+constexpr int kDefaultCUs = 256;  // MI355X compute units; used when the device cannot be queried
 
 struct AttnArgs {
   const uint16_t* k;
@@ -77,9 +77,15 @@ struct AttnPlan {
   size_t part_bytes, ublk_bytes, umask_bytes, ucount_bytes, total_bytes;
 };
 
-// Split policy and workspace layout; identical on every call with the same sizes.
+// Split policy and workspace layout; identical on every call with the same sizes on the
+// same device.  cus = compute units of the current device (device_cus()).
 AttnPlan attn_plan(int32_t mode, int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d,
-                   int32_t page_size, int32_t max_prefix_len, int32_t cap, int32_t max_tail_len);
+                   int32_t page_size, int32_t max_prefix_len, int32_t cap, int32_t max_tail_len,
+                   int32_t cus);
+
+// Compute units of the current HIP device, read once per device (kDefaultCUs when no
+// device can be queried, e.g. for a workspace query on a machine without a GPU).
+int32_t device_cus();
 
 // Launch the attention kernels on `stream`.  Returns hipSuccess or the launch error.
 hipError_t attn_launch(const AttnPlan& plan, AttnArgs args, void* workspace, hipStream_t stream);

@@ -43,9 +43,15 @@ def recall(cfg, kv, idx: np.ndarray, cnt: np.ndarray) -> float:
 
 
 def run(cfg, iters: int, drift: float = 0.1, seed: int = 0, warmup: int = 1, log=None,
-        scores: bool = False) -> dict:
+        scores: bool = False, keep_last: bool = False) -> dict:
     """scores: verify writes per-KV-head partial scores and select reads them, instead
-    of the two collected logit rows (same selection rule, one row per KV head)."""
+    of the two collected logit rows (same selection rule, one row per KV head).
+
+    keep_last: also return, under "last", host copies of the last iteration's inputs and
+    outputs as the calls saw them (the K cache before that iteration's drift, the
+    verifier and draft queries, verify's out and collected rows, the selected sets, the
+    last draft step's output and tail length) and, after the final drift, the device K
+    cache and the host cache it must equal."""
     import torch
 
     from . import lcs, synth
@@ -77,6 +83,7 @@ def run(cfg, iters: int, drift: float = 0.1, seed: int = 0, warmup: int = 1, log
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     rec = {"verify_us": [], "select_us": [], "draft_us": [], "iter_us": [], "recall": [], "moved_rows": []}
     k_flat = k_dev.view(-1, d)
+    last = None
     for it in range(-warmup, iters):
         tag = max(it, 0)
         qv = _bf16(torch, synth.make_queries(cfg, kv, cfg.n_q, seed=seed, tag=1000 + 2 * tag), dev)
@@ -105,6 +112,12 @@ def run(cfg, iters: int, drift: float = 0.1, seed: int = 0, warmup: int = 1, log
         torch.cuda.synchronize()
         if it < 0:
             continue
+        if keep_last and it == iters - 1:
+            last = {"k_before": kv.k.copy(), "q": qv.view(torch.int16).cpu().numpy().view(np.uint16),
+                    "qd": qd[-1].view(torch.int16).cpu().numpy().view(np.uint16),
+                    "out": out.cpu().numpy(), "logits": logits.cpu().numpy(), "idx": idx.cpu().numpy(),
+                    "cnt": cnt.cpu().numpy(), "dout": dout.cpu().numpy(),
+                    "tail_len": cfg.n_q + cfg.n_draft}
         tv, ts, td = (e[0].elapsed_time(e[1]) * 1e3, e[1].elapsed_time(e[2]) * 1e3,
                       e[2].elapsed_time(e[3]) * 1e3)
         rec["verify_us"].append(tv)
@@ -118,11 +131,17 @@ def run(cfg, iters: int, drift: float = 0.1, seed: int = 0, warmup: int = 1, log
         if rows.size:
             k_flat[torch.from_numpy(rows).to(dev)] = _bf16(torch, bits, dev)
         rec["moved_rows"].append(int(rows.size))
+        if last is not None:
+            torch.cuda.synchronize()
+            last["k_after_dev"] = k_dev.view(torch.int16).cpu().numpy().view(np.uint16)
+            last["k_after_host"] = kv.k
+            last["kv"] = kv
         if log is not None and (it % 32 == 0 or it == iters - 1):
             print(f"iteration {it}: verify {tv:.1f} us, select {ts:.1f} us, draft step {td / max(cfg.n_draft, 1):.1f}"
                   f" us, recall {rec['recall'][-1]:.3f}", file=log, flush=True)
     med = {k: float(np.median(v)) for k, v in rec.items() if v}
-    return {"config": cfg.name, "iters": iters, "drift": drift, "scores": scores, "median": med,
+    extra = {"last": last} if keep_last else {}
+    return {**extra, "config": cfg.name, "iters": iters, "drift": drift, "scores": scores, "median": med,
             "recall_first": rec["recall"][0] if rec["recall"] else None,
             "recall_last": rec["recall"][-1] if rec["recall"] else None,
             "gamma_attn": med["draft_us"] / med["verify_us"] if rec["verify_us"] else None}

@@ -20,10 +20,17 @@ def test_cpu_baseline_leg_on_a_bounded_sample():
     sys.path.insert(0, ROOT)
     import bench
     from long_context_self_amd import synth
-    cfg = synth.CONFIGS["llama8b_32k"].with_(L=2048, top_k=256)
-    kv = synth.make_paged_kv(cfg, seed=0)
-    q = synth.make_queries(cfg, kv, cfg.n_q, seed=0)
-    qd = [synth.make_queries(cfg, kv, 1, seed=0, tag=100 + j) for j in range(cfg.n_draft)]
-    rec = bench.cpu_baseline(cfg, kv, q, qd, None, 0.5)
+    cfg = synth.CONFIGS["stress_128k"].with_(L=2048, top_k=256)
+    rec = bench.cpu_baseline(cfg, 0.5)
     assert rec["kind"] == "oracle" and rec["unit"] == "GB/s" and rec["value"] > 0 and rec["cores"] >= 1
+    assert "replicated" in rec["sample"] and "one sequence x one KV head" in rec["sample"]
     json.dumps(rec)
+
+
+def test_default_workload_is_the_largest_one_gpu_config():
+    sys.path.insert(0, ROOT)
+    import bench
+    from long_context_self_amd import synth
+    cfgs = [c for c in synth.CONFIGS.values() if c.mode in ("shared", "per_kv_head")]
+    biggest = max(cfgs, key=lambda c: c.B * c.L * c.Hkv)
+    assert bench.DEFAULT_CONFIG == biggest.name == "stress_128k"

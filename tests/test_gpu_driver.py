@@ -47,3 +47,49 @@ def test_experiments_overlap_and_collect_overhead():
     assert set(pts) == {"0", "1", "2", "half", "all"}
     assert all(p["verify_us"] > 0 for p in pts.values())
     assert pts["all"]["logit_bytes_over_kv"] > pts["2"]["logit_bytes_over_kv"] > 0
+
+
+@pytest.mark.parametrize("mode", ["shared", "per_kv_head"])
+def test_driver_iteration_after_drift_matches_oracle(mode):
+    """Several drift iterations, then the last one checked call by call: the device K
+    cache equals the host cache the drift rewrote (bit for bit), verify's output and
+    collected rows match the fp64 oracle on the drifted cache, select is bit-exact on
+    the GPU's own rows and overlaps the oracle's selection, and the last draft step
+    matches the oracle over the GPU's set plus the tail."""
+    require_gpu()
+    import numpy as np
+
+    from long_context_self_amd import driver
+    from oracle import attention as oa
+    from oracle import select as osel
+    from gpu_helpers import logit_rel_err, scale_for
+
+    cfg = synth.CONFIGS["llama8b_32k"].with_(B=2, L=4096, top_k=256, crit_frac=0.02, mode=mode)
+    res = driver.run(cfg, iters=3, drift=0.1, seed=4, keep_last=True)
+    last = res["last"]
+    kv = last["kv"]
+    assert res["median"]["moved_rows"] > 0
+    # the device-side scatter of the drifted K rows reproduces the host cache exactly
+    assert np.array_equal(last["k_after_dev"], last["k_after_host"])
+    # the last iteration's calls ran on the cache before its own drift
+    scale = scale_for(cfg.d)
+    o_out, o_lg, _ = oa.verify_attn(last["q"], last["k_before"], kv.v, kv.block_table, kv.prefix_len,
+                                    cfg.page_size, scale)
+    assert float(np.max(np.abs(last["out"] - o_out))) <= 1e-2
+    for b in range(cfg.B):
+        L = int(kv.prefix_len[b])
+        assert logit_rel_err(last["logits"][b, :, :, :L], o_lg[b, :, :, :L]) <= 1e-3
+    n_sets = 1 if mode == "shared" else cfg.Hkv
+    ref32 = osel.select(last["logits"], kv.prefix_len, cfg.Hkv, mode, cfg.top_k, cfg.n_sink, cfg.n_recent,
+                        precision="f32")
+    ref64 = osel.select(o_lg, kv.prefix_len, cfg.Hkv, mode, cfg.top_k, cfg.n_sink, cfg.n_recent)
+    for b in range(cfg.B):
+        for s in range(n_sets):
+            got = last["idx"][b, s, :int(last["cnt"][b, s])]
+            assert np.array_equal(got, ref32[b][s]), (b, s)
+            common = np.intersect1d(got, ref64[b][s]).size
+            assert common >= 0.99 * ref64[b][s].size
+    o_d, _ = oa.sparse_attn(last["qd"], last["k_before"], kv.v, kv.block_table, cfg.page_size, mode,
+                            last["idx"], last["cnt"], kv.prefix_len,
+                            np.full(cfg.B, last["tail_len"], dtype=np.int32), scale)
+    assert float(np.max(np.abs(last["dout"] - o_d))) <= 1e-2

@@ -202,3 +202,24 @@ def test_largest_accepted_set():
     idx, cnt = gpu_select(lg, lens, 1, "shared", 5000, 4, 64)
     assert_exact(idx, cnt, cpu_rule(lg, lens, 1, "shared", 5000, 4, 64))
     assert idx[0, 0, cnt[0, 0] - 1] == L - 1
+
+
+@pytest.mark.parametrize("mode,bs", [("shared", 0), ("per_kv_head", 0), ("block", 16)])
+@pytest.mark.parametrize("which", ["top_k", "n_sink", "n_recent"])
+def test_window_sizes_at_int32_max_keep_everything(mode, bs, which):
+    """top_k, n_sink or n_recent at INT32_MAX: the budget covers every item, so every
+    position (or block) is kept, as the CPU rule says; the device's 32-bit window sums
+    must not overflow into a partial selection."""
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, ld = 2, 4, 2, 700
+    lens = np.array([700, 333], dtype=np.int32)
+    lg = rng.standard_normal((B, Hq, 2, ld)).astype(np.float32)
+    sizes = {"top_k": 5, "n_sink": 2, "n_recent": 3}
+    sizes[which] = 2 ** 31 - 1
+    idx, cnt = gpu_select(lg, lens, Hkv, mode, sizes["top_k"], sizes["n_sink"], sizes["n_recent"], bs=bs)
+    res = cpu_rule(lg, lens, Hkv, mode, sizes["top_k"], sizes["n_sink"], sizes["n_recent"], bs=bs)
+    for b in range(B):
+        n_items = -(-int(lens[b]) // bs) if mode == "block" else int(lens[b])
+        for s in range(len(res[b])):
+            assert res[b][s].tolist() == list(range(n_items))
+    assert_exact(idx, cnt, res)
