@@ -8,6 +8,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -59,6 +61,30 @@ lcs_status hip_status(hipError_t e) {
 
 }  // namespace
 
+
+namespace lcs {
+
+int32_t device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int32_t> cache[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  int32_t n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) {
+    (void)hipGetLastError();
+    v = kDefaultCUs;
+  }
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+}  // namespace lcs
+
 extern "C" {
 
 const char* lcs_last_error(void) { return g_err; }
@@ -69,7 +95,8 @@ size_t lcs_verify_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq, const lcs_
                                   int32_t max_prefix_len) {
   if (kv == nullptr || kv->Hkv < 1 || Hq < 1 || n_q < 1 || B < 0 || max_prefix_len < 0) return 0;
   if (Hq % kv->Hkv != 0 || (kv->d != 64 && kv->d != 128)) return 0;
-  return lcs::attn_plan(lcs::MODE_DENSE, B, n_q, Hq, kv->Hkv, kv->d, kv->page_size, max_prefix_len, 0, 0)
+  return lcs::attn_plan(lcs::MODE_DENSE, B, n_q, Hq, kv->Hkv, kv->d, kv->page_size, max_prefix_len, 0, 0,
+                         lcs::device_cus())
       .total_bytes;
 }
 
@@ -94,7 +121,7 @@ lcs_status verify_impl(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t
   if ((long long)max_prefix_len + n_q > (long long)kv->max_pages * kv->page_size)
     return fail(LCS_E_SHAPE, "max_prefix_len + n_q exceeds max_pages * page_size");
   const lcs::AttnPlan plan = lcs::attn_plan(lcs::MODE_DENSE, B, n_q, Hq, kv->Hkv, kv->d, kv->page_size,
-                                            max_prefix_len, 0, 0);
+                                            max_prefix_len, 0, 0, lcs::device_cus());
   if (workspace_bytes < plan.total_bytes || (plan.part_bytes > 0 && workspace == nullptr))
     return fail(LCS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, plan.total_bytes);
   lcs::AttnArgs a{};
@@ -245,7 +272,8 @@ lcs_status select_impl(const float* logits, int64_t logits_ld, int32_t n_rows, i
     if (!is_pow2(block_size) || block_size < 4 || block_size > lcs::kScorePos)
       return fail(LCS_E_UNSUPPORTED, "block_size %d is not a power of two in [4, %d]", block_size, lcs::kScorePos);
     items = (max_prefix_len + block_size - 1) / block_size;
-    need = (n_sink + block_size - 1) / block_size + (long long)top_k + (n_recent + block_size - 1) / block_size + 1;
+    need = ((long long)n_sink + block_size - 1) / block_size + (long long)top_k +
+           ((long long)n_recent + block_size - 1) / block_size + 1;
   } else {
     need = (long long)n_sink + top_k + n_recent;
   }
@@ -269,9 +297,12 @@ lcs_status select_impl(const float* logits, int64_t logits_ld, int32_t n_rows, i
   a.mode = (int32_t)mode;
   a.prefix_len = prefix_len;
   a.max_len = max_prefix_len;
-  a.top_k = top_k;
-  a.n_sink = n_sink;
-  a.n_recent = n_recent;
+  // The kernels add the window sizes in 32-bit arithmetic.  A size at or beyond the
+  // longest prefix (items in block mode) keeps every item either way, so clamping to it
+  // changes no result and keeps those sums far from overflow.
+  a.top_k = (int32_t)(top_k < items ? top_k : items);
+  a.n_sink = n_sink < max_prefix_len ? n_sink : max_prefix_len;
+  a.n_recent = n_recent < max_prefix_len ? n_recent : max_prefix_len;
   a.lg_bs = (mode == LCS_SET_BLOCK) ? ilog2(block_size) : 0;
   a.vec4 = (aligned(logits, 16) && logits_ld % 4 == 0) ? 1 : 0;
   a.indices = indices;
@@ -332,14 +363,19 @@ size_t lcs_sparse_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq, const lcs_
   if (Hq % kv->Hkv != 0 || (kv->d != 64 && kv->d != 128)) return 0;
   const int32_t m = (mode == LCS_SET_BLOCK) ? lcs::MODE_BLOCK
                     : (mode == LCS_SET_SHARED) ? lcs::MODE_LIST_SHARED : lcs::MODE_LIST_PER_HEAD;
-  return lcs::attn_plan(m, B, n_q, Hq, kv->Hkv, kv->d, kv->page_size, 0, cap, max_tail_len).total_bytes;
+  return lcs::attn_plan(m, B, n_q, Hq, kv->Hkv, kv->d, kv->page_size, 0, cap, max_tail_len,
+                         lcs::device_cus()).total_bytes;
 }
 
-lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q, int32_t Hq,
-                                 lcs_set_mode mode, const int32_t* indices, const int32_t* counts,
-                                 int32_t cap, const int32_t* tail_begin, const int32_t* tail_len,
-                                 int32_t max_tail_len, const uint64_t* tail_mask, float scale, float* out,
-                                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+lcs_status sparse_impl(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q, int32_t Hq,
+                       lcs_set_mode mode, const int32_t* indices, const int32_t* counts, int32_t cap,
+                       const int32_t* tail_begin, const int32_t* tail_len, int32_t max_tail_len,
+                       const uint64_t* tail_mask, float scale, float* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   lcs_status st = check_kv(kv);
   if (st != LCS_OK) return st;
   if ((st = check_heads(Hq, kv->Hkv)) != LCS_OK) return st;
@@ -363,7 +399,8 @@ lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t 
                 kv->page_size);
   const int32_t m = (mode == LCS_SET_BLOCK) ? lcs::MODE_BLOCK
                     : (mode == LCS_SET_SHARED) ? lcs::MODE_LIST_SHARED : lcs::MODE_LIST_PER_HEAD;
-  const lcs::AttnPlan plan = lcs::attn_plan(m, B, n_q, Hq, kv->Hkv, kv->d, kv->page_size, 0, cap, max_tail_len);
+  const lcs::AttnPlan plan =
+      lcs::attn_plan(m, B, n_q, Hq, kv->Hkv, kv->d, kv->page_size, 0, cap, max_tail_len, lcs::device_cus());
   if (workspace_bytes < plan.total_bytes ||
       ((plan.part_bytes > 0 || m == lcs::MODE_BLOCK) && workspace == nullptr))
     return fail(LCS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, plan.total_bytes);
@@ -393,6 +430,19 @@ lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t 
   a.out = out;
   a.lse = lse;
   return hip_status(lcs::attn_launch(plan, a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q, int32_t Hq,
+                                 lcs_set_mode mode, const int32_t* indices, const int32_t* counts,
+                                 int32_t cap, const int32_t* tail_begin, const int32_t* tail_len,
+                                 int32_t max_tail_len, const uint64_t* tail_mask, float scale, float* out,
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_impl(kv, q, B, n_q, Hq, mode, indices, counts, cap, tail_begin, tail_len, max_tail_len, tail_mask,
+                     scale, out, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
