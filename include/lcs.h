@@ -28,7 +28,8 @@
  *  - Every pointer argument is DEVICE memory owned by the caller, except the
  *    lcs_paged_kv struct itself (host memory, read during the call only).
  *    The library never allocates or frees device memory and keeps no state
- *    between calls beyond its loaded code objects.
+ *    between calls beyond its loaded code objects (which include the static
+ *    scratch array of lcs_sparse_draft_attn_noalloc).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream).  Outputs are valid once the stream has reached the call.
  *  - All shape and argument checks run on the host before anything is
@@ -302,6 +303,29 @@ lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t 
                                  const int32_t* tail_len, int32_t max_tail_len,
                                  const uint64_t* tail_mask, float scale, float* out, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * lcs_sparse_draft_attn without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.
+ *
+ * Arguments, outputs, limits and results are those of lcs_sparse_draft_attn
+ * (the same kernels run; outputs are bit-identical).  The split-K partials and
+ * the block-union plan go to a static device array of the library, 32 MiB per
+ * GPU, held from the first such call on a device until the process ends; the
+ * call itself allocates and frees nothing.  A call whose workspace need
+ * (lcs_sparse_workspace_bytes) exceeds 32 MiB returns LCS_E_WORKSPACE and
+ * launches nothing.  Every call on one GPU uses that GPU's one array: calls
+ * that overlap on a GPU (concurrent streams, threads) race and give undefined
+ * results; calls ordered on one stream are safe.  Nothing in the array needs
+ * to start at zero (every byte a call reads was written earlier in that call).
+ * ------------------------------------------------------------------------- */
+lcs_status lcs_sparse_draft_attn_noalloc(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q,
+                                         int32_t Hq, lcs_set_mode mode, const int32_t* indices,
+                                         const int32_t* counts, int32_t cap, const int32_t* tail_begin,
+                                         const int32_t* tail_len, int32_t max_tail_len,
+                                         const uint64_t* tail_mask, float scale, float* out, float* lse,
+                                         void* stream);
 
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char* lcs_last_error(void);

@@ -9,6 +9,7 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <mutex>
 
 namespace {
 
@@ -61,11 +62,46 @@ lcs_status hip_status(hipError_t e) {
 
 }  // namespace
 
+// Device scratch of lcs_sparse_draft_attn_noalloc: its split-K partials and block-union
+// plan live here instead of in a caller workspace.  Every GPU the library runs on holds
+// one copy for the life of the process.  Host code never uses this name as an address:
+// it takes the device address from hipGetSymbolAddress (scratch_ptr) once per device.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of the current device's scratch, looked up on its first use there
+// (with that device current) and kept per device.
+lcs_status scratch_ptr(void** out) {
+  static std::atomic<void*> ptrs[kMaxDevices] = {};
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LCS_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LCS_E_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = ptrs[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(LCS_E_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+      ptrs[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return LCS_OK;
+}
+
+}  // namespace
 
 namespace lcs {
 
 int32_t device_cus() {
-  constexpr int kMaxDevices = 64;
   static std::atomic<int32_t> cache[kMaxDevices] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
@@ -371,11 +407,13 @@ size_t lcs_sparse_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq, const lcs_
 
 namespace {
 
+// Shared body of the two sparse entry points.  use_scratch: the workspace is the
+// library's static device scratch of the current device instead of the caller's.
 lcs_status sparse_impl(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q, int32_t Hq,
                        lcs_set_mode mode, const int32_t* indices, const int32_t* counts, int32_t cap,
                        const int32_t* tail_begin, const int32_t* tail_len, int32_t max_tail_len,
                        const uint64_t* tail_mask, float scale, float* out, float* lse, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, void* stream, bool use_scratch) {
   lcs_status st = check_kv(kv);
   if (st != LCS_OK) return st;
   if ((st = check_heads(Hq, kv->Hkv)) != LCS_OK) return st;
@@ -401,6 +439,13 @@ lcs_status sparse_impl(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t
                     : (mode == LCS_SET_SHARED) ? lcs::MODE_LIST_SHARED : lcs::MODE_LIST_PER_HEAD;
   const lcs::AttnPlan plan =
       lcs::attn_plan(m, B, n_q, Hq, kv->Hkv, kv->d, kv->page_size, 0, cap, max_tail_len, lcs::device_cus());
+  if (use_scratch) {
+    if (plan.total_bytes > kStaticScratchBytes)
+      return fail(LCS_E_WORKSPACE, "this call needs %zu bytes of scratch; the static scratch holds %zu",
+                  plan.total_bytes, kStaticScratchBytes);
+    if ((st = scratch_ptr(&workspace)) != LCS_OK) return st;
+    workspace_bytes = kStaticScratchBytes;
+  }
   if (workspace_bytes < plan.total_bytes ||
       ((plan.part_bytes > 0 || m == lcs::MODE_BLOCK) && workspace == nullptr))
     return fail(LCS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, plan.total_bytes);
@@ -442,7 +487,17 @@ lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t 
                                  int32_t max_tail_len, const uint64_t* tail_mask, float scale, float* out,
                                  float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return sparse_impl(kv, q, B, n_q, Hq, mode, indices, counts, cap, tail_begin, tail_len, max_tail_len, tail_mask,
-                     scale, out, lse, workspace, workspace_bytes, stream);
+                     scale, out, lse, workspace, workspace_bytes, stream, false);
+}
+
+lcs_status lcs_sparse_draft_attn_noalloc(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q,
+                                         int32_t Hq, lcs_set_mode mode, const int32_t* indices,
+                                         const int32_t* counts, int32_t cap, const int32_t* tail_begin,
+                                         const int32_t* tail_len, int32_t max_tail_len,
+                                         const uint64_t* tail_mask, float scale, float* out, float* lse,
+                                         void* stream) {
+  return sparse_impl(kv, q, B, n_q, Hq, mode, indices, counts, cap, tail_begin, tail_len, max_tail_len, tail_mask,
+                     scale, out, lse, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

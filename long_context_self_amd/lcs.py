@@ -59,6 +59,8 @@ SIGNATURES = {
     "lcs_sparse_workspace_bytes": (_sz, [_i32, _i32, _i32, _KV, _i32, _i32, _i32]),
     "lcs_sparse_draft_attn": (_i32, [_KV, _p, _i32, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _i32, _p,
                                     _f, _p, _p, _p, _sz, _p]),
+    "lcs_sparse_draft_attn_noalloc": (_i32, [_KV, _p, _i32, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _i32,
+                                            _p, _f, _p, _p, _p]),
     "lcs_last_error": (ctypes.c_char_p, []),
     "lcs_version": (ctypes.c_char_p, []),
 }
@@ -330,6 +332,25 @@ def sparse_draft_attn(kv: PagedKV, q: torch.Tensor, mode: str, indices: torch.Te
                                         _ptr(indices), _ptr(counts), cap, _ptr(tail_begin),
                                         _ptr(tail_len), max_tail_len, _ptr(tail_mask), scale,
                                         _ptr(out), _ptr(lse), ws.data_ptr(), ws.numel(), _stream()))
+    return out, lse
+
+
+def sparse_draft_attn_noalloc(kv: PagedKV, q: torch.Tensor, mode: str, indices: torch.Tensor,
+                              counts: torch.Tensor, tail_begin: torch.Tensor, tail_len: torch.Tensor,
+                              max_tail_len: int, scale: float, tail_mask: Optional[torch.Tensor] = None,
+                              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """lcs_sparse_draft_attn_noalloc: the library's static device scratch instead of a
+    workspace (out and lse must be passed in to allocate nothing).  Returns (out, lse)."""
+    B, n_q, Hq, d = q.shape
+    dev = q.device
+    cap = indices.shape[-1]
+    if out is None:
+        out = torch.empty((B, n_q, Hq, d), dtype=torch.float32, device=dev)
+    desc = kv.desc()
+    _check(load().lcs_sparse_draft_attn_noalloc(ctypes.byref(desc), _ptr(q), B, n_q, Hq, SET_MODES[mode],
+                                                _ptr(indices), _ptr(counts), cap, _ptr(tail_begin),
+                                                _ptr(tail_len), max_tail_len, _ptr(tail_mask), scale,
+                                                _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 

@@ -106,6 +106,20 @@ int main(void) {
   if (lcs_verify_workspace_bytes(1, 9, 33, &kv, 32768) != 0) ++fails;
   if (lcs_select_workspace_bytes(1, 4, 2, LCS_SET_SHARED, 100, 0) == 0) ++fails;
   if (lcs_sparse_workspace_bytes(1, 1, 4, &kv, LCS_SET_SHARED, 10, 4) == 0) ++fails;
+  /* sparse draft without a workspace: argument checks and the scratch-size refusal */
+  EXPECT(lcs_sparse_draft_attn_noalloc(0, P(0x1000), 1, 1, 4, LCS_SET_SHARED, idx, cnt, 10, pl, pl, 4, 0, 0.1f,
+                                       out, 0, 0),
+         LCS_E_ARG);
+  EXPECT(lcs_sparse_draft_attn_noalloc(&kv, P(0x1000), 0, 1, 4, LCS_SET_SHARED, idx, cnt, 10, pl, pl, 4, 0, 0.1f,
+                                       out, 0, 0),
+         LCS_OK);
+  {
+    lcs_paged_kv big = kv;
+    big.page_size = 64;
+    EXPECT(lcs_sparse_draft_attn_noalloc(&big, P(0x1000), 4, 64, 4, LCS_SET_BLOCK, idx, cnt, 100000, pl, pl, 4, 0,
+                                         0.1f, out, 0, 0),
+           LCS_E_WORKSPACE);
+  }
   if (strncmp(lcs_version(), "lcs ", 4) != 0) ++fails;
   printf("%d failures\n", fails);
   return fails != 0;

@@ -162,6 +162,33 @@ def test_sparse_host_errors():
     assert sp(wsb=0, cap=100000, mtl=100) == lcs.LCS_E_WORKSPACE
 
 
+def test_sparse_noalloc_host_errors():
+    """The static-scratch variant checks its arguments like the workspace variant, and
+    refuses a call whose workspace need exceeds its 32 MiB scratch, all before touching
+    a device."""
+    lcs, L = lib()
+    kv = fake_kv(lcs)
+
+    def sp(kvd=kv, **kw):
+        a = dict(q=0x1000, B=1, n_q=1, Hq=4, mode=0, idx=0x2000, cnt=0x3000, cap=10, tb=0x4000, tl=0x5000,
+                 mtl=4, tm=None, scale=0.1, out=0x6000, lse=None)
+        a.update(kw)
+        return L.lcs_sparse_draft_attn_noalloc(ctypes.byref(kvd), a["q"], a["B"], a["n_q"], a["Hq"], a["mode"],
+                                               a["idx"], a["cnt"], a["cap"], a["tb"], a["tl"], a["mtl"], a["tm"],
+                                               a["scale"], a["out"], a["lse"], None)
+
+    assert sp(B=0) == lcs.LCS_OK
+    assert sp(mode=3) == lcs.LCS_E_ARG
+    assert sp(q=0) == lcs.LCS_E_ARG
+    assert sp(n_q=65) == lcs.LCS_E_UNSUPPORTED
+    # block mode, 4 x 2 pairs x 64 rows x 100000 blocks: far beyond 32 MiB of union plan
+    big = fake_kv(lcs, page_size=64)
+    need = L.lcs_sparse_workspace_bytes(4, 64, 4, ctypes.byref(big), 2, 100000, 4)
+    assert need > 32 << 20
+    assert sp(big, B=4, n_q=64, mode=2, cap=100000) == lcs.LCS_E_WORKSPACE
+    assert b"static scratch" in L.lcs_last_error()
+
+
 def test_workspace_queries_are_deterministic():
     lcs, L = lib()
     kv = fake_kv(lcs, page_size=16, max_pages=4096, num_pages=4096 * 8, Hkv=8)
