@@ -13,6 +13,10 @@ Modules
 ``select``     the selector: head-summed two-row scores, sink / recent windows
                and top-k, in fp64 and in the pinned fp32 order that the GPU
                must reproduce bit for bit.
+``nsa``        the NSA branches of sparse speculative verification: block-mean
+               compression of the cache, and the gated sum of the compression,
+               selection and sliding-window branches (exact or approximate
+               grouping of the verifier rows' block sets).
 ``speedup``    the speculative speedup identity and its derivative.
 ``brute``      pure-Python loops for tiny inputs, used to pin ``attention``.
 
@@ -28,5 +32,6 @@ invariants or pairwise enumeration); see ``tests/test_oracle_*.py``.  That
 includes ``attention.attention_one`` (brute force, a verify row, closed form),
 ``attention.sparse_attn`` with a different list per KV head (brute force) and
 ``select.select`` in block mode (rank enumeration over each group's block
-maxima).
+maxima, or block log-sum-exps) and every function of ``nsa`` (brute force per
+branch, linearity in the gates, hand-worked bf16 rounding).
 """

@@ -14,7 +14,9 @@ Definitions followed
   group.
 * SSV page, "What carries the argument" / Figure 3 caption: NSA selects
   hardware-aligned blocks.  A block's score is the max of the position scores
-  inside it (no formula is printed; max is the plainest reading).
+  inside it (no formula is printed; max is the plainest reading).  The
+  alternative aggregation is the block's log-sum-exp, log sum_p exp(sigma_p),
+  a smooth max that also counts how many strong positions a block holds.
 
 Selection rule (the pages are silent on these points; our readings):
 1. sigma_p = sum over heads in the set of (l[h, row0, p] + l[h, row1, p]).
@@ -136,13 +138,25 @@ def block_scores(sigma: np.ndarray, L: int, bs: int) -> np.ndarray:
                     dtype=sigma.dtype)
 
 
+def block_scores_lse(sigma: np.ndarray, L: int, bs: int) -> np.ndarray:
+    """beta_c = log sum over the prefix positions p of block c of exp(sigma_p), in
+    float64 (shifted by the block's max, which leaves the value unchanged)."""
+    nb = (L + bs - 1) // bs
+    out = np.empty(nb)
+    for c in range(nb):
+        x = np.asarray(sigma[c * bs:min(L, (c + 1) * bs)], dtype=np.float64)
+        m = np.max(x)
+        out[c] = m + np.log(np.sum(np.exp(x - m)))
+    return out
+
+
 def topk_blocks(sigma: np.ndarray, L: int, top_k: int, n_sink: int, n_recent: int,
-                bs: int) -> np.ndarray:
-    """Block selection rule; returns ascending int64 block ids."""
+                bs: int, agg: str = "max") -> np.ndarray:
+    """Block selection rule; returns ascending int64 block ids.  agg: "max" or "lse"."""
     nb, sb, rb = block_window(L, bs, n_sink, n_recent)
     if sb >= rb or nb <= sb + top_k + (nb - rb):
         return np.arange(nb, dtype=np.int64)
-    beta = block_scores(sigma, L, bs)
+    beta = block_scores(sigma, L, bs) if agg == "max" else block_scores_lse(sigma, L, bs)
     pool = np.arange(sb, rb, dtype=np.int64)
     order = np.lexsort((pool, -beta[sb:rb]))
     chosen = pool[order[:top_k]]
@@ -151,12 +165,13 @@ def topk_blocks(sigma: np.ndarray, L: int, top_k: int, n_sink: int, n_recent: in
 
 def select(logits: np.ndarray, prefix_len: np.ndarray, Hkv: int, mode: str, top_k: int,
            n_sink: int, n_recent: int, block_size: int = 0, precision: str = "f64",
-           score_kind: str = "logits", lse: np.ndarray = None, rows=None):
+           score_kind: str = "logits", lse: np.ndarray = None, rows=None, block_agg: str = "max"):
     """Run the selector for every (sequence, set).
 
     logits: [B][Hq][n_rows][ld] (the collected rows; two for Collect-2-Query).
     score_kind "weights" scores by softmax weights (needs lse [B][n_q][Hq] and the
-    verifier row of each slot, rows).  Returns a list over b of lists over sets of
+    verifier row of each slot, rows).  block_agg "max" or "lse" aggregates a block's
+    position scores in block mode.  Returns a list over b of lists over sets of
     ascending int64 arrays (positions, or block ids in 'block' mode, where sets
     are per KV head).
     """
@@ -174,7 +189,7 @@ def select(logits: np.ndarray, prefix_len: np.ndarray, Hkv: int, mode: str, top_
         for s in range(n_sets(smode, Hkv)):
             sig = score(logits, b, L, set_heads(smode, Hq, Hkv, s))
             if mode == "block":
-                per.append(topk_blocks(sig, L, top_k, n_sink, n_recent, block_size))
+                per.append(topk_blocks(sig, L, top_k, n_sink, n_recent, block_size, block_agg))
             else:
                 per.append(topk_tokens(sig, L, top_k, n_sink, n_recent))
         res.append(per)
