@@ -81,6 +81,16 @@ typedef enum {
   LCS_SCORE_SOFTMAX_WEIGHT = 1  /* Sparse Glimpse: post-softmax weights of the rows   */
 } lcs_score_kind;
 
+typedef enum {
+  LCS_BLOCK_MAX = 0,  /* a block scores the max of its positions' scores               */
+  LCS_BLOCK_LSE = 1   /* a block scores the log-sum-exp of its positions' scores       */
+} lcs_block_score;
+
+typedef enum {
+  LCS_GROUP_EXACT = 0,       /* SSV exact merged schedule: each row keeps its own blocks */
+  LCS_GROUP_APPROXIMATE = 1  /* SSV approximate mode: every row sees the group's union   */
+} lcs_group_mode;
+
 typedef struct {
   const void* k;              /* device bf16 [num_pages][Hkv][page_size][d]            */
   const void* v;              /* device bf16 [num_pages][Hkv][page_size][d]            */
@@ -218,6 +228,27 @@ lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, in
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Block selection with a choice of block score.
+ *
+ * SSV page, Figure 3 overview (NSA token selection picks hardware-aligned
+ * blocks): the pages print no block score.  LCS_BLOCK_MAX is the max of the
+ * block's position scores (what lcs_select_topk uses in BLOCK mode, with which
+ * this call agrees bit for bit); LCS_BLOCK_LSE is their log-sum-exp,
+ *   beta_c = m + log(sum over p in block c, p < L, of exp(sigma_p - m)),
+ *   m = the block's max, evaluated in fp32 (expf, logf),
+ * which also rewards blocks holding several strong positions.  Sets are per
+ * (sequence, KV head); every other argument, the output layout, the rule and
+ * the workspace (lcs_select_workspace_bytes with LCS_SET_BLOCK) are those of
+ * lcs_select_topk in BLOCK mode.  LSE keys go through expf / logf, so the
+ * result matches the same rule on the CPU up to their rounding.
+ * ------------------------------------------------------------------------- */
+lcs_status lcs_select_topk_blocks(const float* logits, int64_t logits_ld, int32_t B, int32_t Hq, int32_t Hkv,
+                                  const int32_t* prefix_len, int32_t max_prefix_len, lcs_block_score block_score,
+                                  int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t block_size,
+                                  int32_t* indices, int32_t* counts, int32_t cap, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Top-k selection from per-KV-head partial scores (lcs_verify_attn_scores).
  *
  * Rule, modes, windows, outputs and workspace (lcs_select_workspace_bytes with
@@ -303,6 +334,77 @@ lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t 
                                  const int32_t* tail_len, int32_t max_tail_len,
                                  const uint64_t* tail_mask, float scale, float* out, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * NSA sparse verification: token compression, block plan, gated three-branch
+ * attention.
+ *
+ * SSV page, Figure 3 overview: NSA attention runs a token-compression branch,
+ * a token-selection branch and a sliding-window branch for every verifier
+ * query; Figure 10 caption: the grouped-query kernel runs without grouping,
+ * exact or approximate; Figure 3 text: reuse layers take the nearest refresh
+ * layer's index, skip index derivation and go straight into one fused kernel.
+ * The pages print no formula for the branches; this library's reading:
+ *  - compression: compressed block i of (b, g) covers positions
+ *    [i*cmp_stride, i*cmp_stride + cmp_len) and exists once it lies wholly in
+ *    the prefix; its key (value) is the bf16 mean of the block's keys (values)
+ *    (NSA learns this map; the mean is the parameter-free instance);
+ *  - a verifier row attends, in three separate softmaxes, to (a) every
+ *    compressed block of its sequence, (b) its selected blocks (exact) or the
+ *    union of its group's blocks (approximate), clipped to the prefix, plus the
+ *    tail slots it sees, and (c) the last `window` prefix positions plus the
+ *    tail slots it sees;
+ *  - out = g_cmp*o_a + g_slc*o_b + g_win*o_c with the caller's gates; a branch
+ *    that sees nothing contributes 0 and reports lse = -inf.
+ *
+ * lcs_nsa_compress writes the compressed cache:
+ *  k_cmp, v_cmp  bf16 [B][Hkv][max_cmp][d] (caller-owned, written): rows
+ *                i < floor((L - cmp_len) / cmp_stride) + 1 (L = prefix_len[b],
+ *                none if L < cmp_len, at most max_cmp) hold block means, the
+ *                rest zero.
+ *  cmp_len power of two in [1, 1024]; cmp_stride in [1, cmp_len].
+ *
+ * lcs_nsa_plan derives the block index of a layer ("refresh"): the union of
+ * the n_q rows' block lists of every (b, g), ascending, with the rows that
+ * selected each block (group EXACT) or every row (group APPROXIMATE), into the
+ * caller's plan buffer of lcs_nsa_plan_bytes(B, n_q, Hkv, cap) bytes.
+ *  indices, counts  as lcs_sparse_draft_attn's BLOCK mode: [B][n_q][Hkv][cap]
+ *                   ascending distinct block ids, [B][n_q][Hkv].
+ *
+ * lcs_nsa_attn runs the three branches and the gating in one attention kernel
+ * (plus its split-K combine); a "reuse" layer calls it with the plan of the
+ * refresh layer, skipping lcs_nsa_plan.
+ *  q            bf16 [B][n_q][Hq][d]; row i sits at tail slot i.
+ *  plan, plan_bytes, cap  the plan written by lcs_nsa_plan with the same B,
+ *               n_q, Hkv and cap (block = page, page_size % 32 == 0).
+ *  tail_begin   device int32 [B]: the prefix length L (tail slot j is position
+ *               L + j); tail_len [B] <= max_tail_len; tail_mask [B][n_q] or NULL
+ *               as in lcs_sparse_draft_attn.
+ *  gates        fp32 [B][n_q][Hq][3] (compression, selection, window).
+ *  out          fp32 [B][n_q][Hq][d]; lse fp32 [B][n_q][Hq][3] per branch, or NULL.
+ *  workspace    lcs_nsa_workspace_bytes(...) bytes (split-K partials), no init.
+ * Limits: n_q in [1, 64]; d in {64, 128}; B*Hkv*max_cmp < 2^31.  Errors as for
+ * the other calls (host checks, nothing launched on failure).
+ * ------------------------------------------------------------------------- */
+lcs_status lcs_nsa_compress(const lcs_paged_kv* kv, int32_t B, const int32_t* prefix_len, int32_t max_prefix_len,
+                            int32_t cmp_len, int32_t cmp_stride, void* k_cmp, void* v_cmp, int32_t max_cmp,
+                            void* stream);
+
+size_t lcs_nsa_plan_bytes(int32_t B, int32_t n_q, int32_t Hkv, int32_t cap);
+
+lcs_status lcs_nsa_plan(const lcs_paged_kv* kv, int32_t B, int32_t n_q, const int32_t* indices,
+                        const int32_t* counts, int32_t cap, lcs_group_mode group, void* plan, size_t plan_bytes,
+                        void* stream);
+
+size_t lcs_nsa_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq, const lcs_paged_kv* kv, int32_t cap,
+                               int32_t max_tail_len, int32_t max_cmp, int32_t window);
+
+lcs_status lcs_nsa_attn(const lcs_paged_kv* kv, const void* k_cmp, const void* v_cmp, int32_t max_cmp,
+                        int32_t cmp_len, int32_t cmp_stride, int32_t window, const void* q, int32_t B, int32_t n_q,
+                        int32_t Hq, const void* plan, size_t plan_bytes, int32_t cap, const int32_t* tail_begin,
+                        const int32_t* tail_len, int32_t max_tail_len, const uint64_t* tail_mask,
+                        const float* gates, float scale, float* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * lcs_sparse_draft_attn without a workspace, for callers that cannot allocate

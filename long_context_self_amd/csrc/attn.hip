@@ -137,16 +137,40 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 struct SeqInfo {
   int L, cnt, tb, tl, U, T;
+  int br;      // NSA: branch of this workgroup
+  int cbase;   // NSA compression branch: row of (b, g)'s first compressed block
   const int32_t* list;
   const int32_t* ub;
   const uint64_t* um;
 };
 
 // Sequence-level bounds for (b, g); every quantity read from device memory is clamped.
+// NSA: cnt = compressed blocks (compression branch) or window prefix tokens (window
+// branch); the selection branch reads the union plan like block mode.
 template <int MODE>
-__device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, int g) {
+__device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, int g, int br = 0) {
   SeqInfo si{};
   const int P = 1 << a.lg_page;
+  si.br = br;
+  if (MODE == MODE_NSA) {
+    si.tb = max(a.tail_begin[b], 0);
+    si.tl = min(max(a.tail_len[b], 0), a.max_tail_len);
+    if (br == BR_CMP) {
+      si.cnt = (si.tb < a.cmp_len) ? 0 : min((si.tb - a.cmp_len) / a.cmp_stride + 1, a.max_cmp);
+      si.cbase = (b * a.Hkv + g) * a.max_cmp;
+      si.T = (si.cnt + kStepTokens - 1) / kStepTokens;
+    } else if (br == BR_SLC) {
+      const size_t o = (size_t)(b * a.Hkv + g);
+      si.U = min(max(a.ucount[o], 0), a.ucap);
+      si.ub = a.ublk + o * a.ucap;
+      si.um = a.umask + o * a.ucap;
+      si.T = si.U * (P / kStepTokens) + (si.tl + kStepTokens - 1) / kStepTokens;
+    } else {
+      si.cnt = min(a.window, si.tb);
+      si.T = (si.cnt + kStepTokens - 1) / kStepTokens + (si.tl + kStepTokens - 1) / kStepTokens;
+    }
+    return si;
+  }
   if (MODE == MODE_DENSE) {
     si.L = min(max(a.prefix_len[b], 0), a.max_prefix_len);
     si.T = (si.L + a.n_q + kStepTokens - 1) / kStepTokens;
@@ -202,7 +226,7 @@ __device__ __forceinline__ void slot_pos(const AttnArgs& a, const SeqInfo& si, i
   // different steps), read with wave-uniform loads while every lane is active
   int blk = -1;
   uint64_t bmask = 0;
-  if (MODE == MODE_BLOCK && si.U > 0) {
+  if ((MODE == MODE_BLOCK || (MODE == MODE_NSA && si.br == BR_SLC)) && si.U > 0) {
     const int spb = P / kStepTokens;
     const int e_lo = min(__builtin_amdgcn_readfirstlane(step) / spb, si.U - 1);
     const int e_hi = min(__builtin_amdgcn_readlane(step, 32) / spb, si.U - 1);
@@ -222,7 +246,28 @@ __device__ __forceinline__ void slot_pos(const AttnArgs& a, const SeqInfo& si, i
       pos = u;
       jt = u - si.L;
     }
-  } else if (MODE == MODE_BLOCK) {
+  } else if (MODE == MODE_NSA && si.br == BR_CMP) {
+    const int u = step * kStepTokens + t;      // compressed block index
+    if (u < si.cnt) {
+      pos = u;
+      v = kAll;
+    }
+  } else if (MODE == MODE_NSA && si.br == BR_WIN) {
+    const int pre = (si.cnt + kStepTokens - 1) / kStepTokens;
+    if (step < pre) {
+      const int u = step * kStepTokens + t;
+      if (u < si.cnt) {
+        pos = si.tb - si.cnt + u;
+        v = kAll;
+      }
+    } else {
+      const int u = (step - pre) * kStepTokens + t;
+      if (u < si.tl) {
+        pos = si.tb + u;
+        jt = u;
+      }
+    }
+  } else if (MODE == MODE_BLOCK || MODE == MODE_NSA) {
     const int spb = P / kStepTokens;
     const int blk_steps = si.U * spb;
     if (step < blk_steps) {
@@ -308,8 +353,11 @@ __device__ __forceinline__ void meta_stage_c(const AttnArgs& a, const SeqInfo& s
     const uint64_t cm = shfl64(colmask, jt & 63);     // every lane takes part in the shuffle
     if (jt >= 0) v = (jt < 64 || a.rowmask == nullptr) ? cm : 0;
     int row = -1;
-    if (pos >= 0 && (pos >> a.lg_page) < a.max_pages && (unsigned)page[r] < (unsigned)a.num_pages)
+    if (MODE == MODE_NSA && si.br == BR_CMP) {
+      if (pos >= 0) row = si.cbase + pos;        // compressed cache, not paged
+    } else if (pos >= 0 && (pos >> a.lg_page) < a.max_pages && (unsigned)page[r] < (unsigned)a.num_pages) {
       row = ((page[r] * a.Hkv + g) << a.lg_page) | (pos & (P - 1));
+    }
     if (row < 0) v = 0;
     wm.row[nb][tok] = row;
     wm.vis[nb][tok] = v;
@@ -329,7 +377,8 @@ __device__ __forceinline__ void meta_stage_c(const AttnArgs& a, const SeqInfo& s
 // (16 lanes, one chunk index each, 16 different rows) fall on different banks.
 // Tile tt occupies blocks [tt*16/(64/RCH), ...) of 1 KB; V: token t -> block KDMA+t.
 template <int D>
-__device__ __forceinline__ void step_dma(const AttnArgs& a, const int32_t* rows, char* slot, int lane, int x, int j) {
+__device__ __forceinline__ void step_dma(const uint16_t* kb, const uint16_t* vb, const int32_t* rows, char* slot,
+                                         int lane, int x, int j) {
   constexpr int RCH = D / 8;          // 16-byte chunks per row
   constexpr int RPI = 64 / RCH;       // rows per DMA
   constexpr int IPT = 16 / RPI;       // DMAs per 16-token tile
@@ -340,14 +389,14 @@ __device__ __forceinline__ void step_dma(const AttnArgs& a, const int32_t* rows,
     for (int i = 0; i < IPT; ++i) {
       const int tok = 16 * tt + RPI * i + rq;
       const int c = p ^ (tok % RCH);
-      dma16(a.k + (size_t)max(rows[tok], 0) * D + 8 * c, slot + (tt * IPT + i) * 1024);
+      dma16(kb + (size_t)max(rows[tok], 0) * D + 8 * c, slot + (tt * IPT + i) * 1024);
     }
   const int4 rv0 = *reinterpret_cast<const int4*>(rows + 4 * j);
   const int4 rv1 = *reinterpret_cast<const int4*>(rows + 16 + 4 * j);
   const int rv[8] = {rv0.x, rv0.y, rv0.z, rv0.w, rv1.x, rv1.y, rv1.z, rv1.w};
   const int dx = 8 * (x & (D / 8 - 1));   // d = 64: lanes x >= 8 repeat x - 8 (rows unused)
 #pragma unroll
-  for (int t = 0; t < 8; ++t) dma16(a.v + (size_t)max(rv[t], 0) * D + dx, slot + (2 * IPT + t) * 1024);
+  for (int t = 0; t < 8; ++t) dma16(vb + (size_t)max(rv[t], 0) * D + dx, slot + (2 * IPT + t) * 1024);
 }
 
 // The same DMAs one at a time, so that a refill can be spread through the compute of
@@ -369,15 +418,15 @@ __device__ __forceinline__ void dma_rows(const int32_t* rows, int lane, int j, i
   sr[G::NK + 4] = rv1.x; sr[G::NK + 5] = rv1.y; sr[G::NK + 6] = rv1.z; sr[G::NK + 7] = rv1.w;
 }
 template <int D, int n>
-__device__ __forceinline__ void dma_piece(const AttnArgs& a, const int (&sr)[DmaGeom<D>::N], char* slot, int lane,
-                                          int x) {
+__device__ __forceinline__ void dma_piece(const uint16_t* kb, const uint16_t* vb, const int (&sr)[DmaGeom<D>::N],
+                                          char* slot, int lane, int x) {
   using G = DmaGeom<D>;
   if (n < G::NK) {
     const int tok = 16 * (n / G::IPT) + G::RPI * (n % G::IPT) + lane / G::RCH;
     const int c = (lane % G::RCH) ^ (tok % G::RCH);
-    dma16(a.k + (size_t)max(sr[n], 0) * D + 8 * c, slot + n * 1024);
+    dma16(kb + (size_t)max(sr[n], 0) * D + 8 * c, slot + n * 1024);
   } else {
-    dma16(a.v + (size_t)max(sr[n], 0) * D + 8 * (x & (D / 8 - 1)), slot + n * 1024);
+    dma16(vb + (size_t)max(sr[n], 0) * D + 8 * (x & (D / 8 - 1)), slot + n * 1024);
   }
 }
 
@@ -473,6 +522,81 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int pid, int r, int
     a.lse[(size_t)(b * a.n_q + i) * a.Hq + h] = (Ls > 0.f) ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
 }
 
+// Split-order merge of splits [s0, s0 + n) of q-row r (n <= 128): running max M (log2
+// units), sum Ls and the unnormalised output columns of this lane.  One wave.
+template <int D>
+__device__ __forceinline__ void merge_range(const float* base, size_t pstride, int r, int s0, int n, int lane,
+                                            float& M, float& Ls, float (&acc)[D / 64]) {
+  constexpr int CPL = D / 64;
+  const float* mcol = base + (size_t)kMaxRowsPerWG * D + r;
+  const float* ocol = base + (size_t)r * D + CPL * lane;
+  float mv[2], lv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int sp = lane + 64 * u;
+    mv[u] = -INFINITY;
+    lv[u] = 0.f;
+    if (sp < n) {
+      const size_t o = (size_t)(s0 + sp) * pstride;
+      mv[u] = mcol[o];
+      lv[u] = mcol[o + kMaxRowsPerWG];
+    }
+  }
+  M = fmaxf(mv[0], mv[1]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float Ms = (M == -INFINITY) ? 0.f : M;
+  float wv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) wv[u] = __builtin_amdgcn_exp2f(mv[u] - Ms);
+  Ls = wv[0] * lv[0] + wv[1] * lv[1];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+#pragma unroll 8
+  for (int sp = 0; sp < n; ++sp) {
+    const float w = lane_f(sp < 64 ? wv[0] : wv[1], sp & 63);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] += w * ocol[(size_t)(s0 + sp) * pstride + c];
+  }
+}
+
+// NSA: merge each branch's splits, then out = sum over branches of gate * branch output;
+// lse [B][n_q][Hq][3] holds each branch's log-sum-exp (-inf for a branch that saw nothing).
+template <int D>
+__device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int pid, int r, int lane) {
+  constexpr int CPL = D / 64;
+  const int rc = pid % a.n_rc;
+  const int bg = pid / a.n_rc;
+  const int g = bg % a.Hkv;
+  const int b = bg / a.Hkv;
+  const size_t pstride = (size_t)kMaxRowsPerWG * (D + 2);
+  const float* base = a.part + (size_t)pid * a.n_split * pstride;
+  const int rr = rc * kMaxRowsPerWG + r;
+  const int i = rr / a.G;
+  const int h = g * a.G + (rr - i * a.G);
+  const size_t qh = (size_t)(b * a.n_q + i) * a.Hq + h;
+  float res[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) res[c] = 0.f;
+  const int s0[3] = {0, a.ns0, a.ns0 + a.ns1};
+  const int ns[3] = {a.ns0, a.ns1, a.ns2};
+#pragma unroll
+  for (int br = 0; br < 3; ++br) {
+    float M, Ls, acc[CPL];
+    merge_range<D>(base, pstride, r, s0[br], ns[br], lane, M, Ls, acc);
+    const float gate = a.gates[qh * 3 + br];
+    const float f = (Ls > 0.f) ? gate / Ls : 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) res[c] += f * acc[c];
+    if (lane == 0 && a.lse != nullptr) a.lse[qh * 3 + br] = (Ls > 0.f) ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+  }
+  float* op = a.out + qh * D + CPL * lane;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) op[c] = res[c];
+}
+
 template <int D, int MODE>
 __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   const int pid = blockIdx.x;                   // (b*Hkv + g)*n_rc + rc
@@ -480,7 +604,8 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   const int nrows = min(kMaxRowsPerWG, a.rows - rc * kMaxRowsPerWG);
   const int r = blockIdx.y * combine_rows<MODE>() + (threadIdx.x >> 6);
   if (r >= nrows) return;
-  merge_row<D>(a, pid, r, threadIdx.x & 63);
+  if constexpr (MODE == MODE_NSA) merge_row_nsa<D>(a, pid, r, threadIdx.x & 63);
+  else merge_row<D>(a, pid, r, threadIdx.x & 63);
 }
 
 // SC: dense verify that writes per-KV-head partial scores of the two collected rows
@@ -517,14 +642,23 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   char* ring = reinterpret_cast<char*>(wbase_lds + sizeof(WaveMeta));
   float* s_merge = reinterpret_cast<float*>(smem_raw);
 
-  const SeqInfo si = seq_info<MODE>(a, b, g);
+  // NSA: the launch's splits are the compression, then selection, then window branch's
+  int br = 0, s_loc = s, ns_loc = a.n_split;
+  if constexpr (MODE == MODE_NSA) {
+    br = (s >= a.ns0 + a.ns1) ? BR_WIN : (s >= a.ns0 ? BR_SLC : BR_CMP);
+    s_loc = s - (br == BR_WIN ? a.ns0 + a.ns1 : (br == BR_SLC ? a.ns0 : 0));
+    ns_loc = (br == BR_WIN) ? a.ns2 : (br == BR_SLC ? a.ns1 : a.ns0);
+  }
+  const uint16_t* kb = (MODE == MODE_NSA && br == BR_CMP) ? a.ck : a.k;
+  const uint16_t* vb = (MODE == MODE_NSA && br == BR_CMP) ? a.cv : a.v;
+  const SeqInfo si = seq_info<MODE>(a, b, g, br);
   // balanced contiguous step ranges: the n_split * kWaves waves of this (sequence, KV
   // head) split its steps evenly (to within one step); a workgroup's waves are adjacent
   // Token-list modes split the launch's step bound (cap + max tail) instead of the
   // sequence's own, so that the index-list DMA can go out before the sequence's counts
   // arrive; waves past the sequence's end then have nothing to do.
-  const long long nwv = (long long)a.n_split * kWaves;
-  const long long gwv = (long long)s * kWaves + wave;
+  const long long nwv = (long long)ns_loc * kWaves;
+  const long long gwv = (long long)s_loc * kWaves + wave;
   const long long Tsp = (MODE == MODE_LIST_SHARED) ? (long long)a.T_max : (long long)si.T;
   const int w0 = (int)(gwv * Tsp / nwv);
   const int w1s = (int)((gwv + 1) * Tsp / nwv);
@@ -599,8 +733,8 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   if (MODE != MODE_LIST_SHARED && w0 < w1) {
     meta_stage_c<MODE>(a, si, g, w0, w1, colmask, lane, wm, 0);
     wait_lgkm0();
-    step_dma<D>(a, wm.row[0], ring, lane, x, j);
-    if (w0 + 1 < w1) step_dma<D>(a, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
+    step_dma<D>(kb, vb, wm.row[0], ring, lane, x, j);
+    if (w0 + 1 < w1) step_dma<D>(kb, vb, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
   }
   // Q in LDS.  An LDS-only barrier: __syncthreads would also wait for those DMAs.
   wait_lgkm0();
@@ -629,8 +763,8 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
       wait_vm<0>();
       meta_stage_c<MODE>(a, si, g, w0, w1, colmask, lane, wm, 0);
       wait_lgkm0();
-      step_dma<D>(a, wm.row[0], ring, lane, x, j);
-      if (w0 + 1 < w1) step_dma<D>(a, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
+      step_dma<D>(kb, vb, wm.row[0], ring, lane, x, j);
+      if (w0 + 1 < w1) step_dma<D>(kb, vb, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
     }
     // Software pipeline.  Iteration s waits for slot s and moves it to registers, issues
     // the metadata stage, runs S(s) on the matrix core, stores S(s)'s collected logits,
@@ -747,7 +881,7 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
       pv([&](auto ec) {
         constexpr int e = decltype(ec)::value;
         static_for<e * NDMA / 8, (e + 1) * NDMA / 8>([&](auto nc) {
-          if (FAST || dma_due) dma_piece<D, decltype(nc)::value>(a, sr, slot, lane, x);
+          if (FAST || dma_due) dma_piece<D, decltype(nc)::value>(kb, vb, sr, slot, lane, x);
         });
       });
       bool grow_any = false;
@@ -921,7 +1055,7 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   for (int qt = 0; qt < QT; ++qt) {
     const int r = 16 * qt + x;
     if (r >= nrows || 32 * j >= D) continue;
-    if (a.n_split == 1) {
+    if (MODE != MODE_NSA && a.n_split == 1) {
       const int rr = r0 + r;
       const int i = rr / a.G;
       const int h = g * a.G + (rr - i * a.G);
@@ -963,6 +1097,7 @@ __global__ void __launch_bounds__(256) block_union_kernel(AttnArgs a) {
   __shared__ int32_t scnt[64];
   int32_t* ub = const_cast<int32_t*>(a.ublk) + (size_t)bg * a.ucap;
   uint64_t* um = const_cast<uint64_t*>(a.umask) + (size_t)bg * a.ucap;
+  const uint64_t all_rows = (a.n_q >= 64) ? kAll : ((1ull << a.n_q) - 1);
   int total = 0;
   for (int base = 0; base < a.max_pages; base += kPlanChunk) {
     const int span = min(kPlanChunk, a.max_pages - base);     // block ids of this chunk
@@ -1010,7 +1145,7 @@ __global__ void __launch_bounds__(256) block_union_kernel(AttnArgs a) {
       const uint64_t msk = ((uint64_t)mhi[id] << 32) | mlo[id];
       if (msk != 0 && (int)pos < a.ucap) {
         ub[pos] = base + id;
-        um[pos] = msk;
+        um[pos] = a.approx ? all_rows : msk;   // approximate: every row sees the union
         ++pos;
       }
     }
@@ -1018,6 +1153,57 @@ __global__ void __launch_bounds__(256) block_union_kernel(AttnArgs a) {
     __syncthreads();
   }
   if (tid == 0) const_cast<int32_t*>(a.ucount)[bg] = min(total, a.ucap);
+}
+
+// NSA token compression: compressed row i of (b, g) is the mean of the K (V) rows of
+// positions [i*stride, i*stride + len), rounded to bf16 (nearest, ties to even); rows of
+// blocks that do not lie entirely in the prefix are zero.  Lane group: one compressed row,
+// one 16-byte chunk of dims per lane; the len rows are summed in position order in fp32.
+template <int D>
+__global__ void __launch_bounds__(256) compress_kernel(AttnArgs a, const int32_t* prefix_len, uint16_t* kc,
+                                                       uint16_t* vc) {
+  constexpr int CH = D / 8;           // 16-byte chunks per row
+  constexpr int RPW = 256 / CH;       // compressed rows per workgroup
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int i = blockIdx.x * RPW + (int)threadIdx.x / CH;
+  const int c = (int)threadIdx.x % CH;
+  if (i >= a.max_cmp) return;
+  const int P = 1 << a.lg_page;
+  const int L = min(max(prefix_len[b], 0), a.max_prefix_len);
+  const int n = (L < a.cmp_len) ? 0 : min((L - a.cmp_len) / a.cmp_stride + 1, a.max_cmp);
+  u32x4 ko = u32x4{0, 0, 0, 0}, vo = u32x4{0, 0, 0, 0};
+  if (i < n) {
+    float ks[8], vs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ks[e] = vs[e] = 0.f;
+    const int p0 = i * a.cmp_stride;
+    const int32_t* bt = a.bt + (size_t)b * a.max_pages;
+#pragma unroll 4
+    for (int t = 0; t < a.cmp_len; ++t) {
+      const int p = p0 + t;
+      const int page = bt[p >> a.lg_page];
+      if ((unsigned)page >= (unsigned)a.num_pages) continue;   // outside the cache: skipped
+      const size_t row = ((size_t)(page * a.Hkv + g) << a.lg_page) | (size_t)(p & (P - 1));
+      const u32x4 kk = *reinterpret_cast<const u32x4*>(a.k + row * D + 8 * c);
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(a.v + row * D + 8 * c);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        ks[2 * w] += bf16_to_f32(kk[w] & 0xffffu);
+        ks[2 * w + 1] += bf16_to_f32(kk[w] >> 16);
+        vs[2 * w] += bf16_to_f32(vv[w] & 0xffffu);
+        vs[2 * w + 1] += bf16_to_f32(vv[w] >> 16);
+      }
+    }
+    const float inv = 1.f / (float)a.cmp_len;     // a power of two: exact
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      ko[w] = pack_bf16(ks[2 * w] * inv, ks[2 * w + 1] * inv);
+      vo[w] = pack_bf16(vs[2 * w] * inv, vs[2 * w + 1] * inv);
+    }
+  }
+  const size_t o = ((size_t)(b * a.Hkv + g) * a.max_cmp + i) * D + 8 * c;
+  *reinterpret_cast<u32x4*>(kc + o) = ko;
+  *reinterpret_cast<u32x4*>(vc + o) = vo;
 }
 
 template <int D, int MODE>
@@ -1040,7 +1226,7 @@ hipError_t launch_main_mode(const AttnPlan& p, const AttnArgs& a, hipStream_t st
     default: hipLaunchKernelGGL((attn_kernel<D, 3, MODE>), grid, dim3(256), 0, stream, a); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_split == 1) return e;
+  if (e != hipSuccess || (MODE != MODE_NSA && p.n_split == 1)) return e;
   const int rows_wg = p.rows < kMaxRowsPerWG ? p.rows : kMaxRowsPerWG;
   constexpr int CR = combine_rows<MODE>();
   hipLaunchKernelGGL((combine_kernel<D, MODE>), dim3(a.B * a.Hkv * p.n_rc, (rows_wg + CR - 1) / CR),
@@ -1053,6 +1239,7 @@ hipError_t launch_main(const AttnPlan& p, const AttnArgs& a, hipStream_t stream)
   // the two token-list modes differ only in which list a KV head reads
   if (a.mode == MODE_DENSE) return launch_main_mode<D, MODE_DENSE>(p, a, stream);
   if (a.mode == MODE_BLOCK) return launch_main_mode<D, MODE_BLOCK>(p, a, stream);
+  if (a.mode == MODE_NSA) return launch_main_mode<D, MODE_NSA>(p, a, stream);
   return launch_main_mode<D, MODE_LIST_SHARED>(p, a, stream);
 }
 
@@ -1114,6 +1301,76 @@ AttnPlan attn_plan(int32_t mode, int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv
   return p;
 }
 
+UnionLayout union_layout(int32_t B, int32_t Hkv, int32_t n_q, int32_t cap) {
+  UnionLayout u{};
+  const size_t ucap = (size_t)n_q * (cap > 0 ? cap : 0);
+  u.ublk_bytes = align_up((size_t)B * Hkv * ucap * 4, 256);
+  u.umask_bytes = align_up((size_t)B * Hkv * ucap * 8, 256);
+  u.ucount_bytes = align_up((size_t)B * Hkv * 4, 256);
+  u.total_bytes = u.ublk_bytes + u.umask_bytes + u.ucount_bytes;
+  return u;
+}
+
+AttnPlan attn_plan_nsa(int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d, int32_t page_size,
+                       int32_t cap, int32_t max_tail_len, int32_t max_cmp, int32_t window, int32_t cus) {
+  AttnPlan p{};
+  p.D = d;
+  const int G = Hq / Hkv;
+  p.rows = n_q * G;
+  p.n_rc = (p.rows + kMaxRowsPerWG - 1) / kMaxRowsPerWG;
+  const int rows_wg = p.rows < kMaxRowsPerWG ? p.rows : kMaxRowsPerWG;
+  p.QT = (rows_wg + 15) / 16;
+  const long long tail_steps = ((long long)max_tail_len + kStepTokens - 1) / kStepTokens;
+  const long long T[3] = {((long long)max_cmp + kStepTokens - 1) / kStepTokens,
+                          (long long)n_q * cap * (page_size / kStepTokens) + tail_steps,
+                          ((long long)window + kStepTokens - 1) / kStepTokens + tail_steps};
+  long long pairs = (long long)B * Hkv * p.n_rc;
+  if (pairs < 1) pairs = 1;
+  // one round of workgroups over the CUs, shared by the branches in proportion to their
+  // step bounds; every branch gets at least one split, and a split streams enough KV
+  // that its partial stays a small share of what it reads
+  const long long ncu = cus > 0 ? cus : kDefaultCUs;
+  long long total = ncu / pairs;
+  if (total < 3) total = 3;
+  const long long partial_bytes = (long long)rows_wg * (d + 2) * 4;
+  const long long step_bytes = (long long)kStepTokens * 2 * d * 2;
+  long long min_steps = (partial_bytes * 25 + step_bytes - 1) / step_bytes;
+  if (min_steps < kWaves) min_steps = kWaves;
+  const long long sumT = T[0] + T[1] + T[2];
+  int n = 0;
+  for (int c = 0; c < 3; ++c) {
+    long long ns = (sumT > 0) ? total * T[c] / sumT : 1;
+    const long long ns_cap = (T[c] + min_steps - 1) / min_steps;
+    if (ns > ns_cap) ns = ns_cap;
+    if (ns > kMaxSplits / 3) ns = kMaxSplits / 3;
+    if (ns < 1) ns = 1;
+    p.ns_br[c] = (int32_t)ns;
+    n += (int32_t)ns;
+  }
+  p.n_split = n;
+  p.T_max = (int32_t)(T[0] > T[1] ? (T[0] > T[2] ? T[0] : T[2]) : (T[1] > T[2] ? T[1] : T[2]));
+  p.part_bytes = align_up((size_t)pairs * p.n_split * kMaxRowsPerWG * (d + 2) * 4, 256);
+  p.total_bytes = p.part_bytes;
+  return p;
+}
+
+hipError_t union_launch(const AttnArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(block_union_kernel, dim3(a.B * a.Hkv), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t compress_launch(const AttnArgs& a, int32_t d, int32_t B, const int32_t* prefix_len, uint16_t* kc,
+                           uint16_t* vc, hipStream_t stream) {
+  if (a.max_cmp < 1 || B < 1) return hipSuccess;
+  const int per = 256 / (d / 8);                 // compressed rows per workgroup
+  const dim3 grid((a.max_cmp + per - 1) / per, a.Hkv, B);
+  if (d == 128)
+    hipLaunchKernelGGL(compress_kernel<128>, grid, dim3(256), 0, stream, a, prefix_len, kc, vc);
+  else
+    hipLaunchKernelGGL(compress_kernel<64>, grid, dim3(256), 0, stream, a, prefix_len, kc, vc);
+  return hipGetLastError();
+}
+
 hipError_t attn_launch(const AttnPlan& p, AttnArgs a, void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   a.part = p.part_bytes ? reinterpret_cast<float*>(ws) : nullptr;
@@ -1122,6 +1379,12 @@ hipError_t attn_launch(const AttnPlan& p, AttnArgs a, void* workspace, hipStream
   a.n_split = p.n_split;
   a.rows = p.rows;
   a.n_rc = p.n_rc;
+  if (a.mode == MODE_NSA) {      // the union plan is the caller's (a.ublk, a.umask, a.ucount)
+    a.ns0 = p.ns_br[0];
+    a.ns1 = p.ns_br[1];
+    a.ns2 = p.ns_br[2];
+    return (p.D == 128) ? launch_main<128>(p, a, stream) : launch_main<64>(p, a, stream);
+  }
   if (a.mode == MODE_BLOCK) {
     a.ublk = reinterpret_cast<const int32_t*>(ws);
     ws += p.ublk_bytes;

@@ -287,7 +287,7 @@ lcs_status select_impl(const float* logits, int64_t logits_ld, int32_t n_rows, i
                        int32_t n_q, uint64_t rows_mask, int32_t B, int32_t Hq, int32_t Hkv,
                        const int32_t* prefix_len, int32_t max_prefix_len, lcs_set_mode mode, int32_t top_k,
                        int32_t n_sink, int32_t n_recent, int32_t block_size, int32_t* indices, int32_t* counts,
-                       int32_t cap, void* workspace, size_t workspace_bytes, void* stream) {
+                       int32_t cap, void* workspace, size_t workspace_bytes, void* stream, int32_t block_lse = 0) {
   if (Hkv < 1) return fail(LCS_E_SHAPE, "Hkv must be >= 1");
   lcs_status st = check_heads(Hq, Hkv);
   if (st != LCS_OK) return st;
@@ -341,6 +341,7 @@ lcs_status select_impl(const float* logits, int64_t logits_ld, int32_t n_rows, i
   a.n_recent = n_recent < max_prefix_len ? n_recent : max_prefix_len;
   a.lg_bs = (mode == LCS_SET_BLOCK) ? ilog2(block_size) : 0;
   a.vec4 = (aligned(logits, 16) && logits_ld % 4 == 0) ? 1 : 0;
+  a.block_lse = block_lse;
   a.indices = indices;
   a.counts = counts;
   a.cap = cap;
@@ -359,6 +360,18 @@ lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, in
   return select_impl(logits, logits_ld, 2, lcs::SCORE_LOGIT_SUM, nullptr, 0, 0, B, Hq, Hkv, prefix_len,
                      max_prefix_len, mode, top_k, n_sink, n_recent, block_size, indices, counts, cap, workspace,
                      workspace_bytes, stream);
+}
+
+lcs_status lcs_select_topk_blocks(const float* logits, int64_t logits_ld, int32_t B, int32_t Hq, int32_t Hkv,
+                                  const int32_t* prefix_len, int32_t max_prefix_len, lcs_block_score block_score,
+                                  int32_t top_k, int32_t n_sink, int32_t n_recent, int32_t block_size,
+                                  int32_t* indices, int32_t* counts, int32_t cap, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (block_score != LCS_BLOCK_MAX && block_score != LCS_BLOCK_LSE)
+    return fail(LCS_E_ARG, "unknown block score %d", (int)block_score);
+  return select_impl(logits, logits_ld, 2, lcs::SCORE_LOGIT_SUM, nullptr, 0, 0, B, Hq, Hkv, prefix_len,
+                     max_prefix_len, LCS_SET_BLOCK, top_k, n_sink, n_recent, block_size, indices, counts, cap,
+                     workspace, workspace_bytes, stream, block_score == LCS_BLOCK_LSE ? 1 : 0);
 }
 
 lcs_status lcs_select_topk_scores(const float* scores, int64_t scores_ld, int32_t B, int32_t Hkv,
@@ -498,6 +511,173 @@ lcs_status lcs_sparse_draft_attn_noalloc(const lcs_paged_kv* kv, const void* q, 
                                          void* stream) {
   return sparse_impl(kv, q, B, n_q, Hq, mode, indices, counts, cap, tail_begin, tail_len, max_tail_len, tail_mask,
                      scale, out, lse, nullptr, 0, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+lcs::AttnArgs kv_args(const lcs_paged_kv* kv) {
+  lcs::AttnArgs a{};
+  a.k = static_cast<const uint16_t*>(kv->k);
+  a.v = static_cast<const uint16_t*>(kv->v);
+  a.bt = kv->block_table;
+  a.num_pages = kv->num_pages;
+  a.lg_page = ilog2(kv->page_size);
+  a.max_pages = kv->max_pages;
+  a.Hkv = kv->Hkv;
+  return a;
+}
+
+lcs_status check_compression(int32_t cmp_len, int32_t cmp_stride, int32_t max_cmp) {
+  if (!is_pow2(cmp_len) || cmp_len > 1024)
+    return fail(LCS_E_UNSUPPORTED, "cmp_len %d is not a power of two in [1, 1024]", cmp_len);
+  if (cmp_stride < 1 || cmp_stride > cmp_len)
+    return fail(LCS_E_ARG, "cmp_stride %d outside [1, cmp_len = %d]", cmp_stride, cmp_len);
+  if (max_cmp < 1) return fail(LCS_E_SHAPE, "max_cmp must be >= 1");
+  return LCS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lcs_status lcs_nsa_compress(const lcs_paged_kv* kv, int32_t B, const int32_t* prefix_len, int32_t max_prefix_len,
+                            int32_t cmp_len, int32_t cmp_stride, void* k_cmp, void* v_cmp, int32_t max_cmp,
+                            void* stream) {
+  lcs_status st = check_kv(kv);
+  if (st != LCS_OK) return st;
+  if ((st = check_compression(cmp_len, cmp_stride, max_cmp)) != LCS_OK) return st;
+  if (B < 0 || max_prefix_len < 0) return fail(LCS_E_SHAPE, "B and max_prefix_len must be >= 0");
+  if ((long long)max_prefix_len > (long long)kv->max_pages * kv->page_size)
+    return fail(LCS_E_SHAPE, "max_prefix_len exceeds max_pages * page_size");
+  if ((long long)B * kv->Hkv * max_cmp >= (1ll << 31))
+    return fail(LCS_E_UNSUPPORTED, "B * Hkv * max_cmp must stay below 2^31 rows");
+  if (B == 0) return LCS_OK;
+  if (prefix_len == nullptr || k_cmp == nullptr || v_cmp == nullptr)
+    return fail(LCS_E_ARG, "prefix_len, k_cmp and v_cmp must be non-NULL");
+  if (!aligned(k_cmp, 16) || !aligned(v_cmp, 16)) return fail(LCS_E_ARG, "k_cmp and v_cmp must be 16-byte aligned");
+  lcs::AttnArgs a = kv_args(kv);
+  a.max_prefix_len = max_prefix_len;
+  a.cmp_len = cmp_len;
+  a.cmp_stride = cmp_stride;
+  a.max_cmp = max_cmp;
+  return hip_status(lcs::compress_launch(a, kv->d, B, prefix_len, static_cast<uint16_t*>(k_cmp),
+                                         static_cast<uint16_t*>(v_cmp), static_cast<hipStream_t>(stream)));
+}
+
+size_t lcs_nsa_plan_bytes(int32_t B, int32_t n_q, int32_t Hkv, int32_t cap) {
+  if (B < 0 || n_q < 1 || Hkv < 1 || cap < 0) return 0;
+  return lcs::union_layout(B, Hkv, n_q, cap).total_bytes;
+}
+
+lcs_status lcs_nsa_plan(const lcs_paged_kv* kv, int32_t B, int32_t n_q, const int32_t* indices,
+                        const int32_t* counts, int32_t cap, lcs_group_mode group, void* plan, size_t plan_bytes,
+                        void* stream) {
+  lcs_status st = check_kv(kv);
+  if (st != LCS_OK) return st;
+  if (group != LCS_GROUP_EXACT && group != LCS_GROUP_APPROXIMATE)
+    return fail(LCS_E_ARG, "unknown group mode %d", (int)group);
+  if (B < 0 || cap < 0) return fail(LCS_E_SHAPE, "B and cap must be >= 0");
+  if (n_q < 1) return fail(LCS_E_SHAPE, "n_q must be >= 1");
+  if (n_q > 64) return fail(LCS_E_UNSUPPORTED, "n_q %d > 64 rows", n_q);
+  const lcs::UnionLayout u = lcs::union_layout(B, kv->Hkv, n_q, cap);
+  if (B == 0) return LCS_OK;
+  if (plan == nullptr || plan_bytes < u.total_bytes)
+    return fail(LCS_E_WORKSPACE, "plan of %zu bytes, %zu needed", plan_bytes, u.total_bytes);
+  if (cap > 0 && (indices == nullptr || counts == nullptr))
+    return fail(LCS_E_ARG, "indices and counts must be non-NULL when cap > 0");
+  lcs::AttnArgs a = kv_args(kv);
+  a.B = B;
+  a.n_q = n_q;
+  a.indices = indices;
+  a.counts = counts;
+  a.cap = cap;
+  a.ucap = n_q * cap;
+  char* pb = static_cast<char*>(plan);
+  a.ublk = reinterpret_cast<const int32_t*>(pb);
+  a.umask = reinterpret_cast<const uint64_t*>(pb + u.ublk_bytes);
+  a.ucount = reinterpret_cast<const int32_t*>(pb + u.ublk_bytes + u.umask_bytes);
+  a.approx = (group == LCS_GROUP_APPROXIMATE) ? 1 : 0;
+  return hip_status(lcs::union_launch(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t lcs_nsa_workspace_bytes(int32_t B, int32_t n_q, int32_t Hq, const lcs_paged_kv* kv, int32_t cap,
+                               int32_t max_tail_len, int32_t max_cmp, int32_t window) {
+  if (kv == nullptr || kv->Hkv < 1 || Hq < 1 || n_q < 1 || B < 0 || cap < 0 || max_tail_len < 0 || max_cmp < 1 ||
+      window < 0)
+    return 0;
+  if (Hq % kv->Hkv != 0 || (kv->d != 64 && kv->d != 128)) return 0;
+  return lcs::attn_plan_nsa(B, n_q, Hq, kv->Hkv, kv->d, kv->page_size, cap, max_tail_len, max_cmp, window,
+                            lcs::device_cus())
+      .total_bytes;
+}
+
+lcs_status lcs_nsa_attn(const lcs_paged_kv* kv, const void* k_cmp, const void* v_cmp, int32_t max_cmp,
+                        int32_t cmp_len, int32_t cmp_stride, int32_t window, const void* q, int32_t B, int32_t n_q,
+                        int32_t Hq, const void* plan, size_t plan_bytes, int32_t cap, const int32_t* tail_begin,
+                        const int32_t* tail_len, int32_t max_tail_len, const uint64_t* tail_mask,
+                        const float* gates, float scale, float* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  lcs_status st = check_kv(kv);
+  if (st != LCS_OK) return st;
+  if ((st = check_heads(Hq, kv->Hkv)) != LCS_OK) return st;
+  if ((st = check_compression(cmp_len, cmp_stride, max_cmp)) != LCS_OK) return st;
+  if (B < 0 || cap < 0 || max_tail_len < 0 || window < 0)
+    return fail(LCS_E_SHAPE, "B, cap, max_tail_len and window must be >= 0");
+  if (n_q < 1) return fail(LCS_E_SHAPE, "n_q must be >= 1");
+  if (n_q > 64) return fail(LCS_E_UNSUPPORTED, "n_q %d > 64 rows", n_q);
+  if (Hq / kv->Hkv > 64) return fail(LCS_E_UNSUPPORTED, "Hq / Hkv = %d > 64 query heads per KV head", Hq / kv->Hkv);
+  if (kv->page_size % lcs::kStepTokens != 0)
+    return fail(LCS_E_UNSUPPORTED, "NSA selection needs page_size %% %d == 0 (page_size %d)", lcs::kStepTokens,
+                kv->page_size);
+  if (tail_mask != nullptr && max_tail_len > 64)
+    return fail(LCS_E_UNSUPPORTED, "a tail mask covers at most 64 tail slots (max_tail_len %d)", max_tail_len);
+  if ((long long)B * kv->Hkv * max_cmp >= (1ll << 31))
+    return fail(LCS_E_UNSUPPORTED, "B * Hkv * max_cmp must stay below 2^31 rows");
+  if (B == 0) return LCS_OK;
+  if (q == nullptr || out == nullptr || tail_begin == nullptr || tail_len == nullptr || gates == nullptr ||
+      plan == nullptr || k_cmp == nullptr || v_cmp == nullptr)
+    return fail(LCS_E_ARG, "q, out, tail_begin, tail_len, gates, plan, k_cmp and v_cmp must be non-NULL");
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cmp, 16) || !aligned(v_cmp, 16))
+    return fail(LCS_E_ARG, "q, out, k_cmp and v_cmp must be 16-byte aligned");
+  if (!isfinite(scale) || !(scale > 0.f)) return fail(LCS_E_ARG, "scale must be finite and positive");
+  const lcs::UnionLayout u = lcs::union_layout(B, kv->Hkv, n_q, cap);
+  if (plan_bytes < u.total_bytes) return fail(LCS_E_WORKSPACE, "plan of %zu bytes, %zu needed", plan_bytes,
+                                              u.total_bytes);
+  const lcs::AttnPlan p = lcs::attn_plan_nsa(B, n_q, Hq, kv->Hkv, kv->d, kv->page_size, cap, max_tail_len, max_cmp,
+                                             window, lcs::device_cus());
+  if (workspace == nullptr || workspace_bytes < p.total_bytes)
+    return fail(LCS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, p.total_bytes);
+  lcs::AttnArgs a = kv_args(kv);
+  a.q = static_cast<const uint16_t*>(q);
+  a.B = B;
+  a.n_q = n_q;
+  a.Hq = Hq;
+  a.G = Hq / kv->Hkv;
+  a.mode = lcs::MODE_NSA;
+  a.rowmask = tail_mask;
+  a.cap = cap;
+  a.tail_begin = tail_begin;
+  a.tail_len = tail_len;
+  a.max_tail_len = max_tail_len;
+  const char* pb = static_cast<const char*>(plan);
+  a.ublk = reinterpret_cast<const int32_t*>(pb);
+  a.umask = reinterpret_cast<const uint64_t*>(pb + u.ublk_bytes);
+  a.ucount = reinterpret_cast<const int32_t*>(pb + u.ublk_bytes + u.umask_bytes);
+  a.ucap = n_q * cap;
+  a.ck = static_cast<const uint16_t*>(k_cmp);
+  a.cv = static_cast<const uint16_t*>(v_cmp);
+  a.max_cmp = max_cmp;
+  a.cmp_len = cmp_len;
+  a.cmp_stride = cmp_stride;
+  a.window = window;
+  a.gates = gates;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(lcs::attn_launch(p, a, workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

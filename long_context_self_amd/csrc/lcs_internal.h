@@ -15,8 +15,12 @@ enum AttnMode : int32_t {
   MODE_DENSE = 0,          // verify: every cache position [0, L + n_q)
   MODE_LIST_SHARED = 1,    // sparse: one token list per sequence
   MODE_LIST_PER_HEAD = 2,  // sparse: one token list per (sequence, KV head)
-  MODE_BLOCK = 3           // sparse: per-row block lists, merged into a union
+  MODE_BLOCK = 3,          // sparse: per-row block lists, merged into a union
+  MODE_NSA = 4             // NSA: compression, selection (union plan) and window branches
 };
+
+// NSA branches, in the order of their split ranges in a launch and of the gates
+enum NsaBranch : int32_t { BR_CMP = 0, BR_SLC = 1, BR_WIN = 2 };
 
 constexpr int kStepTokens = 32;   // tokens consumed per inner step of a wave
 constexpr int kWaves = 4;         // waves per workgroup (one token stream each)
@@ -63,6 +67,16 @@ struct AttnArgs {
   // the sum over the group's heads, ascending, of (row0 + row1) logits
   float* scores;
   int64_t scores_ld;
+  // NSA: compressed cache [B][Hkv][max_cmp][d], compression block length and stride,
+  // window length, gates [B][n_q][Hq][3]; the launch's splits are ns0 compression splits,
+  // then ns1 selection splits, then ns2 window splits.  approx: the union plan gives
+  // every row of a group the whole union (approximate grouping).
+  const uint16_t* ck;
+  const uint16_t* cv;
+  int32_t max_cmp, cmp_len, cmp_stride, window;
+  const float* gates;
+  int32_t ns0, ns1, ns2;
+  int32_t approx;
   // split-K
   float* part;
   int32_t n_split;
@@ -74,8 +88,27 @@ struct AttnArgs {
 
 struct AttnPlan {
   int32_t D, QT, rows, n_rc, n_split, T_max;
+  int32_t ns_br[3];   // MODE_NSA: splits of each branch (sum = n_split)
   size_t part_bytes, ublk_bytes, umask_bytes, ucount_bytes, total_bytes;
 };
+
+// Byte layout of a block-union plan for (B, Hkv) pairs of n_q rows x cap blocks:
+// ublk int32 [B*Hkv][n_q*cap], umask uint64 [B*Hkv][n_q*cap], ucount int32 [B*Hkv].
+struct UnionLayout {
+  size_t ublk_bytes, umask_bytes, ucount_bytes, total_bytes;
+};
+UnionLayout union_layout(int32_t B, int32_t Hkv, int32_t n_q, int32_t cap);
+
+// NSA split policy and workspace (split-K partials only; the union plan is the caller's).
+AttnPlan attn_plan_nsa(int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t d, int32_t page_size,
+                       int32_t cap, int32_t max_tail_len, int32_t max_cmp, int32_t window, int32_t cus);
+
+// Build the block-union plan of a.indices / a.counts into a.ublk / a.umask / a.ucount.
+hipError_t union_launch(const AttnArgs& a, hipStream_t stream);
+
+// Compressed cache: row i of (b, g) = bf16 mean of positions [i*stride, i*stride + len).
+hipError_t compress_launch(const AttnArgs& a, int32_t d, int32_t B, const int32_t* prefix_len, uint16_t* kc,
+                           uint16_t* vc, hipStream_t stream);
 
 // Split policy and workspace layout; identical on every call with the same sizes on the
 // same device.  cus = compute units of the current device (device_cus()).
@@ -116,6 +149,7 @@ struct SelArgs {
   const int32_t* prefix_len;
   int32_t max_len;
   int32_t top_k, n_sink, n_recent, lg_bs, vec4;
+  int32_t block_lse;       // block mode: score a block by log-sum-exp instead of max
   int32_t* indices;
   int32_t* counts;
   int32_t cap;

@@ -6,7 +6,9 @@
 //    the k prefix positions with the largest combined score are kept.
 //  * Sparse Glimpse page, "Core claim": sink + recent + top-ranked history, one
 //    set per head (here per KV head, scored over the heads of its group).
-//  * SSV page, NSA block selection: a block scores the max of its positions.
+//  * SSV page, NSA block selection: a block scores the max of its positions, or
+//    (the alternative aggregation) their log-sum-exp, m + log(sum exp(sigma_p - m)),
+//    computed in fp32 with expf / logf after the block's position scores.
 //  Score of position p: sigma_p = sum over the set's heads h (ascending) of
 //  (l[h,row0,p] + l[h,row1,p]) in that fixed fp32 order; -0 is taken as +0.  Ties
 //  at the k-th place go to the smaller index; output is ascending.  With n collected
@@ -173,6 +175,7 @@ __global__ void __launch_bounds__(256) score_kernel(SelArgs a) {
 
   __shared__ uint32_t lh[kHistBins];
   __shared__ uint32_t bm[kScorePos / 4];
+  __shared__ float sg[kScorePos];      // block log-sum-exp: the workgroup's position scores
   for (int i = tid; i < kHistBins; i += 256) lh[i] = 0;
   if (a.mode == LCS_SEL_BLOCK)
     for (int i = tid; i < kScorePos / 4; i += 256) bm[i] = 0;
@@ -212,19 +215,34 @@ __global__ void __launch_bounds__(256) score_kernel(SelArgs a) {
     }
     if (p >= w.lo && p < w.hi) atomicAdd(&lh[k0 >> 20], 1u);
     if (p + 1 >= w.lo && p + 1 < w.hi) atomicAdd(&lh[k1 >> 20], 1u);
-  } else {
+  } else if (!a.block_lse) {
     if (p < w.L) atomicMax(&bm[(2 * tid) >> a.lg_bs], k0);
     if (p + 1 < w.L) atomicMax(&bm[(2 * tid + 1) >> a.lg_bs], k1);
+  } else {
+    sg[2 * tid] = acc0;
+    sg[2 * tid + 1] = acc1;
   }
   __syncthreads();
   if (a.mode == LCS_SEL_BLOCK) {
+    const int bs = 1 << a.lg_bs;
     const int nbc = kScorePos >> a.lg_bs;
     const int c0 = p0 >> a.lg_bs;
     for (int cl = tid; cl < nbc; cl += 256) {
       const int c = c0 + cl;
       if (c < w.n) {
-        keys[c] = bm[cl];
-        if (c >= w.lo && c < w.hi) atomicAdd(&lh[bm[cl] >> 20], 1u);
+        uint32_t key = bm[cl];
+        if (a.block_lse) {
+          // log-sum-exp of the block's prefix positions, shifted by their max
+          const int n = min(bs, w.L - c * bs);
+          const float* x = sg + cl * bs;
+          float m = -INFINITY;
+          for (int t = 0; t < n; ++t) m = fmaxf(m, x[t]);
+          float z = 0.f;
+          for (int t = 0; t < n; ++t) z += expf(x[t] - m);
+          key = f2key(m + logf(z));
+        }
+        keys[c] = key;
+        if (c >= w.lo && c < w.hi) atomicAdd(&lh[key >> 20], 1u);
       }
     }
     __syncthreads();

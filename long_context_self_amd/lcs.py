@@ -61,6 +61,14 @@ SIGNATURES = {
                                     _f, _p, _p, _p, _sz, _p]),
     "lcs_sparse_draft_attn_noalloc": (_i32, [_KV, _p, _i32, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _i32,
                                             _p, _f, _p, _p, _p]),
+    "lcs_select_topk_blocks": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p,
+                                     _i32, _p, _sz, _p]),
+    "lcs_nsa_compress": (_i32, [_KV, _i32, _p, _i32, _i32, _i32, _p, _p, _i32, _p]),
+    "lcs_nsa_plan_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "lcs_nsa_plan": (_i32, [_KV, _i32, _i32, _p, _p, _i32, _i32, _p, _sz, _p]),
+    "lcs_nsa_workspace_bytes": (_sz, [_i32, _i32, _i32, _KV, _i32, _i32, _i32, _i32]),
+    "lcs_nsa_attn": (_i32, [_KV, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _i32, _i32, _p, _sz, _i32, _p, _p, _i32,
+                           _p, _p, _f, _p, _p, _p, _sz, _p]),
     "lcs_last_error": (ctypes.c_char_p, []),
     "lcs_version": (ctypes.c_char_p, []),
 }
@@ -332,6 +340,93 @@ def sparse_draft_attn(kv: PagedKV, q: torch.Tensor, mode: str, indices: torch.Te
                                         _ptr(indices), _ptr(counts), cap, _ptr(tail_begin),
                                         _ptr(tail_len), max_tail_len, _ptr(tail_mask), scale,
                                         _ptr(out), _ptr(lse), ws.data_ptr(), ws.numel(), _stream()))
+    return out, lse
+
+
+BLOCK_SCORES = {"max": 0, "lse": 1}
+GROUP_MODES = {"exact": 0, "approximate": 1}
+
+
+def select_topk_blocks(logits: torch.Tensor, prefix_len: torch.Tensor, max_prefix_len: int, Hkv: int,
+                       block_score: str, top_k: int, n_sink: int, n_recent: int, block_size: int,
+                       cap: Optional[int] = None, indices: Optional[torch.Tensor] = None,
+                       counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """lcs_select_topk_blocks: per-KV-head block sets scored by "max" or "lse".
+    Returns (indices [B][Hkv][cap], counts [B][Hkv])."""
+    B, Hq = logits.shape[0], logits.shape[1]
+    dev = logits.device
+    if cap is None:
+        nb = -(-max_prefix_len // block_size)
+        cap = max(1, min(nb, -(-n_sink // block_size) + top_k + -(-n_recent // block_size) + 1))
+    if indices is None:
+        indices = torch.full((B, Hkv, cap), -1, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+    need = load().lcs_select_workspace_bytes(B, Hq, Hkv, SET_MODES["block"], max_prefix_len, block_size)
+    ws = _workspace(need, dev, workspace)
+    _check(load().lcs_select_topk_blocks(_ptr(logits), logits.stride(2), B, Hq, Hkv, _ptr(prefix_len),
+                                         max_prefix_len, BLOCK_SCORES[block_score], top_k, n_sink, n_recent,
+                                         block_size, _ptr(indices), _ptr(counts), cap, ws.data_ptr(), ws.numel(),
+                                         _stream()))
+    return indices, counts
+
+
+def nsa_compress(kv: PagedKV, prefix_len: torch.Tensor, max_prefix_len: int, cmp_len: int, cmp_stride: int,
+                 max_cmp: int, k_cmp: Optional[torch.Tensor] = None, v_cmp: Optional[torch.Tensor] = None):
+    """lcs_nsa_compress.  Returns the compressed cache (k_cmp, v_cmp) bf16 [B][Hkv][max_cmp][d]."""
+    B = prefix_len.shape[0]
+    _, Hkv, _, d = kv.k.shape
+    dev = kv.k.device
+    if k_cmp is None:
+        k_cmp = torch.empty((B, Hkv, max_cmp, d), dtype=torch.bfloat16, device=dev)
+    if v_cmp is None:
+        v_cmp = torch.empty((B, Hkv, max_cmp, d), dtype=torch.bfloat16, device=dev)
+    desc = kv.desc()
+    _check(load().lcs_nsa_compress(ctypes.byref(desc), B, _ptr(prefix_len), max_prefix_len, cmp_len, cmp_stride,
+                                   _ptr(k_cmp), _ptr(v_cmp), max_cmp, _stream()))
+    return k_cmp, v_cmp
+
+
+def nsa_plan(kv: PagedKV, indices: torch.Tensor, counts: torch.Tensor, group: str = "exact",
+             plan: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """lcs_nsa_plan: block-union plan of indices [B][n_q][Hkv][cap].  Returns the plan buffer."""
+    B, n_q, Hkv, cap = indices.shape
+    need = load().lcs_nsa_plan_bytes(B, n_q, Hkv, cap)
+    if plan is None or plan.numel() < need:
+        plan = torch.empty(max(need, 256), dtype=torch.uint8, device=indices.device)
+    desc = kv.desc()
+    _check(load().lcs_nsa_plan(ctypes.byref(desc), B, n_q, _ptr(indices), _ptr(counts), cap, GROUP_MODES[group],
+                               _ptr(plan), plan.numel(), _stream()))
+    return plan
+
+
+def nsa_workspace_bytes(kv: PagedKV, B: int, n_q: int, Hq: int, cap: int, max_tail_len: int, max_cmp: int,
+                        window: int) -> int:
+    d = kv.desc()
+    return load().lcs_nsa_workspace_bytes(B, n_q, Hq, ctypes.byref(d), cap, max_tail_len, max_cmp, window)
+
+
+def nsa_attn(kv: PagedKV, k_cmp: torch.Tensor, v_cmp: torch.Tensor, cmp_len: int, cmp_stride: int, window: int,
+             q: torch.Tensor, plan: torch.Tensor, cap: int, tail_begin: torch.Tensor, tail_len: torch.Tensor,
+             max_tail_len: int, gates: torch.Tensor, scale: float, tail_mask: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None):
+    """lcs_nsa_attn: gated compression / selection / window attention of q bf16 [B][n_q][Hq][d].
+    Returns (out [B][n_q][Hq][d], lse [B][n_q][Hq][3])."""
+    B, n_q, Hq, d = q.shape
+    dev = q.device
+    max_cmp = k_cmp.shape[2]
+    if out is None:
+        out = torch.empty((B, n_q, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, n_q, Hq, 3), dtype=torch.float32, device=dev)
+    desc = kv.desc()
+    need = load().lcs_nsa_workspace_bytes(B, n_q, Hq, ctypes.byref(desc), cap, max_tail_len, max_cmp, window)
+    ws = _workspace(need, dev, workspace)
+    _check(load().lcs_nsa_attn(ctypes.byref(desc), _ptr(k_cmp), _ptr(v_cmp), max_cmp, cmp_len, cmp_stride, window,
+                               _ptr(q), B, n_q, Hq, _ptr(plan), plan.numel(), cap, _ptr(tail_begin), _ptr(tail_len),
+                               max_tail_len, _ptr(tail_mask), _ptr(gates), scale, _ptr(out), _ptr(lse),
+                               ws.data_ptr(), ws.numel(), _stream()))
     return out, lse
 
 

@@ -84,6 +84,12 @@ class Config:
     blocks_per_row: int = 0
     core_blocks: int = 0
     tree_branches: int = 0  # >0: n_q rows form this many root chains
+    # NSA branches (SSV sparse verification): compression block length and stride,
+    # sliding-window length.  The pages name the branches without sizes; these are
+    # NSA's published sizes (blocks of 32 at stride 16, a 512-token window).
+    cmp_len: int = 0
+    cmp_stride: int = 0
+    window: int = 0
 
     @property
     def G(self) -> int:
@@ -116,7 +122,8 @@ CONFIGS: Dict[str, Config] = {
     "nsa_16k": Config("nsa_16k", B=2, Hq=32, Hkv=8, d=128, L=16384,
                       page_size=64, n_q=8, n_draft=0, top_k=16, n_sink=0,
                       n_recent=0, mode="block", crit_frac=0.0,
-                      blocks_per_row=16, core_blocks=10, tree_branches=2),
+                      blocks_per_row=16, core_blocks=10, tree_branches=2,
+                      cmp_len=32, cmp_stride=16, window=512),
     # Long-context stress: B8 at 128K, draft 8, 4096 + 4 + 64.
     "stress_128k": Config("stress_128k", B=8, Hq=32, Hkv=8, d=128, L=131072,
                           page_size=16, n_q=9, n_draft=8, top_k=4096, n_sink=4,
@@ -280,6 +287,19 @@ def make_block_sets(cfg: Config, n_blocks: int, seed: int = 0) -> np.ndarray:
                 p = ids[core + i * priv: core + (i + 1) * priv]
                 out[b, i, g] = np.sort(np.concatenate([c, p]))
     return out
+
+
+def make_gates(cfg: Config, n_rows: int, seed: int = 0) -> np.ndarray:
+    """float32 [B][n_rows][Hq][3] branch gates, uniform in [0, 1) (NSA's gates are sigmoids)."""
+    return _rng(seed, 9).uniform(0.0, 1.0, (cfg.B, n_rows, cfg.Hq, 3)).astype(np.float32)
+
+
+def make_compressed_cache(cfg: Config, max_cmp: int, seed: int = 0):
+    """bf16 bits [B][Hkv][max_cmp][d] x 2: stand-in compressed keys and values, N(0, 1)."""
+    r = _rng(seed, 10)
+    shape = (cfg.B, cfg.Hkv, max_cmp, cfg.d)
+    return (f32_to_bf16_bits(r.standard_normal(shape, dtype=np.float32)),
+            f32_to_bf16_bits(r.standard_normal(shape, dtype=np.float32)))
 
 
 def drift_critical(cfg: Config, kv: PagedKV, frac: float, seed: int, it: int) -> List[List[np.ndarray]]:

@@ -1,0 +1,218 @@
+"""GPU parity of the NSA calls (lcs_nsa_compress, lcs_nsa_plan, lcs_nsa_attn) and of
+block selection by log-sum-exp (lcs_select_topk_blocks) against the fp64 oracle.
+
+* compression: every compressed element within one bf16 step of the oracle's (the
+  kernel sums in fp32 before rounding; the oracle rounds the exact mean), almost all
+  equal; rows past the sequence's complete blocks zero;
+* gated three-branch attention on stand-in compressed caches drawn by the generator:
+  exact and approximate grouping, tree masks, ragged prefixes, windows shorter and
+  longer than the prefix, several row chunks, head dims 64 and 128: out within 1e-2
+  max-abs, per-branch lse within 1e-3;
+* compression then attention end to end against the oracle's own compression;
+* a plan built once serves later calls on other caches (the reuse layers);
+* block log-sum-exp selection: >= 99 % overlap with the oracle on the GPU's logits,
+  and every swap at the boundary is a near-tie of the fp64 block scores.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from long_context_self_amd import synth
+from oracle import attention as oa
+from oracle import nsa
+from oracle import select as osel
+
+from gpu_helpers import bf16_dev, i32_dev, kv_dev, require_gpu, scale_for, u64_dev
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+def nsa_case(cfg, seed, lens, max_cmp=None):
+    kv = synth.make_paged_kv(cfg, seed=seed, lens=lens, extra_tokens=cfg.n_q)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=seed)
+    nblk = max(max(lens) // cfg.page_size, cfg.core_blocks + cfg.n_q * (cfg.blocks_per_row - cfg.core_blocks))
+    sets = synth.make_block_sets(cfg, nblk, seed=seed)
+    cnt = np.full(sets.shape[:3], sets.shape[3], dtype=np.int32)
+    tm = np.stack([synth.tree_tail_masks(cfg.n_q, cfg.tree_branches)] * cfg.B)
+    gates = synth.make_gates(cfg, cfg.n_q, seed=seed)
+    if max_cmp is None:
+        max_cmp = max(1, nsa.n_compressed(max(lens), cfg.cmp_len, cfg.cmp_stride))
+    kc, vc = synth.make_compressed_cache(cfg, max_cmp, seed=seed)
+    return kv, q, sets, cnt, tm, gates, kc, vc
+
+
+def gpu_nsa(cfg, kv, q, sets, cnt, tm, gates, kc, vc, window, group="exact", dkv=None):
+    torch, lcs = require_gpu()
+    dkv = dkv if dkv is not None else kv_dev(kv, torch, lcs)
+    plan = lcs.nsa_plan(dkv, i32_dev(sets, torch), i32_dev(cnt, torch), group)
+    B, n_q = q.shape[0], q.shape[1]
+    out = torch.full((B, n_q, cfg.Hq, cfg.d), float("nan"), device="cuda")
+    lse = torch.full((B, n_q, cfg.Hq, 3), float("nan"), device="cuda")
+    lcs.nsa_attn(dkv, bf16_dev(kc, torch), bf16_dev(vc, torch), cfg.cmp_len, cfg.cmp_stride, window,
+                 bf16_dev(q, torch), plan, sets.shape[3], i32_dev(kv.prefix_len, torch),
+                 i32_dev(np.full(B, n_q), torch), n_q, torch.from_numpy(gates).cuda(), scale_for(cfg.d),
+                 tail_mask=u64_dev(tm, torch), out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def check_nsa(cfg, kv, q, sets, cnt, tm, gates, kc, vc, window, group="exact"):
+    out, lse = gpu_nsa(cfg, kv, q, sets, cnt, tm, gates, kc, vc, window, group)
+    o_out, o_lse = nsa.nsa_attn(q, kv.k, kv.v, kv.block_table, cfg.page_size, kc, vc, cfg.cmp_len, cfg.cmp_stride,
+                                sets, cnt, kv.prefix_len, np.full(cfg.B, cfg.n_q), window, gates, scale_for(cfg.d),
+                                tail_mask=tm, group=group)
+    assert np.isfinite(out).all()
+    err = float(np.max(np.abs(out - o_out)))
+    assert err <= OUT_TOL, f"max-abs err {err}"
+    fin = np.isfinite(o_lse)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert float(np.max(np.abs(lse[fin] - o_lse[fin]), initial=0.0)) <= LSE_TOL
+    return err
+
+
+@pytest.mark.parametrize("d,cmp_len,cmp_stride,lens", [(128, 32, 16, [4096, 3001]), (128, 64, 64, [2048, 2111]),
+                                                      (64, 16, 8, [1000, 777])])
+def test_compress_matches_oracle(d, cmp_len, cmp_stride, lens):
+    torch, lcs = require_gpu()
+    cfg = synth.CONFIGS["nsa_16k"].with_(d=d, Hq=8, Hkv=4, cmp_len=cmp_len, cmp_stride=cmp_stride)
+    kv = synth.make_paged_kv(cfg, seed=41, lens=lens, extra_tokens=cfg.n_q)
+    max_cmp = nsa.n_compressed(max(lens), cmp_len, cmp_stride) + 3      # rows past the last block
+    kc, vc = lcs.nsa_compress(kv_dev(kv, torch, lcs), i32_dev(kv.prefix_len, torch), max(lens), cmp_len,
+                              cmp_stride, max_cmp)
+    torch.cuda.synchronize()
+    g_k = kc.view(torch.int16).cpu().numpy().view(np.uint16)
+    g_v = vc.view(torch.int16).cpu().numpy().view(np.uint16)
+    o_k, o_v = nsa.compress(kv.k, kv.v, kv.block_table, kv.prefix_len, cfg.page_size, cmp_len, cmp_stride, max_cmp)
+    for g_, o_ in ((g_k, o_k), (g_v, o_v)):
+        gf = synth.bf16_bits_to_f32(g_).astype(np.float64)
+        of = synth.bf16_bits_to_f32(o_).astype(np.float64)
+        step = np.maximum(np.abs(of), 1e-30) * 2.0 ** -7            # one bf16 step at that magnitude
+        assert np.all(np.abs(gf - of) <= step)
+        assert np.mean(g_ == o_) >= 0.999
+        for b, L in enumerate(lens):
+            assert np.all(g_[b, :, nsa.n_compressed(L, cmp_len, cmp_stride):] == 0)
+
+
+@pytest.mark.parametrize("group", ["exact", "approximate"])
+@pytest.mark.parametrize("window", [0, 100, 512, 100000])
+def test_nsa_attn_reduced_nsa_16k(group, window):
+    cfg = synth.CONFIGS["nsa_16k"].with_(L=4096)
+    kv, q, sets, cnt, tm, gates, kc, vc = nsa_case(cfg, 42, [4096, 3333])
+    err = check_nsa(cfg, kv, q, sets, cnt, tm, gates, kc, vc, window, group)
+    print(f"group {group} window {window}: max-abs err {err:.2e}")
+
+
+@pytest.mark.parametrize("d,G,n_q,branches", [(64, 4, 8, 2), (128, 1, 4, 1), (128, 8, 16, 4), (128, 4, 16, 2)])
+def test_nsa_attn_shapes(d, G, n_q, branches):
+    """Head dim 64, one query head per KV head, and 64 / 128 q-rows per group (two and
+    three row chunks)."""
+    cfg = synth.CONFIGS["nsa_16k"].with_(L=2048, d=d, Hkv=2, Hq=2 * G, n_q=n_q, tree_branches=branches,
+                                         blocks_per_row=6, core_blocks=3)
+    kv, q, sets, cnt, tm, gates, kc, vc = nsa_case(cfg, 43, [2048, 1500])
+    check_nsa(cfg, kv, q, sets, cnt, tm, gates, kc, vc, 300)
+
+
+def test_nsa_attn_empty_branches():
+    """Prefixes shorter than one compressed block, empty block lists and no window: those
+    branches contribute nothing and report lse = -inf; the tail still counts."""
+    cfg = synth.CONFIGS["nsa_16k"].with_(L=2048, Hkv=2, Hq=8)
+    kv, q, sets, cnt, tm, gates, kc, vc = nsa_case(cfg, 44, [20, 2048], max_cmp=128)
+    cnt = cnt.copy()
+    cnt[0] = 0
+    check_nsa(cfg, kv, q, sets, cnt, tm, gates, kc, vc, 0)
+
+
+def test_nsa_compress_then_attend_end_to_end():
+    torch, lcs = require_gpu()
+    cfg = synth.CONFIGS["nsa_16k"].with_(L=4096, Hkv=4, Hq=16)
+    kv, q, sets, cnt, tm, gates, _, _ = nsa_case(cfg, 45, [4096, 2500])
+    max_cmp = nsa.n_compressed(4096, cfg.cmp_len, cfg.cmp_stride)
+    dkv = kv_dev(kv, torch, lcs)
+    kc, vc = lcs.nsa_compress(dkv, i32_dev(kv.prefix_len, torch), 4096, cfg.cmp_len, cfg.cmp_stride, max_cmp)
+    plan = lcs.nsa_plan(dkv, i32_dev(sets, torch), i32_dev(cnt, torch))
+    out, lse = lcs.nsa_attn(dkv, kc, vc, cfg.cmp_len, cfg.cmp_stride, cfg.window, bf16_dev(q, torch), plan,
+                            sets.shape[3], i32_dev(kv.prefix_len, torch), i32_dev(np.full(cfg.B, cfg.n_q), torch),
+                            cfg.n_q, torch.from_numpy(gates).cuda(), scale_for(cfg.d), tail_mask=u64_dev(tm, torch))
+    torch.cuda.synchronize()
+    o_kc, o_vc = nsa.compress(kv.k, kv.v, kv.block_table, kv.prefix_len, cfg.page_size, cfg.cmp_len,
+                              cfg.cmp_stride, max_cmp)
+    o_out, _ = nsa.nsa_attn(q, kv.k, kv.v, kv.block_table, cfg.page_size, o_kc, o_vc, cfg.cmp_len, cfg.cmp_stride,
+                            sets, cnt, kv.prefix_len, np.full(cfg.B, cfg.n_q), cfg.window, gates, scale_for(cfg.d),
+                            tail_mask=tm)
+    assert float(np.max(np.abs(out.cpu().numpy() - o_out))) <= OUT_TOL
+
+
+def test_reuse_layers_share_one_plan():
+    """The refresh layer derives the plan; two reuse layers with their own caches run the
+    fused attention on that plan alone and match the oracle on their own caches."""
+    torch, lcs = require_gpu()
+    cfg = synth.CONFIGS["nsa_16k"].with_(L=2048, Hkv=4, Hq=16)
+    kv, q, sets, cnt, tm, gates, kc, vc = nsa_case(cfg, 46, [2048, 1800])
+    dkv = kv_dev(kv, torch, lcs)
+    plan = lcs.nsa_plan(dkv, i32_dev(sets, torch), i32_dev(cnt, torch))
+    for layer in range(2):
+        # another layer: its own cache and page table; the plan holds logical block ids
+        kv_l = synth.make_paged_kv(cfg, seed=100 + layer, lens=[2048, 1800], extra_tokens=cfg.n_q)
+        d_l = kv_dev(kv_l, torch, lcs)
+        out, _ = lcs.nsa_attn(d_l, bf16_dev(kc, torch), bf16_dev(vc, torch), cfg.cmp_len, cfg.cmp_stride, 256,
+                              bf16_dev(q, torch), plan, sets.shape[3], i32_dev(kv.prefix_len, torch),
+                              i32_dev(np.full(cfg.B, cfg.n_q), torch), cfg.n_q, torch.from_numpy(gates).cuda(),
+                              scale_for(cfg.d), tail_mask=u64_dev(tm, torch))
+        torch.cuda.synchronize()
+        o_out, _ = nsa.nsa_attn(q, kv_l.k, kv_l.v, kv_l.block_table, cfg.page_size, kc, vc, cfg.cmp_len,
+                                cfg.cmp_stride, sets, cnt, kv.prefix_len, np.full(cfg.B, cfg.n_q), 256, gates,
+                                scale_for(cfg.d), tail_mask=tm)
+        assert float(np.max(np.abs(out.cpu().numpy() - o_out))) <= OUT_TOL
+
+
+def test_nsa_full_size_nsa_16k():
+    """The SSV workload at full size: B = 2, 16K prefixes, 8 tree rows x 16 blocks of 64."""
+    cfg = synth.CONFIGS["nsa_16k"]
+    kv, q, sets, cnt, tm, gates, kc, vc = nsa_case(cfg, 47, [cfg.L, cfg.L - 777])
+    for group in ("exact", "approximate"):
+        check_nsa(cfg, kv, q, sets, cnt, tm, gates, kc, vc, cfg.window, group)
+
+
+@pytest.mark.parametrize("bs,L,B", [(64, 16384, 2), (16, 5000, 3), (512, 9000, 1)])
+def test_block_lse_selection(bs, L, B):
+    torch, lcs = require_gpu()
+    cfg = synth.CONFIGS["llama8b_32k"].with_(L=L, B=B)
+    lens = [L - 333 * b for b in range(B)]
+    kv = synth.make_paged_kv(cfg, seed=48, lens=lens)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=48)
+    dkv = kv_dev(kv, torch, lcs)
+    pl = i32_dev(kv.prefix_len, torch)
+    _, logits, _ = lcs.verify_attn(dkv, bf16_dev(q, torch), pl, L, scale_for(cfg.d), cfg.collect_rows)
+    top_k, ns, nr = 24, 70, 200
+    idx, cnt = lcs.select_topk_blocks(logits, pl, L, cfg.Hkv, "lse", top_k, ns, nr, bs)
+    # max aggregation through this entry point equals lcs_select_topk in block mode
+    idx_m, cnt_m = lcs.select_topk_blocks(logits, pl, L, cfg.Hkv, "max", top_k, ns, nr, bs)
+    ref_i, ref_c = lcs.select_topk(logits, pl, L, cfg.Hkv, "block", top_k, ns, nr, block_size=bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(cnt_m.cpu().numpy(), ref_c.cpu().numpy())
+    assert np.array_equal(idx_m.cpu().numpy(), ref_i.cpu().numpy())
+    g_lg = logits.cpu().numpy()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    ref = osel.select(g_lg, kv.prefix_len, cfg.Hkv, "block", top_k, ns, nr, block_size=bs, block_agg="lse")
+    G = cfg.G
+    for b in range(B):
+        Lb = int(kv.prefix_len[b])
+        for g in range(cfg.Hkv):
+            got = idx[b, g, :cnt[b, g]]
+            want = ref[b][g]
+            assert cnt[b, g] == want.size
+            common = np.intersect1d(got, want).size
+            assert common >= 0.99 * want.size
+            if common < want.size:
+                # every disagreement is a near-tie of the fp64 block scores at the boundary
+                sig = osel.scores_f64(g_lg, b, Lb, list(range(g * G, (g + 1) * G)))
+                beta = osel.block_scores_lse(sig, Lb, bs)
+                _, sb, rb = osel.block_window(Lb, bs, ns, nr)
+                pool_keep = want[(want >= sb) & (want < rb)]
+                gap = np.abs(beta[np.setxor1d(got, want)] - np.min(beta[pool_keep]))
+                assert np.all(gap <= 1e-4 * max(1.0, float(np.max(np.abs(beta)))))
+
