@@ -228,6 +228,41 @@ lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, in
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Selection handed to the draft as physical cache slots.
+ *
+ * Vegas page, "What carries the argument": the selector's output feeds the
+ * drafting phase directly.  These two calls hand the set over as physical
+ * slots of the paged cache, slot = block_table[b][p / page_size] * page_size
+ * + p % page_size, so that the draft reads each selected K/V row without its
+ * own block-table lookup (only the tail slots still go through the table).
+ *
+ * lcs_select_topk_physical: lcs_select_topk for SHARED and PER_KV_HEAD sets
+ * (BLOCK returns LCS_E_UNSUPPORTED) that writes, in the same ascending order of
+ * positions, the physical slot of each selected position through kv's block
+ * table (kv->block_table [B][max_pages]; only the table and page geometry are
+ * read).  Requires max_prefix_len <= max_pages * page_size and
+ * num_pages * page_size < 2^31.  Workspace, counts and errors as lcs_select_topk.
+ *
+ * lcs_sparse_draft_attn_physical: lcs_sparse_draft_attn for SHARED and
+ * PER_KV_HEAD lists whose entries are such physical slots (the result is that
+ * of lcs_sparse_draft_attn on the positions they stand for, bit for bit).
+ * Workspace as lcs_sparse_workspace_bytes.  A slot whose page is outside the
+ * cache is skipped.
+ * ------------------------------------------------------------------------- */
+lcs_status lcs_select_topk_physical(const float* logits, int64_t logits_ld, int32_t B, int32_t Hq, int32_t Hkv,
+                                    const int32_t* prefix_len, int32_t max_prefix_len, lcs_set_mode mode,
+                                    int32_t top_k, int32_t n_sink, int32_t n_recent, const lcs_paged_kv* kv,
+                                    int32_t* indices, int32_t* counts, int32_t cap, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+lcs_status lcs_sparse_draft_attn_physical(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q,
+                                          int32_t Hq, lcs_set_mode mode, const int32_t* indices,
+                                          const int32_t* counts, int32_t cap, const int32_t* tail_begin,
+                                          const int32_t* tail_len, int32_t max_tail_len, const uint64_t* tail_mask,
+                                          float scale, float* out, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Block selection with a choice of block score.
  *
  * SSV page, Figure 3 overview (NSA token selection picks hardware-aligned

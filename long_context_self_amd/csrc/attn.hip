@@ -325,6 +325,7 @@ __device__ __forceinline__ void meta_stage_b(const AttnArgs& a, const SeqInfo& s
     int pos, jt;
     uint64_t v;
     slot_pos<MODE>(a, si, wbase, w1, tok, (MODE == MODE_LIST_SHARED) ? sidx[tok] : 0, pos, jt, v);
+    if (MODE == MODE_LIST_SHARED && a.phys && jt < 0) continue;   // a listed physical slot needs no lookup
     const int pi = pos >> a.lg_page;
     const bool ok = pos >= 0 && pi < a.max_pages;
     dma4(a.bt + (size_t)b * a.max_pages + (ok ? pi : 0), spg + 64 * r);
@@ -355,6 +356,9 @@ __device__ __forceinline__ void meta_stage_c(const AttnArgs& a, const SeqInfo& s
     int row = -1;
     if (MODE == MODE_NSA && si.br == BR_CMP) {
       if (pos >= 0) row = si.cbase + pos;        // compressed cache, not paged
+    } else if (MODE == MODE_LIST_SHARED && a.phys && jt < 0) {
+      const int pg = pos >> a.lg_page;           // a listed entry is a physical slot
+      if (pos >= 0 && pg < a.num_pages) row = ((pg * a.Hkv + g) << a.lg_page) | (pos & (P - 1));
     } else if (pos >= 0 && (pos >> a.lg_page) < a.max_pages && (unsigned)page[r] < (unsigned)a.num_pages) {
       row = ((page[r] * a.Hkv + g) << a.lg_page) | (pos & (P - 1));
     }
@@ -698,8 +702,11 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   }
   // Prologue: window-0 metadata DMAs go out together with the Q loads, so the block-table
   // round trip overlaps the Q fetch and the Q -> LDS copy.
+  // Physical-slot lists need block-table entries for the tail slots only, whose
+  // positions do not depend on the list: those go out together with the list DMA.
   if (MODE == MODE_LIST_SHARED) {
     if (w0 < w1s) meta_stage_a<MODE>(a, si, w0, lane, wm, 0);
+    if (a.phys && w0 < w1) meta_stage_b<MODE>(a, si, b, w0, w1, lane, wm, 0);
   } else if (w0 < w1) {
     meta_stage_b<MODE>(a, si, b, w0, w1, lane, wm, 0);
   }
@@ -720,7 +727,7 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
     }
   }
   wait_vm<0>();
-  if (MODE == MODE_LIST_SHARED && w0 < w1) meta_stage_b<MODE>(a, si, b, w0, w1, lane, wm, 0);
+  if (MODE == MODE_LIST_SHARED && !a.phys && w0 < w1) meta_stage_b<MODE>(a, si, b, w0, w1, lane, wm, 0);
 #pragma unroll
   for (int u = 0; u < kQPer; ++u) {
     const int e = tid + 256 * u;
@@ -730,7 +737,7 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   }
   // dense and block modes have the first window's block-table entries already: their
   // first two K/V steps go out before the Q barrier, so the Q staging overlaps them
-  if (MODE != MODE_LIST_SHARED && w0 < w1) {
+  if ((MODE != MODE_LIST_SHARED || a.phys) && w0 < w1) {
     meta_stage_c<MODE>(a, si, g, w0, w1, colmask, lane, wm, 0);
     wait_lgkm0();
     step_dma<D>(kb, vb, wm.row[0], ring, lane, x, j);
@@ -759,7 +766,7 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   }
 
   if (w0 < w1) {
-    if (MODE == MODE_LIST_SHARED) {
+    if (MODE == MODE_LIST_SHARED && !a.phys) {
       wait_vm<0>();
       meta_stage_c<MODE>(a, si, g, w0, w1, colmask, lane, wm, 0);
       wait_lgkm0();

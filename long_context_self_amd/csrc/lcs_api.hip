@@ -287,7 +287,8 @@ lcs_status select_impl(const float* logits, int64_t logits_ld, int32_t n_rows, i
                        int32_t n_q, uint64_t rows_mask, int32_t B, int32_t Hq, int32_t Hkv,
                        const int32_t* prefix_len, int32_t max_prefix_len, lcs_set_mode mode, int32_t top_k,
                        int32_t n_sink, int32_t n_recent, int32_t block_size, int32_t* indices, int32_t* counts,
-                       int32_t cap, void* workspace, size_t workspace_bytes, void* stream, int32_t block_lse = 0) {
+                       int32_t cap, void* workspace, size_t workspace_bytes, void* stream, int32_t block_lse = 0,
+                       const lcs_paged_kv* phys_kv = nullptr) {
   if (Hkv < 1) return fail(LCS_E_SHAPE, "Hkv must be >= 1");
   lcs_status st = check_heads(Hq, Hkv);
   if (st != LCS_OK) return st;
@@ -342,6 +343,18 @@ lcs_status select_impl(const float* logits, int64_t logits_ld, int32_t n_rows, i
   a.lg_bs = (mode == LCS_SET_BLOCK) ? ilog2(block_size) : 0;
   a.vec4 = (aligned(logits, 16) && logits_ld % 4 == 0) ? 1 : 0;
   a.block_lse = block_lse;
+  if (phys_kv != nullptr) {
+    // physical slots: page * page_size + slot through the sequence's block table
+    if (mode == LCS_SET_BLOCK) return fail(LCS_E_UNSUPPORTED, "physical slots are for token sets, not blocks");
+    if ((st = check_kv(phys_kv)) != LCS_OK) return st;
+    if ((long long)max_prefix_len > (long long)phys_kv->max_pages * phys_kv->page_size)
+      return fail(LCS_E_SHAPE, "max_prefix_len exceeds max_pages * page_size");
+    if ((long long)phys_kv->num_pages * phys_kv->page_size >= (1ll << 31))
+      return fail(LCS_E_UNSUPPORTED, "num_pages * page_size must stay below 2^31 slots");
+    a.bt = phys_kv->block_table;
+    a.max_pages = phys_kv->max_pages;
+    a.lg_page = ilog2(phys_kv->page_size);
+  }
   a.indices = indices;
   a.counts = counts;
   a.cap = cap;
@@ -360,6 +373,17 @@ lcs_status lcs_select_topk(const float* logits, int64_t logits_ld, int32_t B, in
   return select_impl(logits, logits_ld, 2, lcs::SCORE_LOGIT_SUM, nullptr, 0, 0, B, Hq, Hkv, prefix_len,
                      max_prefix_len, mode, top_k, n_sink, n_recent, block_size, indices, counts, cap, workspace,
                      workspace_bytes, stream);
+}
+
+lcs_status lcs_select_topk_physical(const float* logits, int64_t logits_ld, int32_t B, int32_t Hq, int32_t Hkv,
+                                    const int32_t* prefix_len, int32_t max_prefix_len, lcs_set_mode mode,
+                                    int32_t top_k, int32_t n_sink, int32_t n_recent, const lcs_paged_kv* kv,
+                                    int32_t* indices, int32_t* counts, int32_t cap, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (kv == nullptr) return fail(LCS_E_ARG, "kv is NULL");
+  return select_impl(logits, logits_ld, 2, lcs::SCORE_LOGIT_SUM, nullptr, 0, 0, B, Hq, Hkv, prefix_len,
+                     max_prefix_len, mode, top_k, n_sink, n_recent, 0, indices, counts, cap, workspace,
+                     workspace_bytes, stream, 0, kv);
 }
 
 lcs_status lcs_select_topk_blocks(const float* logits, int64_t logits_ld, int32_t B, int32_t Hq, int32_t Hkv,
@@ -426,7 +450,7 @@ lcs_status sparse_impl(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t
                        lcs_set_mode mode, const int32_t* indices, const int32_t* counts, int32_t cap,
                        const int32_t* tail_begin, const int32_t* tail_len, int32_t max_tail_len,
                        const uint64_t* tail_mask, float scale, float* out, float* lse, void* workspace,
-                       size_t workspace_bytes, void* stream, bool use_scratch) {
+                       size_t workspace_bytes, void* stream, bool use_scratch, bool phys = false) {
   lcs_status st = check_kv(kv);
   if (st != LCS_OK) return st;
   if ((st = check_heads(Hq, kv->Hkv)) != LCS_OK) return st;
@@ -483,6 +507,7 @@ lcs_status sparse_impl(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t
   a.max_tail_len = max_tail_len;
   a.tail_begin = tail_begin;
   a.tail_len = tail_len;
+  a.phys = phys ? 1 : 0;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = out;
@@ -501,6 +526,19 @@ lcs_status lcs_sparse_draft_attn(const lcs_paged_kv* kv, const void* q, int32_t 
                                  float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return sparse_impl(kv, q, B, n_q, Hq, mode, indices, counts, cap, tail_begin, tail_len, max_tail_len, tail_mask,
                      scale, out, lse, workspace, workspace_bytes, stream, false);
+}
+
+lcs_status lcs_sparse_draft_attn_physical(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q,
+                                          int32_t Hq, lcs_set_mode mode, const int32_t* indices,
+                                          const int32_t* counts, int32_t cap, const int32_t* tail_begin,
+                                          const int32_t* tail_len, int32_t max_tail_len, const uint64_t* tail_mask,
+                                          float scale, float* out, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (mode == LCS_SET_BLOCK) return fail(LCS_E_UNSUPPORTED, "physical slots are for token sets, not blocks");
+  if (kv != nullptr && (long long)kv->num_pages * kv->page_size >= (1ll << 31))
+    return fail(LCS_E_UNSUPPORTED, "num_pages * page_size must stay below 2^31 slots");
+  return sparse_impl(kv, q, B, n_q, Hq, mode, indices, counts, cap, tail_begin, tail_len, max_tail_len, tail_mask,
+                     scale, out, lse, workspace, workspace_bytes, stream, false, true);
 }
 
 lcs_status lcs_sparse_draft_attn_noalloc(const lcs_paged_kv* kv, const void* q, int32_t B, int32_t n_q,

@@ -49,6 +49,7 @@ struct AttnArgs {
   const int32_t* tail_begin;
   const int32_t* tail_len;
   int32_t max_tail_len;   // tail_len values above it are clamped
+  int32_t phys;           // token lists hold physical slots (page * page_size + slot), not positions
   // block-union plan (workspace)
   const int32_t* ublk;
   const uint64_t* umask;
@@ -150,6 +151,8 @@ struct SelArgs {
   int32_t max_len;
   int32_t top_k, n_sink, n_recent, lg_bs, vec4;
   int32_t block_lse;       // block mode: score a block by log-sum-exp instead of max
+  const int32_t* bt;       // non-null: emit physical slots bt[b][p / P] * P + p % P, not positions
+  int32_t max_pages, lg_page;
   int32_t* indices;
   int32_t* counts;
   int32_t cap;

@@ -332,6 +332,13 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
     }
 }
 
+// The id written for item it of sequence b: the position, or its physical slot.
+__device__ __forceinline__ int32_t emit_id(const SelArgs& a, int b, int it) {
+  if (a.bt == nullptr) return it;
+  const int32_t page = a.bt[(size_t)b * a.max_pages + (it >> a.lg_page)];
+  return (page << a.lg_page) | (it & ((1 << a.lg_page) - 1));
+}
+
 constexpr int kFinLDS = 8192;      // candidates a workgroup holds in LDS
 constexpr int kFinIPT = kItemChunk / 1024;   // consecutive items per thread in finish
 
@@ -350,7 +357,7 @@ __global__ void __launch_bounds__(1024) finish_kernel(SelArgs a) {
   int32_t* out = a.indices + (size_t)set * a.cap;
   if (w.all) {
     for (int it = c0 + tid; it < min(w.n, c0 + kItemChunk); it += 1024)
-      if (it < a.cap) out[it] = it;
+      if (it < a.cap) out[it] = emit_id(a, b, it);
     if (blockIdx.x == 0 && tid == 0) a.counts[set] = min(w.n, a.cap);
     return;
   }
@@ -464,12 +471,12 @@ __global__ void __launch_bounds__(1024) finish_kernel(SelArgs a) {
     const int it = t0 + e;
     if (it >= w.n) continue;
     if (it < w.lo) {
-      if (it < a.cap) out[it] = it;
+      if (it < a.cap) out[it] = emit_id(a, b, it);
     } else if (it >= w.hi) {
       const int o = w.lo + K + (it - w.hi);
-      if (o < a.cap) out[o] = it;
+      if (o < a.cap) out[o] = emit_id(a, b, it);
     } else if (flags & (1u << e)) {
-      if ((int)pos < a.cap) out[pos] = it;
+      if ((int)pos < a.cap) out[pos] = emit_id(a, b, it);
       ++pos;
     }
   }

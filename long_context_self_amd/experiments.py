@@ -5,6 +5,7 @@
     python -m long_context_self_amd.experiments row-scaling --config llama8b_32k
     python -m long_context_self_amd.experiments block-merge --config nsa_16k
     python -m long_context_self_amd.experiments latency --config llama8b_32k
+    python -m long_context_self_amd.experiments layer-stack [--layers 16] [--context 32768]
 
 collect-overhead: verify latency against the number of collected logit rows (none,
 one, the two boundary rows, half, all n_q).  The Vegas page (Figure 6 and its text)
@@ -25,8 +26,16 @@ many drafts, SSV page), on the workload's shapes.
 block-merge: SSV block mode (section 4.2 of the SSV page): the tree's rows in one call,
 which loads the union of their block sets once, against each row alone.
 
+nsa: NSA sparse verification (SSV page, Figure 3 and Figure 10): compression, the
+block plan, and the fused three-branch attention with exact, approximate or no
+grouping of the tree's rows.
+
 latency: p10 / p50 / p90 of every call over 100 calls, each after a 512 MiB cache
 flush, with GB/s against the 8 TB/s peak and against a measured device copy.
+
+layer-stack: forward latency of a random-weight Llama-3.2-1B-shaped stack at 32K
+context against the draft length, with dense verification or NSA sparse
+verification as its attention (SSV page, Figure 7; `layer_stack`).
 
 Host orchestration only: every step runs in the library's kernels.  Inputs are the
 seeded synthetic workloads of `synth`; the numbers are properties of those inputs,
@@ -195,6 +204,90 @@ def block_merge(cfg, replicas: int, iters: int, seed: int = 0) -> dict:
     return {"config": cfg.name, "replicas": replicas, "iters": iters, "points": res}
 
 
+def nsa(cfg, replicas: int, iters: int, seed: int = 0) -> dict:
+    """NSA sparse verification on the SSV workload: the compression pass, the block plan
+    (index derivation of a refresh layer), and the fused three-branch attention with the
+    rows grouped exactly, approximately, or not at all (each row alone, with its own plan),
+    each call on a KV replica last touched several calls earlier."""
+    import torch
+
+    from . import lcs, synth
+    from .metrics import nsa_bytes
+    kv = synth.make_paged_kv(cfg, seed=seed, extra_tokens=cfg.n_q)
+    nblk = cfg.L // cfg.page_size
+    sets = synth.make_block_sets(cfg, nblk, seed=seed)
+    q_np = synth.make_queries(cfg, kv, cfg.n_q, seed=seed)
+    tm_np = np.stack([synth.tree_tail_masks(cfg.n_q, cfg.tree_branches)] * cfg.B)
+    gates_np = synth.make_gates(cfg, cfg.n_q, seed=seed)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    k0, v0 = bf16(kv.k), bf16(kv.v)
+    bt = torch.from_numpy(kv.block_table).to("cuda")
+    layers = [lcs.PagedKV(k0 if r == 0 else k0.clone(), v0 if r == 0 else v0.clone(), bt) for r in range(replicas)]
+    B, n_q, Hq, d = cfg.B, cfg.n_q, cfg.Hq, cfg.d
+    pl = torch.from_numpy(kv.prefix_len).to("cuda")
+    max_cmp = (cfg.L - cfg.cmp_len) // cfg.cmp_stride + 1
+    comp = [lcs.nsa_compress(layers[r], pl, cfg.L, cfg.cmp_len, cfg.cmp_stride, max_cmp) for r in range(replicas)]
+    q = bf16(q_np)
+    idx = torch.from_numpy(sets).to("cuda")
+    cnt = torch.full((B, n_q, cfg.Hkv), cfg.blocks_per_row, dtype=torch.int32, device="cuda")
+    tl = torch.full((B,), n_q, dtype=torch.int32, device="cuda")
+    tm = torch.from_numpy(tm_np.view(np.int64)).to("cuda")
+    gates = torch.from_numpy(gates_np).to("cuda")
+    scale = 1.0 / math.sqrt(d)
+    plans = {grp: lcs.nsa_plan(layers[0], idx, cnt, grp) for grp in ("exact", "approximate")}
+    rows = []
+    for i in range(n_q):
+        ii, ci = idx[:, i:i + 1].contiguous(), cnt[:, i:i + 1].contiguous()
+        rows.append((q[:, i:i + 1].contiguous(), ii, ci, lcs.nsa_plan(layers[0], ii, ci),
+                     gates[:, i:i + 1].contiguous(), tm[:, i:i + 1].contiguous()))
+    out = torch.empty((B, n_q, Hq, d), dtype=torch.float32, device="cuda")
+    out1 = torch.empty((B, 1, Hq, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lcs.nsa_workspace_bytes(layers[0], B, n_q, Hq, cfg.blocks_per_row, n_q, max_cmp, cfg.window),
+                     dtype=torch.uint8, device="cuda")
+
+    def attn(r, grp):
+        lcs.nsa_attn(layers[r], comp[r][0], comp[r][1], cfg.cmp_len, cfg.cmp_stride, cfg.window, q, plans[grp],
+                     cfg.blocks_per_row, pl, tl, n_q, gates, scale, tail_mask=tm, out=out, workspace=ws)
+
+    def per_row(r):
+        for qi, ii, ci, pi, gi, ti in rows:
+            lcs.nsa_plan(layers[r], ii, ci, plan=pi)
+            lcs.nsa_attn(layers[r], comp[r][0], comp[r][1], cfg.cmp_len, cfg.cmp_stride, cfg.window, qi, pi,
+                         cfg.blocks_per_row, pl, tl, n_q, gi, scale, tail_mask=ti, out=out1, workspace=ws)
+
+    calls = {
+        "compress": lambda r: lcs.nsa_compress(layers[r], pl, cfg.L, cfg.cmp_len, cfg.cmp_stride, max_cmp,
+                                               k_cmp=comp[r][0], v_cmp=comp[r][1]),
+        "plan (refresh layer)": lambda r: lcs.nsa_plan(layers[r], idx, cnt, plan=plans["exact"]),
+        "attention, exact grouping (reuse layer)": lambda r: attn(r, "exact"),
+        "attention, approximate grouping": lambda r: attn(r, "approximate"),
+        "no grouping (each row: plan + attention)": per_row,
+    }
+    res = {}
+    for name, fn in calls.items():
+        for r in range(replicas):
+            fn(r)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            for r in range(replicas):
+                fn(r)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = {"us": round(e0.elapsed_time(e1) * 1e3 / (iters * replicas), 2)}
+    union = sum(len(np.unique(sets[b, :, g])) for b in range(B) for g in range(cfg.Hkv))
+    by = nsa_bytes(cfg, union, max_cmp)
+    for name in ("attention, exact grouping (reuse layer)", "attention, approximate grouping"):
+        res[name]["bytes"] = by
+        res[name]["GB/s"] = round(by / (res[name]["us"] * 1e3), 1)
+    return {"config": cfg.name, "replicas": replicas, "iters": iters, "max_cmp": max_cmp,
+            "mean_union_blocks": round(union / (B * cfg.Hkv), 2), "points": res}
+
+
 def latency(cfg, calls: int = 100, warmup: int = 10, flush_mib: int = 512, seed: int = 0,
             flush: str = "read") -> dict:
     """p10 / p50 / p90 latency of each call under a cold-cache protocol: before every
@@ -343,13 +436,21 @@ def overlap(cfg, seed: int = 0) -> dict:
 
 def main(argv=None) -> None:
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    p.add_argument("what", choices=["collect-overhead", "overlap", "row-scaling", "block-merge", "latency"])
+    p.add_argument("what", choices=["collect-overhead", "overlap", "row-scaling", "block-merge", "latency",
+                                    "layer-stack", "nsa"])
+    p.add_argument("--layers", type=int, default=16, help="layer-stack: layers")
+    p.add_argument("--context", type=int, default=32768, help="layer-stack: prefix length")
     p.add_argument("--config", default="llama8b_32k")
     p.add_argument("--replicas", type=int, default=0, help="KV copies rotated per timed call (0: sized to ~2 GB)")
     p.add_argument("--iters", type=int, default=5)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--flush", choices=["read", "write"], default="read", help="latency: how the caches are flushed")
     a = p.parse_args(argv)
+    if a.what == "layer-stack":
+        from . import layer_stack
+        shape = layer_stack.StackShape(layers=a.layers, context=a.context)
+        print(json.dumps(layer_stack.run(shape, iters=a.iters, seed=a.seed, log=sys.stderr)), flush=True)
+        return
     from . import synth
     cfg = synth.CONFIGS[a.config]
     kv_bytes = 4 * cfg.B * cfg.Hkv * cfg.d * cfg.L
@@ -362,6 +463,8 @@ def main(argv=None) -> None:
         res = block_merge(cfg, reps, a.iters, seed=a.seed)
     elif a.what == "latency":
         res = latency(cfg, seed=a.seed, flush=a.flush)
+    elif a.what == "nsa":
+        res = nsa(cfg, reps, a.iters, seed=a.seed)
     else:
         res = overlap(cfg, a.seed)
     print(json.dumps(res), flush=True)

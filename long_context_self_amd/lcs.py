@@ -61,6 +61,10 @@ SIGNATURES = {
                                     _f, _p, _p, _p, _sz, _p]),
     "lcs_sparse_draft_attn_noalloc": (_i32, [_KV, _p, _i32, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _i32,
                                             _p, _f, _p, _p, _p]),
+    "lcs_select_topk_physical": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _i32, _i32, _i32, _i32, _i32, _KV, _p, _p,
+                                       _i32, _p, _sz, _p]),
+    "lcs_sparse_draft_attn_physical": (_i32, [_KV, _p, _i32, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _i32, _p,
+                                             _f, _p, _p, _p, _sz, _p]),
     "lcs_select_topk_blocks": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p,
                                      _i32, _p, _sz, _p]),
     "lcs_nsa_compress": (_i32, [_KV, _i32, _p, _i32, _i32, _i32, _p, _p, _i32, _p]),
@@ -340,6 +344,54 @@ def sparse_draft_attn(kv: PagedKV, q: torch.Tensor, mode: str, indices: torch.Te
                                         _ptr(indices), _ptr(counts), cap, _ptr(tail_begin),
                                         _ptr(tail_len), max_tail_len, _ptr(tail_mask), scale,
                                         _ptr(out), _ptr(lse), ws.data_ptr(), ws.numel(), _stream()))
+    return out, lse
+
+
+def select_topk_physical(logits: torch.Tensor, prefix_len: torch.Tensor, max_prefix_len: int, Hkv: int,
+                         mode: str, top_k: int, n_sink: int, n_recent: int, kv: PagedKV,
+                         cap: Optional[int] = None, indices: Optional[torch.Tensor] = None,
+                         counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """lcs_select_topk_physical: the selected positions as physical cache slots through
+    kv's block table.  Returns (indices [B][n_sets][cap], counts [B][n_sets])."""
+    B, Hq = logits.shape[0], logits.shape[1]
+    dev = logits.device
+    n_sets = 1 if mode == "shared" else Hkv
+    if cap is None:
+        cap = max(1, min(max_prefix_len, n_sink + top_k + n_recent))
+    if indices is None:
+        indices = torch.full((B, n_sets, cap), -1, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.zeros((B, n_sets), dtype=torch.int32, device=dev)
+    need = load().lcs_select_workspace_bytes(B, Hq, Hkv, SET_MODES[mode], max_prefix_len, 0)
+    ws = _workspace(need, dev, workspace)
+    desc = kv.desc()
+    _check(load().lcs_select_topk_physical(_ptr(logits), logits.stride(2), B, Hq, Hkv, _ptr(prefix_len),
+                                           max_prefix_len, SET_MODES[mode], top_k, n_sink, n_recent,
+                                           ctypes.byref(desc), _ptr(indices), _ptr(counts), cap, ws.data_ptr(),
+                                           ws.numel(), _stream()))
+    return indices, counts
+
+
+def sparse_draft_attn_physical(kv: PagedKV, q: torch.Tensor, mode: str, indices: torch.Tensor,
+                               counts: torch.Tensor, tail_begin: torch.Tensor, tail_len: torch.Tensor,
+                               max_tail_len: int, scale: float, tail_mask: Optional[torch.Tensor] = None,
+                               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None):
+    """lcs_sparse_draft_attn_physical: lists of physical cache slots.  Returns (out, lse)."""
+    B, n_q, Hq, d = q.shape
+    dev = q.device
+    cap = indices.shape[-1]
+    if out is None:
+        out = torch.empty((B, n_q, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, n_q, Hq), dtype=torch.float32, device=dev)
+    desc = kv.desc()
+    need = load().lcs_sparse_workspace_bytes(B, n_q, Hq, ctypes.byref(desc), SET_MODES[mode], cap, max_tail_len)
+    ws = _workspace(need, dev, workspace)
+    _check(load().lcs_sparse_draft_attn_physical(ctypes.byref(desc), _ptr(q), B, n_q, Hq, SET_MODES[mode],
+                                                 _ptr(indices), _ptr(counts), cap, _ptr(tail_begin),
+                                                 _ptr(tail_len), max_tail_len, _ptr(tail_mask), scale,
+                                                 _ptr(out), _ptr(lse), ws.data_ptr(), ws.numel(), _stream()))
     return out, lse
 
 

@@ -31,3 +31,13 @@ def draft_bytes(cfg, S: int, tail_len: int) -> int:
     n_sets = 1 if cfg.mode == "shared" else Hkv
     return (4 * B * Hkv * d * (S + tail_len) + 4 * B * n_sets * S + 2 * B * Hq * d + 4 * B * Hq * d
             + 4 * B * Hq)
+
+
+def nsa_bytes(cfg, union_blocks: int, max_cmp: int) -> int:
+    """NSA sparse verification of the n_q rows: the compressed K/V of every compressed
+    block, the K/V of the union blocks (union_blocks summed over (b, g)), the window's
+    prefix positions and the tail once per branch that reads them, Q, the gates, O."""
+    B, Hq, Hkv, d, n_q, P = cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.n_q, cfg.page_size
+    win = min(cfg.window, cfg.L)
+    kv_rows = B * Hkv * max_cmp + union_blocks * P + B * Hkv * (win + 2 * n_q)
+    return 4 * d * kv_rows + 2 * B * n_q * Hq * d + 4 * B * n_q * Hq * 3 + 4 * B * n_q * Hq * d

@@ -207,3 +207,11 @@ def pack(res, cap: int):
             idx[b, s, :a.size] = a
             cnt[b, s] = a.size
     return idx, cnt
+
+
+def to_physical(positions: np.ndarray, block_table: np.ndarray, b: int, page_size: int) -> np.ndarray:
+    """Physical cache slots of sequence b's logical positions: the paged layout puts
+    position p in page block_table[b][p // P] at slot p % P, i.e. slot page * P + p % P
+    (the hand-off of a selection to the draft as physical rows)."""
+    p = np.asarray(positions, dtype=np.int64)
+    return (block_table[b][p // page_size].astype(np.int64) * page_size + p % page_size).astype(np.int64)

@@ -216,3 +216,16 @@ def test_block_lse_selection(bs, L, B):
                 gap = np.abs(beta[np.setxor1d(got, want)] - np.min(beta[pool_keep]))
                 assert np.all(gap <= 1e-4 * max(1.0, float(np.max(np.abs(beta)))))
 
+
+def test_layer_stack_timing_loop_runs():
+    """The random-weight layer stack (timing only) runs dense and NSA verification for
+    draft lengths 1 .. 64 on a small stack and yields finite times."""
+    require_gpu()
+    from long_context_self_amd import layer_stack
+    shape = layer_stack.StackShape(layers=2, hidden=256, Hq=8, Hkv=2, d=64, mlp=512, context=16384,
+                                   blocks_per_row=4, core_blocks=2)
+    res = layer_stack.run(shape, gammas=(1, 4, 64), iters=2, warmup=1)
+    for n_q in ("1", "4", "64"):
+        pt = res["points"][n_q]
+        assert math.isfinite(pt["dense_ms"]) and pt["dense_ms"] > 0
+        assert math.isfinite(pt["nsa_ms"]) and pt["nsa_ms"] > 0

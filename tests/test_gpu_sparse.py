@@ -216,3 +216,42 @@ def test_any_workspace_contents(name, L, B, mode):
     for o in outs[1:]:
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
     assert np.max(np.abs(outs[0] - o_out)) <= OUT_TOL
+
+
+@pytest.mark.parametrize("name,L,B,mode", [("llama8b_32k", 6000, 2, "shared"), ("qwen14b_64k", 5000, 2, "per_kv_head"),
+                                           ("tiny", None, 1, "shared")])
+def test_physical_hand_off(name, L, B, mode):
+    """Select writes physical cache slots through the block table (the same set as the
+    logical selection, mapped), and the draft over those slots equals the draft over the
+    positions bit for bit, and the oracle within tolerance."""
+    torch, lcs = require_gpu()
+    cfg = synth.CONFIGS[name]
+    cfg = cfg.with_(B=B, L=L if L else cfg.L, top_k=min(cfg.top_k, (L or cfg.L) // 4))
+    lens = [cfg.L - 61 * b for b in range(B)]
+    kv = synth.make_paged_kv(cfg, seed=51, lens=lens)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=51)
+    dkv = kv_dev(kv, torch, lcs)
+    pl = i32_dev(kv.prefix_len, torch)
+    _, logits, _ = lcs.verify_attn(dkv, bf16_dev(q, torch), pl, cfg.L, scale_for(cfg.d), cfg.collect_rows)
+    idx, cnt = lcs.select_topk(logits, pl, cfg.L, cfg.Hkv, mode, cfg.top_k, cfg.n_sink, cfg.n_recent)
+    pidx, pcnt = lcs.select_topk_physical(logits, pl, cfg.L, cfg.Hkv, mode, cfg.top_k, cfg.n_sink, cfg.n_recent, dkv)
+    torch.cuda.synchronize()
+    idx_n, cnt_n, pidx_n = idx.cpu().numpy(), cnt.cpu().numpy(), pidx.cpu().numpy()
+    assert np.array_equal(cnt_n, pcnt.cpu().numpy())
+    for b in range(B):
+        for s in range(cnt_n.shape[1]):
+            n = int(cnt_n[b, s])
+            want = osel.to_physical(idx_n[b, s, :n], kv.block_table, b, cfg.page_size)
+            assert np.array_equal(pidx_n[b, s, :n], want)
+    qd = synth.make_queries(cfg, kv, 1, seed=51, tag=100)
+    tl = np.full(B, cfg.n_q + 1, dtype=np.int32)
+    args = (bf16_dev(qd, torch), mode)
+    out_l, lse_l = lcs.sparse_draft_attn(dkv, *args, idx, cnt, pl, i32_dev(tl, torch), int(tl.max()), scale_for(cfg.d))
+    out_p, lse_p = lcs.sparse_draft_attn_physical(dkv, *args, pidx, pcnt, pl, i32_dev(tl, torch), int(tl.max()),
+                                                  scale_for(cfg.d))
+    torch.cuda.synchronize()
+    assert np.array_equal(out_l.cpu().numpy(), out_p.cpu().numpy())
+    assert np.array_equal(lse_l.cpu().numpy(), lse_p.cpu().numpy())
+    ref, _ = oa.sparse_attn(qd, kv.k, kv.v, kv.block_table, cfg.page_size, mode, idx_n, cnt_n, kv.prefix_len, tl,
+                            scale_for(cfg.d))
+    assert float(np.max(np.abs(out_p.cpu().numpy() - ref))) <= OUT_TOL

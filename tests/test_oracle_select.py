@@ -273,3 +273,15 @@ def test_select_block_mode_per_group_matches_rank_enumeration(seed):
             assert got[b][g].tolist() == sorted(ref), (b, g)
     # the groups really select differently on these inputs (so the test can tell them apart)
     assert any(got[b][0].tolist() != got[b][g].tolist() for b in range(B) for g in range(1, Hkv))
+
+
+def test_to_physical_hand_worked_and_round_trip():
+    bt = np.array([[3, 0, 2, 1]], dtype=np.int32)     # logical page i lives in physical page bt[0][i]
+    P = 4
+    assert osel.to_physical(np.array([0, 5, 9, 15]), bt, 0, P).tolist() == [12, 1, 9, 7]
+    rng = np.random.default_rng(9)
+    bt = rng.permutation(64).astype(np.int32)[None, :]
+    pos = np.sort(rng.choice(64 * 16, 100, replace=False))
+    phys = osel.to_physical(pos, bt, 0, 16)
+    inv = np.argsort(bt[0])                              # physical page -> logical page
+    assert np.array_equal(inv[phys // 16] * 16 + phys % 16, pos)
