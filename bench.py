@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--config", default=DEFAULT_CONFIG)
     p.add_argument("--layers", type=int, default=0,
                    help="layers (KV replicas); 0 = the workload's default (4 at 128K x 8, 32 at 32K)")
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip the fused variants (partial scores, physical hand-off) on the same inputs")
     p.add_argument("--no-secondary", action="store_true",
                    help="skip the secondary per-call measurement on the 32K workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -65,6 +67,8 @@ def parse():
     p.add_argument("--scores", action="store_true",
                    help="verify writes per-KV-head partial scores and select reads them, instead of the "
                         "two collected logit rows")
+    p.add_argument("--physical", action="store_true",
+                   help="select hands its sets to the draft as physical cache slots (the fused hand-off)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="run one device-to-device copy of this size first (counter calibration)")
     return p.parse_args()
@@ -196,17 +200,14 @@ def oracle_timing():
           flush=True)
 
 
-def measure(cfg, R, steps, warmup, scores=False, refresh_every=1, copy_calibration_mib=0, log=None):
-    """Time `steps` bench steps of workload cfg over R layers on the GPU.  Returns the
-    per-call latencies (us, HIP events on the calling stream), the algorithmic bytes and
-    the step time."""
+def setup_workload(cfg, R, copy_calibration_mib=0, log=None):
+    """Device inputs of workload cfg over R layers (each layer its own KV replica)."""
     import torch
 
     from long_context_self_amd import lcs, synth
 
     assert cfg.mode in ("shared", "per_kv_head"), "bench covers the token-set workloads"
     dev = "cuda"
-    scale = 1.0 / math.sqrt(cfg.d)
     t_setup = time.perf_counter()
     kv = synth.make_paged_kv(cfg, seed=0)
     q = synth.make_queries(cfg, kv, cfg.n_q, seed=0)
@@ -220,8 +221,29 @@ def measure(cfg, R, steps, warmup, scores=False, refresh_every=1, copy_calibrati
     pl = torch.from_numpy(kv.prefix_len).to(dev)
     del kv
     layers = [lcs.PagedKV(k0 if r == 0 else k0.clone(), v0 if r == 0 else v0.clone(), bt) for r in range(R)]
-    qv = bf16(q)
-    qds = [bf16(x) for x in qd]
+    if copy_calibration_mib > 0:
+        src = torch.empty(copy_calibration_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    torch.cuda.synchronize()
+    if log:
+        print(f"{cfg.name}: set up {R} layers in {time.perf_counter() - t_setup:.1f} s", file=log, flush=True)
+    return {"cfg": cfg, "R": R, "layers": layers, "qv": bf16(q), "qds": [bf16(x) for x in qd], "pl": pl}
+
+
+def measure(ws, steps, warmup, scores=False, refresh_every=1, physical=False):
+    """Time `steps` bench steps on the set-up workload ws.  Returns the per-call latencies
+    (us, HIP events on the calling stream), the algorithmic bytes and the step time."""
+    import torch
+
+    from long_context_self_amd import lcs
+
+    cfg, R, layers, qv, qds, pl = ws["cfg"], ws["R"], ws["layers"], ws["qv"], ws["qds"], ws["pl"]
+    dev = "cuda"
+    scale = 1.0 / math.sqrt(cfg.d)
     B, Hq, L = cfg.B, cfg.Hq, cfg.L
     n_sets = 1 if cfg.mode == "shared" else cfg.Hkv
     S = cfg.n_sink + cfg.top_k + cfg.n_recent
@@ -251,7 +273,10 @@ def measure(cfg, R, steps, warmup, scores=False, refresh_every=1, copy_calibrati
                             workspace=ws_v)
 
     def select(r):
-        if scores:
+        if physical:
+            lcs.select_topk_physical(logits[r], pl, L, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent,
+                                     layers[r], cap=S, indices=idx[r], counts=cnt[r], workspace=ws_s)
+        elif scores:
             lcs.select_topk_scores(logits[r], pl, L, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
                                    indices=idx[r], counts=cnt[r], workspace=ws_s, Hq=Hq)
         else:
@@ -263,24 +288,14 @@ def measure(cfg, R, steps, warmup, scores=False, refresh_every=1, copy_calibrati
 
     def draft(r, j):
         rs = r - r % RF                                  # reuse layers take the refresh layer's sets
-        lcs.sparse_draft_attn(layers[r], qds[j], cfg.mode, idx[rs], cnt[rs], pl, tls[j], max_tl, scale,
-                              out=dout, lse=dlse, workspace=ws_d)
-
-    if copy_calibration_mib > 0:
-        src = torch.empty(copy_calibration_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        draft_fn = lcs.sparse_draft_attn_physical if physical else lcs.sparse_draft_attn
+        draft_fn(layers[r], qds[j], cfg.mode, idx[rs], cnt[rs], pl, tls[j], max_tl, scale, out=dout, lse=dlse,
+                 workspace=ws_d)
 
     for r in range(R):       # the first iteration's sparse sets
         verify(r)
         select(r)
     torch.cuda.synchronize()
-    setup_s = time.perf_counter() - t_setup
-    if log:
-        print(f"{cfg.name}: set up {R} layers in {setup_s:.1f} s", file=log, flush=True)
 
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     phase_ms = {"draft": 0.0, "verify": 0.0, "select": 0.0}
@@ -320,13 +335,12 @@ def measure(cfg, R, steps, warmup, scores=False, refresh_every=1, copy_calibrati
     tail_lens = [cfg.n_q + j + 1 for j in range(cfg.n_draft)]
     vb, sb, db = algorithmic_bytes(cfg, s_count, tail_lens, scores=scores)
     step_bytes = R * (vb + sum(db)) + len(refresh) * sb
-    del layers, k0, v0
-    torch.cuda.empty_cache()
+    del logits, idx, cnt, ws_v, ws_s, ws_d
     return {"ms_per_step": ms_per_step, "step_bytes": step_bytes, "us": {"verify": t_verify_us,
             "select": t_select_us, "draft_step": t_draft_us},
             "bytes": {"verify": vb, "select": sb, "draft_step": int(sum(db) / len(db))},
             "share": {"verify": phase_ms["verify"], "select": phase_ms["select"], "draft": phase_ms["draft"]},
-            "selected": s_count, "R": R, "refresh": len(refresh), "RF": RF, "setup_s": setup_s}
+            "selected": s_count, "R": R, "refresh": len(refresh), "RF": RF}
 
 
 def kernel_table(cfg, m):
@@ -365,15 +379,26 @@ def main():
     torch.cuda.set_device(0)
     cfg = synth.CONFIGS[args.config]
     R = args.layers or DEFAULT_LAYERS.get(cfg.name, 4)
-    m = measure(cfg, R, args.steps, args.warmup, scores=args.scores, refresh_every=args.refresh_every,
-                copy_calibration_mib=args.copy_calibration_mib, log=sys.stderr)
+    ws = setup_workload(cfg, R, copy_calibration_mib=args.copy_calibration_mib, log=sys.stderr)
+    m = measure(ws, args.steps, args.warmup, scores=args.scores, refresh_every=args.refresh_every,
+                physical=args.physical)
+    variants = {}
+    if not args.no_variants and not (args.scores or args.physical or args.refresh_every != 1):
+        # the fused variants of the same step on the same inputs (not the headline)
+        for name, kw in (("partial_scores", {"scores": True}), ("physical_hand_off", {"physical": True})):
+            mv = measure(ws, args.steps, args.warmup, **kw)
+            variants[name] = {"ms_per_step": round(mv["ms_per_step"], 4),
+                              "value_GB/s": round(mv["step_bytes"] / (mv["ms_per_step"] * 1e-3) / 1e9, 2),
+                              "kernels": kernel_table(cfg, mv)}
+    del ws
+    torch.cuda.empty_cache()
     kern = kernel_table(cfg, m)
     value = m["step_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
     # the call with the largest share of the step's time carries the roofline
     share = {"verify": m["share"]["verify"], "select": m["share"]["select"], "draft_step": m["share"]["draft"]}
     dom = max(share, key=share.get)
     traffic = None
-    if not args.scores and args.refresh_every == 1:
+    if not args.scores and not args.physical and args.refresh_every == 1:
         traffic = traffic_record(cfg.name, dom)
     result = {
         "metric": "draft-step & verify-step attention latency (us), achieved HBM GB/s vs peak",
@@ -392,6 +417,7 @@ def main():
                    "page_size": cfg.page_size, "n_q": cfg.n_q, "n_draft": cfg.n_draft,
                    "select": f"{cfg.mode} top-{cfg.top_k}+{cfg.n_sink} sink+{cfg.n_recent} recent",
                    "collected": "per-KV-head partial scores" if args.scores else "two logit rows",
+                   "hand_off": "physical cache slots" if args.physical else "positions",
                    "refresh_every": m["RF"], "layers": R},
         "kernels": kern,
         "step_share": {k: round(v / sum(share.values()), 4) for k, v in share.items()},
@@ -401,9 +427,13 @@ def main():
                      "kernel": f"{dom}: {CALL_KERNELS[dom]}, per call",
                      "algorithmic_bytes": kern[dom]["bytes"]},
     }
+    if variants:
+        result["variants"] = variants
     if not args.no_secondary and args.config != SECONDARY_CONFIG:
         c2 = synth.CONFIGS[SECONDARY_CONFIG]
-        m2 = measure(c2, DEFAULT_LAYERS[SECONDARY_CONFIG], args.steps, args.warmup, log=sys.stderr)
+        ws2 = setup_workload(c2, DEFAULT_LAYERS[SECONDARY_CONFIG], log=sys.stderr)
+        m2 = measure(ws2, args.steps, args.warmup, scores=args.scores, physical=args.physical)
+        del ws2
         result["secondary"] = {"workload": c2.name, "layers": m2["R"], "ms_per_step": round(m2["ms_per_step"], 4),
                                "value_GB/s": round(m2["step_bytes"] / (m2["ms_per_step"] * 1e-3) / 1e9, 2),
                                "kernels": kernel_table(c2, m2)}

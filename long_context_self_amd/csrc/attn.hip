@@ -202,6 +202,8 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, int g, int
 // The stage scratch (indices, pages) lives in the next window's mask buffer.
 // ---------------------------------------------------------------------------
 constexpr int kMW = 4;                      // steps per metadata window
+constexpr int kStageRows = 8;               // collected logit rows (slots x heads) a wave stages
+constexpr int kStageSteps = 4;              // steps staged before one flush (512-byte row runs)
 constexpr int kMT = kMW * kStepTokens;      // token slots per window
 constexpr int kTokPerLane = kMT / 64;       // slots each lane handles per stage
 
@@ -623,7 +625,12 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   constexpr int kPer = 4 * 8 + 2;             // merge floats per lane per q-tile
   constexpr size_t kQBytes = (size_t)QT * 16 * D * 2;
   constexpr size_t kWaveBytes = sizeof(WaveMeta) + 2 * (size_t)kSlot;
-  constexpr size_t kLoopBytes = kQBytes + kWaves * kWaveBytes;
+  // Collected logit rows are staged per wave (kStageRows rows x kStageSteps steps) in an
+  // area that starts with the Q tile, free once every wave holds Q in registers
+  constexpr bool kCanStage = MODE == MODE_DENSE && !SC;
+  constexpr size_t kStageWave = (size_t)kStageRows * kStageSteps * kStepTokens * 4;
+  constexpr size_t kHead = (kCanStage && kWaves * kStageWave > kQBytes) ? kWaves * kStageWave : kQBytes;
+  constexpr size_t kLoopBytes = kHead + kWaves * kWaveBytes;
   constexpr size_t kMergeBytes = (size_t)kWaves * QT * kPer * 64 * 4;
   constexpr size_t kSmem = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmem];
@@ -641,7 +648,7 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   const int nrows = min(kMaxRowsPerWG, a.rows - r0);
 
   uint16_t* s_q = reinterpret_cast<uint16_t*>(smem_raw);
-  unsigned char* wbase_lds = smem_raw + kQBytes + (size_t)wave * kWaveBytes;
+  unsigned char* wbase_lds = smem_raw + kHead + (size_t)wave * kWaveBytes;
   WaveMeta& wm = *reinterpret_cast<WaveMeta*>(wbase_lds);
   char* ring = reinterpret_cast<char*>(wbase_lds + sizeof(WaveMeta));
   float* s_merge = reinterpret_cast<float*>(smem_raw);
@@ -690,6 +697,9 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
       cslot[qt] = __popcll(a.cmask & ((1ull << rowi[qt]) - 1)) ^ a.cswap;
   }
   const bool collect = MODE == MODE_DENSE && !SC && a.logits != nullptr;
+  // stage the collected rows of kStageSteps steps in LDS and write each row as one run:
+  // needs at most kStageRows rows per group and 16-byte aligned rows
+  const bool stage = kCanStage && collect && a.lvec4 && a.n_cl * a.G <= kStageRows;
 
   float m[QT], l[QT];
   f32x4 O[QT][8];
@@ -758,8 +768,8 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
       qop[qt][ks] = *reinterpret_cast<const u32x4*>(s_q + (r * QCH + (c ^ (r % QCH))) * 8);
     }
   }
-  // partial scores stage their logits in the Q area, free once every wave holds Q
-  if constexpr (SC) {
+  // partial scores and staged logit rows use the Q area, free once every wave holds Q
+  if (SC || stage) {
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -848,6 +858,67 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
           }
         }
       }
+    };
+    // Staged collected rows: each step's scaled logits go to this wave's staging area as
+    // [slot c * G + head][kStageSteps * 32 tokens]; after kStageSteps steps (or the wave's
+    // last prefix step) the staged run of every row is written with 16-byte streaming
+    // stores, one row run of up to 512 contiguous bytes per 32 lanes.
+    float* stg = reinterpret_cast<float*>(smem_raw) + (size_t)wave * (kStageWave / 4);
+    const int st_last = min(w1, (si.L + kStepTokens - 1) / kStepTokens) - 1;   // last prefix step
+    int st_first = w0;                                                       // first staged step
+    // staged rows that this workgroup's row chunk holds (a row chunk may hold one slot only)
+    uint32_t smask = 0;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      if (cslot[qt] < 0) continue;
+      const int hh = r0 + 16 * qt + x - rowi[qt] * a.G;
+      smask |= 1u << (cslot[qt] * a.G + hh);
+      if (a.cdup) smask |= 1u << ((cslot[qt] + 1) * a.G + hh);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) smask |= __shfl_xor(smask, off);
+    auto stage_logits = [&](int st) {
+      if (st > st_last) return;
+      const int col = (st - st_first) * kStepTokens + 4 * j;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        if (cslot[qt] < 0) continue;
+        const int hh = r0 + 16 * qt + x - rowi[qt] * a.G;
+        float* dst = stg + (cslot[qt] * a.G + hh) * (kStageSteps * kStepTokens) + col;
+        *reinterpret_cast<f32x4*>(dst) = S[0][qt] * a.scale;
+        *reinterpret_cast<f32x4*>(dst + 16) = S[1][qt] * a.scale;
+        if (a.cdup) {
+          float* d2 = dst + a.G * (kStageSteps * kStepTokens);
+          *reinterpret_cast<f32x4*>(d2) = S[0][qt] * a.scale;
+          *reinterpret_cast<f32x4*>(d2 + 16) = S[1][qt] * a.scale;
+        }
+      }
+      if (st - st_first + 1 < kStageSteps && st < st_last) return;
+      // flush: chunk q = lane + 64u covers row q / 32 (of n_cl * G rows), 16 bytes at column
+      // 4 * (q % 32) of the staged run [st_first * 32, (st + 1) * 32) clipped to the prefix
+      wait_lgkm0();
+      const int p0 = st_first * kStepTokens;
+      const int ncol = min((st + 1) * kStepTokens, si.L) - p0;
+      const int nrow = a.n_cl * a.G;
+#pragma unroll 1
+      for (int u = 0; u < kStageRows * kStageSteps * kStepTokens / 4 / 64; ++u) {
+        const int q = lane + 64 * u;
+        const int rr = q / (kStageSteps * kStepTokens / 4);
+        const int cc = 4 * (q % (kStageSteps * kStepTokens / 4));
+        if (rr >= nrow || cc >= ncol || !((smask >> rr) & 1u)) continue;
+        const int c = rr / a.G;
+        const int h = g * a.G + (rr - c * a.G);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rr * (kStageSteps * kStepTokens) + cc);
+        float* dst = a.logits + ((size_t)(b * a.Hq + h) * a.n_cl + c) * a.logits_ld + p0 + cc;
+        if (cc + 4 <= ncol) {
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (cc + e < ncol) dst[e] = v[e];
+        }
+      }
+      st_first = st + 1;
     };
     // Partial scores: the lanes of the collected rows put their scaled logits of the
     // step in this wave's part of the Q area as [slot c * G + head][32 tokens]; lanes
@@ -979,7 +1050,8 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
             S[1][qt] = mfma16(kop[1][ks], qop[qt][ks], S[1][qt]);
           }
         }
-        if (collect) store_logits(step);
+        if (stage) stage_logits(step);
+        else if (collect) store_logits(step);
         if constexpr (SC) store_scores(step);
         // cache rows of step s+2, which refills this slot (read even when no refill is
         // due: the pointer stays inside this wave's metadata area)

@@ -294,6 +294,12 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
     sh_bin = 0;
     sh_above = 0;
   }
+  // this thread's kIPT consecutive keys do not depend on the bin: they load while the
+  // histogram is scanned
+  const int i0 = blockIdx.x * kItemChunk + kIPT * tid;
+  const bool mine = i0 < w.hi && i0 + kIPT > w.lo;
+  uint32_t k[kIPT], flags = 0, n_above = 0;
+  if (mine) load16(a.keys + (size_t)set * a.item_cap, i0, k);
   __syncthreads();
   find_bin(a, set, s_wave, &sh_bin, &sh_above);
   const int bin = sh_bin;
@@ -301,11 +307,8 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
     a.thr[(size_t)set * 2 + 0] = (uint64_t)bin;
     a.thr[(size_t)set * 2 + 1] = (uint64_t)sh_above;
   }
-  // this thread's kIPT consecutive items: count those above the bin, flag the bin's
-  const int i0 = blockIdx.x * kItemChunk + kIPT * tid;
-  uint32_t k[kIPT], flags = 0, n_above = 0;
-  if (i0 < w.hi && i0 + kIPT > w.lo) {
-    load16(a.keys + (size_t)set * a.item_cap, i0, k);
+  // count the items above the bin, flag the bin's
+  if (mine) {
 #pragma unroll
     for (int e = 0; e < kIPT; ++e) {
       if (i0 + e < w.lo || i0 + e >= w.hi) continue;

@@ -17,7 +17,10 @@ cached position, two logit rows collected) or NSA sparse verification
 sliding window, gated per head by a sigmoid of a gate projection).  The projections
 and the MLP are plain library GEMMs (torch.matmul); RMSNorm, SiLU, the sigmoid and
 the cache writes are torch element-wise operations.  Rotary embeddings are left out:
-with random weights they change no timing of the attention path.
+with random weights they change no timing of the attention path.  Each forward is
+captured once in a HIP graph and replayed for timing (eager launches of ~15 small
+operations per layer are bound by host dispatch); every replay is checked against
+the eager forward.
 
     python -m long_context_self_amd.experiments layer-stack [--layers 16] [--context 32768]
 """
@@ -153,19 +156,37 @@ def run(shape: StackShape, gammas=(1, 2, 4, 8, 16, 32, 64), iters: int = 10, war
         for kind in ("dense", "nsa"):
             if kind == "nsa" and plan is None:
                 continue
-            for _ in range(warmup):
-                forward(kind)
+            # eager reference, then the whole forward captured in a HIP graph and replayed:
+            # eagerly, the ~15 launches per layer are bound by host dispatch, not the GPU
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for _ in range(warmup):
+                    ref = forward(kind)
+            torch.cuda.current_stream().wait_stream(side)
             torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ref = forward(kind)
+            e1.record()
+            torch.cuda.synchronize()
+            point[f"{kind}_eager_ms"] = e0.elapsed_time(e1)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                y = forward(kind)
             times = []
             for _ in range(iters):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                y = forward(kind)
+                graph.replay()
                 e1.record()
                 torch.cuda.synchronize()
                 times.append(e0.elapsed_time(e1))
-            assert bool(torch.isfinite(y.float()).all())
+                # every replay reproduces the eager forward
+                assert bool(torch.isfinite(y.float()).all())
+                assert float((y.float() - ref.float()).abs().max()) <= 1e-2 * max(1.0, float(ref.float().abs().max()))
             point[f"{kind}_ms"] = float(np.median(times))
+            del graph
         res["points"][str(n_q)] = point
         if log is not None:
             print(f"gamma {n_q}: {point}", file=log, flush=True)
