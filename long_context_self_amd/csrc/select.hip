@@ -343,7 +343,9 @@ __device__ __forceinline__ int32_t emit_id(const SelArgs& a, int b, int it) {
 }
 
 constexpr int kFinLDS = 8192;      // candidates a workgroup holds in LDS
-constexpr int kFinIPT = kItemChunk / 1024;   // consecutive items per thread in finish
+constexpr int kFinThreads = 1024;  // threads of a finish workgroup
+constexpr int kFinIPT = kItemChunk / kFinThreads;   // consecutive items per thread in finish
+constexpr int kFinBPT = 2048 / kFinThreads;         // radix bins per thread in a pass
 
 // Boundary and output of one 4096-item chunk (one workgroup per chunk and set).  Every
 // chunk's workgroup finds the exact boundary composite itself: the radix passes over
@@ -351,7 +353,7 @@ constexpr int kFinIPT = kItemChunk / 1024;   // consecutive items per thread in 
 // kept items after the sink window, the kept items of the chunks before it (their items
 // above the bin, counted by collect, and their candidates at or above the boundary) and
 // the kept items before it in this chunk.
-__global__ void __launch_bounds__(1024) finish_kernel(SelArgs a) {
+__global__ void __launch_bounds__(kFinThreads) finish_kernel(SelArgs a) {
   const int set = blockIdx.y;
   const int b = set / a.n_sets;
   const Win w = window(a, b);
@@ -359,7 +361,7 @@ __global__ void __launch_bounds__(1024) finish_kernel(SelArgs a) {
   const int c0 = blockIdx.x * kItemChunk;          // first item of this chunk
   int32_t* out = a.indices + (size_t)set * a.cap;
   if (w.all) {
-    for (int it = c0 + tid; it < min(w.n, c0 + kItemChunk); it += 1024)
+    for (int it = c0 + tid; it < min(w.n, c0 + kItemChunk); it += kFinThreads)
       if (it < a.cap) out[it] = emit_id(a, b, it);
     if (blockIdx.x == 0 && tid == 0) a.counts[set] = min(w.n, a.cap);
     return;
@@ -367,16 +369,26 @@ __global__ void __launch_bounds__(1024) finish_kernel(SelArgs a) {
   const int K = a.top_k;
   __shared__ uint64_t lc[kFinLDS];
   __shared__ uint32_t hist[2048];
-  __shared__ uint32_t s_wave[16];
+  __shared__ uint32_t s_wave[kFinThreads / 64];
   __shared__ uint64_t sh_prefix, sh_one;
   __shared__ uint32_t sh_rem, sh_cnt;
   // this thread's kFinIPT consecutive items (t0 is a multiple of 4 below item_cap, a
-  // multiple of 16, so the 16-byte load stays inside the set's keys); they do not depend
+  // multiple of 16, so the 16-byte loads stay inside the set's keys); they do not depend
   // on the boundary, so they are loaded first
   const int t0 = c0 + kFinIPT * tid;
-  uint4 kq = make_uint4(0u, 0u, 0u, 0u);
-  if (K > 0 && t0 < w.hi && t0 + kFinIPT > w.lo)
-    kq = *reinterpret_cast<const uint4*>(a.keys + (size_t)set * a.item_cap + t0);
+  uint32_t kk[kFinIPT];
+#pragma unroll
+  for (int e = 0; e < kFinIPT; ++e) kk[e] = 0u;
+  if (K > 0 && t0 < w.hi && t0 + kFinIPT > w.lo) {
+#pragma unroll
+    for (int v = 0; v < kFinIPT / 4; ++v) {
+      const uint4 q = *reinterpret_cast<const uint4*>(a.keys + (size_t)set * a.item_cap + t0 + 4 * v);
+      kk[4 * v] = q.x;
+      kk[4 * v + 1] = q.y;
+      kk[4 * v + 2] = q.z;
+      kk[4 * v + 3] = q.w;
+    }
+  }
   int bin = 0;
   uint64_t cstar = ~0ull;
   uint32_t base = (uint32_t)w.lo;
@@ -387,7 +399,7 @@ __global__ void __launch_bounds__(1024) finish_kernel(SelArgs a) {
     const uint64_t* gcand = a.cand + (size_t)set * a.item_cap;
     const bool in_lds = n_c <= kFinLDS;
     if (in_lds)
-      for (int e = tid; e < n_c; e += 1024) lc[e] = gcand[e];
+      for (int e = tid; e < n_c; e += kFinThreads) lc[e] = gcand[e];
     const uint64_t* cand = in_lds ? lc : gcand;
     if (tid == 0) {
       sh_prefix = 0;
@@ -400,31 +412,37 @@ __global__ void __launch_bounds__(1024) finish_kernel(SelArgs a) {
     int pass = 0;
     for (; pass < 4; ++pass) {
       const int shift = 33 - 11 * pass;
-      hist[tid] = 0;
-      hist[tid + 1024] = 0;
+      for (int i = tid; i < 2048; i += kFinThreads) hist[i] = 0;
       __syncthreads();
       const uint64_t prefix = sh_prefix;
       const uint32_t rem = sh_rem;
-      for (int e = tid; e < n_c; e += 1024) {
+      for (int e = tid; e < n_c; e += kFinThreads) {
         const uint64_t cv = cand[e];
         if ((cv & mask) == prefix) atomicAdd(&hist[(cv >> shift) & 2047u], 1u);
       }
       __syncthreads();
-      // the digit holding the rem-th largest remaining composite (suffix sums over bins)
-      const uint32_t hl = hist[2 * tid], hh = hist[2 * tid + 1];
-      const uint32_t c = hl + hh;
+      // the digit holding the rem-th largest remaining composite (suffix sums over bins):
+      // this thread owns bins [kFinBPT * tid, kFinBPT * tid + kFinBPT)
+      uint32_t hv[kFinBPT], c = 0;
+#pragma unroll
+      for (int e = 0; e < kFinBPT; ++e) {
+        hv[e] = hist[kFinBPT * tid + e];
+        c += hv[e];
+      }
       uint32_t total;
-      const uint32_t excl = block_excl_scan<1024>(c, s_wave, total);
+      const uint32_t excl = block_excl_scan<kFinThreads>(c, s_wave, total);
       const uint32_t above_t = total - excl - c;
       if (above_t < rem && above_t + c >= rem) {
-        if (above_t + hh >= rem) {
-          sh_prefix = prefix | ((uint64_t)(2 * tid + 1) << shift);
-          sh_rem = rem - above_t;
-          sh_cnt = hh;
-        } else {
-          sh_prefix = prefix | ((uint64_t)(2 * tid) << shift);
-          sh_rem = rem - above_t - hh;
-          sh_cnt = hl;
+        uint32_t cum = above_t;
+#pragma unroll
+        for (int e = kFinBPT - 1; e >= 0; --e) {
+          if (cum + hv[e] >= rem) {
+            sh_prefix = prefix | ((uint64_t)(kFinBPT * tid + e) << shift);
+            sh_rem = rem - cum;
+            sh_cnt = hv[e];
+            break;
+          }
+          cum += hv[e];
         }
       }
       mask |= (uint64_t)2047u << shift;
@@ -434,7 +452,7 @@ __global__ void __launch_bounds__(1024) finish_kernel(SelArgs a) {
     cstar = sh_prefix;
     if (pass < 3) {                 // one candidate carries the chosen prefix: it is the answer
       const uint64_t prefix = sh_prefix;
-      for (int e = tid; e < n_c; e += 1024) {
+      for (int e = tid; e < n_c; e += kFinThreads) {
         const uint64_t cv = cand[e];
         if ((cv & mask) == prefix) sh_one = cv;
       }
@@ -443,17 +461,16 @@ __global__ void __launch_bounds__(1024) finish_kernel(SelArgs a) {
     }
     // kept items of the chunks before this one
     uint32_t part = 0;
-    for (int c = tid; c < (int)blockIdx.x; c += 1024) part += a.chunk_above[(size_t)set * a.n_chunks + c];
-    for (int e = tid; e < n_c; e += 1024) {
+    for (int c = tid; c < (int)blockIdx.x; c += kFinThreads) part += a.chunk_above[(size_t)set * a.n_chunks + c];
+    for (int e = tid; e < n_c; e += kFinThreads) {
       const uint64_t cv = cand[e];
       const int item = (int)(kItemMask - (uint32_t)(cv & kItemMask));
       part += (cv >= cstar && item < c0) ? 1u : 0u;
     }
     uint32_t before;
-    block_excl_scan<1024>(part, s_wave, before);
+    block_excl_scan<kFinThreads>(part, s_wave, before);
     base += before;
   }
-  const uint32_t kk[kFinIPT] = {kq.x, kq.y, kq.z, kq.w};
   uint32_t flags = 0, cnt = 0;
   if (K > 0) {
 #pragma unroll
@@ -468,7 +485,7 @@ __global__ void __launch_bounds__(1024) finish_kernel(SelArgs a) {
     }
   }
   uint32_t total;
-  uint32_t pos = base + block_excl_scan<1024>(cnt, s_wave, total);
+  uint32_t pos = base + block_excl_scan<kFinThreads>(cnt, s_wave, total);
 #pragma unroll
   for (int e = 0; e < kFinIPT; ++e) {
     const int it = t0 + e;
@@ -536,7 +553,7 @@ hipError_t select_launch(const SelPlan& p, SelArgs a, void* workspace, hipStream
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(collect_kernel, dim3(p.n_chunks, NS), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(finish_kernel, dim3(p.n_chunks, NS), dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL(finish_kernel, dim3(p.n_chunks, NS), dim3(kFinThreads), 0, stream, a);
   return hipGetLastError();
 }
 
