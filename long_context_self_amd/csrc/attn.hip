@@ -204,6 +204,7 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, int g, int
 constexpr int kMW = 4;                      // steps per metadata window
 constexpr int kStageRows = 8;               // collected logit rows (slots x heads) a wave stages
 constexpr int kStageSteps = 4;              // steps staged before one flush (512-byte row runs)
+constexpr int kStageStride = kStageSteps * 32 + 4;   // floats per staged row: 16 bytes of padding
 constexpr int kMT = kMW * kStepTokens;      // token slots per window
 constexpr int kTokPerLane = kMT / 64;       // slots each lane handles per stage
 
@@ -628,7 +629,7 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   // Collected logit rows are staged per wave (kStageRows rows x kStageSteps steps) in an
   // area that starts with the Q tile, free once every wave holds Q in registers
   constexpr bool kCanStage = MODE == MODE_DENSE && !SC;
-  constexpr size_t kStageWave = (size_t)kStageRows * kStageSteps * kStepTokens * 4;
+  constexpr size_t kStageWave = (size_t)kStageRows * kStageStride * 4;
   constexpr size_t kHead = (kCanStage && kWaves * kStageWave > kQBytes) ? kWaves * kStageWave : kQBytes;
   constexpr size_t kLoopBytes = kHead + kWaves * kWaveBytes;
   constexpr size_t kMergeBytes = (size_t)kWaves * QT * kPer * 64 * 4;
@@ -884,11 +885,11 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
       for (int qt = 0; qt < QT; ++qt) {
         if (cslot[qt] < 0) continue;
         const int hh = r0 + 16 * qt + x - rowi[qt] * a.G;
-        float* dst = stg + (cslot[qt] * a.G + hh) * (kStageSteps * kStepTokens) + col;
+        float* dst = stg + (cslot[qt] * a.G + hh) * kStageStride + col;
         *reinterpret_cast<f32x4*>(dst) = S[0][qt] * a.scale;
         *reinterpret_cast<f32x4*>(dst + 16) = S[1][qt] * a.scale;
         if (a.cdup) {
-          float* d2 = dst + a.G * (kStageSteps * kStepTokens);
+          float* d2 = dst + a.G * kStageStride;
           *reinterpret_cast<f32x4*>(d2) = S[0][qt] * a.scale;
           *reinterpret_cast<f32x4*>(d2 + 16) = S[1][qt] * a.scale;
         }
@@ -908,7 +909,7 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
         if (rr >= nrow || cc >= ncol || !((smask >> rr) & 1u)) continue;
         const int c = rr / a.G;
         const int h = g * a.G + (rr - c * a.G);
-        const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rr * (kStageSteps * kStepTokens) + cc);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rr * kStageStride + cc);
         float* dst = a.logits + ((size_t)(b * a.Hq + h) * a.n_cl + c) * a.logits_ld + p0 + cc;
         if (cc + 4 <= ncol) {
           __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
