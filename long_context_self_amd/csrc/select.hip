@@ -39,6 +39,7 @@
 namespace lcs {
 namespace {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -132,11 +133,12 @@ __device__ __forceinline__ void head_score(const SelArgs& a, const float* hb, in
   const int nr = NR2 ? 2 : a.n_rows;
   if (KIND == SCORE_LOGIT_SUM) {
     if (BOTH) {
-      float2 x = *reinterpret_cast<const float2*>(hb);
+      // each logit is read once per call: non-temporal loads (128K x 8: 71.9 -> 68.5 us)
+      f32x2 x = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(hb));
       t0 = x.x;
       t1 = x.y;
       for (int c = 1; c < nr; ++c) {
-        x = *reinterpret_cast<const float2*>(hb + (size_t)c * a.ld);
+        x = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(hb + (size_t)c * a.ld));
         t0 = t0 + x.x;
         t1 = t1 + x.y;
       }
