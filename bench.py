@@ -250,9 +250,9 @@ def measure(ws, steps, warmup, scores=False, refresh_every=1, physical=False):
     outs = torch.empty((B, cfg.n_q, Hq, cfg.d), dtype=torch.float32, device=dev)
     lses = torch.empty((B, cfg.n_q, Hq), dtype=torch.float32, device=dev)
     if scores:
-        logits = [torch.empty((B, cfg.Hkv, L), dtype=torch.float32, device=dev) for _ in range(R)]
+        logits = [torch.empty((B, cfg.Hkv, lcs.row_ld(L)), dtype=torch.float32, device=dev) for _ in range(R)]
     else:
-        logits = [torch.empty((B, Hq, 2, L), dtype=torch.float32, device=dev) for _ in range(R)]
+        logits = [torch.empty((B, Hq, 2, lcs.row_ld(L)), dtype=torch.float32, device=dev) for _ in range(R)]
     idx = [torch.empty((B, n_sets, S), dtype=torch.int32, device=dev) for _ in range(R)]
     cnt = [torch.empty((B, n_sets), dtype=torch.int32, device=dev) for _ in range(R)]
     dout = torch.empty((B, 1, Hq, cfg.d), dtype=torch.float32, device=dev)

@@ -122,7 +122,12 @@ typedef struct {
  *  out          fp32 [B][n_q][Hq][d]: softmax(scale q K^T) V.
  *  logits       fp32 [B][Hq][2][logits_ld]: scale*q.k of the two collected rows
  *               for columns p < prefix_len[b]; other columns are untouched.
- *               logits_ld >= max_prefix_len.
+ *               logits_ld >= max_prefix_len.  Rows 16-byte aligned (logits_ld a
+ *               multiple of 4) take the fast write path; a row stride of 32 floats
+ *               past a multiple of 64 (e.g. round_up(max_prefix_len, 64) + 32)
+ *               spreads the rows' concurrent writes over the HBM channels, where a
+ *               power-of-two stride makes them collide (B = 8 at 128K: 852 us
+ *               against 876-886 us per call).
  *  lse          fp32 [B][n_q][Hq] natural-log sum-exp of the scaled logits, or NULL.
  *  workspace    device scratch of at least lcs_verify_workspace_bytes(...) bytes
  *               (no initialisation needed; contents are clobbered).

@@ -67,9 +67,9 @@ def run(cfg, iters: int, drift: float = 0.1, seed: int = 0, warmup: int = 1, log
     S = cfg.n_sink + cfg.top_k + cfg.n_recent
     pl = torch.from_numpy(kv.prefix_len).to(dev)
     if scores:
-        logits = torch.empty((B, cfg.Hkv, L), dtype=torch.float32, device=dev)
+        logits = torch.empty((B, cfg.Hkv, lcs.row_ld(L)), dtype=torch.float32, device=dev)
     else:
-        logits = torch.empty((B, Hq, 2, L), dtype=torch.float32, device=dev)
+        logits = torch.empty((B, Hq, 2, lcs.row_ld(L)), dtype=torch.float32, device=dev)
     out = torch.empty((B, cfg.n_q, Hq, d), dtype=torch.float32, device=dev)
     dout = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=dev)
     idx = torch.empty((B, n_sets, S), dtype=torch.int32, device=dev)
@@ -115,7 +115,7 @@ def run(cfg, iters: int, drift: float = 0.1, seed: int = 0, warmup: int = 1, log
         if keep_last and it == iters - 1:
             last = {"k_before": kv.k.copy(), "q": qv.view(torch.int16).cpu().numpy().view(np.uint16),
                     "qd": qd[-1].view(torch.int16).cpu().numpy().view(np.uint16),
-                    "out": out.cpu().numpy(), "logits": logits.cpu().numpy(), "idx": idx.cpu().numpy(),
+                    "out": out.cpu().numpy(), "logits": logits[..., :L].cpu().numpy(), "idx": idx.cpu().numpy(),
                     "cnt": cnt.cpu().numpy(), "dout": dout.cpu().numpy(),
                     "tail_len": cfg.n_q + cfg.n_draft}
         tv, ts, td = (e[0].elapsed_time(e[1]) * 1e3, e[1].elapsed_time(e[2]) * 1e3,

@@ -78,7 +78,7 @@ def collect_overhead(cfg, replicas: int, iters: int, seed: int = 0) -> dict:
     ws = torch.empty(lcs.verify_workspace_bytes(layers[0], B, n_q, Hq, L), dtype=torch.uint8, device="cuda")
     res = {}
     for name, rows in sets.items():
-        lg = (torch.empty((B, Hq, len(rows), L), dtype=torch.float32, device="cuda") if rows else None)
+        lg = (torch.empty((B, Hq, len(rows), lcs.row_ld(L)), dtype=torch.float32, device="cuda") if rows else None)
 
         def call(r):
             lcs.verify_attn_rows(layers[r], q, pl, L, scale, rows or [0], out=out, logits=lg, lse=lse,
@@ -117,7 +117,7 @@ def row_scaling(cfg, replicas: int, iters: int, n_qs=(9, 16, 17, 33, 64), seed: 
         B, Hq, L = c.B, c.Hq, c.L
         scale = 1.0 / math.sqrt(c.d)
         out = torch.empty((B, n_q, Hq, c.d), dtype=torch.float32, device="cuda")
-        lg = torch.empty((B, Hq, 2, L), dtype=torch.float32, device="cuda")
+        lg = torch.empty((B, Hq, 2, lcs.row_ld(L)), dtype=torch.float32, device="cuda")
         ws = torch.empty(lcs.verify_workspace_bytes(layers[0], B, n_q, Hq, L), dtype=torch.uint8, device="cuda")
 
         def call(r):
@@ -313,7 +313,7 @@ def latency(cfg, calls: int = 100, warmup: int = 10, flush_mib: int = 512, seed:
     tail = cfg.n_q + 1
     out = torch.empty((B, cfg.n_q, Hq, d), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, cfg.n_q, Hq), dtype=torch.float32, device="cuda")
-    lg = torch.empty((B, Hq, 2, L), dtype=torch.float32, device="cuda")
+    lg = torch.empty((B, Hq, 2, lcs.row_ld(L)), dtype=torch.float32, device="cuda")
     idx = torch.empty((B, n_sets, S), dtype=torch.int32, device="cuda")
     cnt = torch.empty((B, n_sets), dtype=torch.int32, device="cuda")
     dout = torch.empty((B, 1, Hq, d), dtype=torch.float32, device="cuda")

@@ -122,7 +122,7 @@ def run(shape: StackShape, gammas=(1, 2, 4, 8, 16, 32, 64), iters: int = 10, war
         ws_v = torch.empty(lcs.verify_workspace_bytes(caches[0], 1, n_q, S.Hq, L), dtype=torch.uint8, device=dev)
         ws_n = torch.empty(lcs.nsa_workspace_bytes(caches[0], 1, n_q, S.Hq, S.blocks_per_row, n_q, max_cmp,
                                                    S.window), dtype=torch.uint8, device=dev)
-        logits = torch.empty((1, S.Hq, 2, L), dtype=torch.float32, device=dev)
+        logits = torch.empty((1, S.Hq, 2, lcs.row_ld(L)), dtype=torch.float32, device=dev)
         out = torch.empty((1, n_q, S.Hq, S.d), dtype=torch.float32, device=dev)
         x0 = randn(n_q, S.hidden)
 

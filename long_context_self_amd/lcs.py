@@ -138,6 +138,14 @@ def verify_workspace_bytes(kv: PagedKV, B: int, n_q: int, Hq: int, max_prefix_le
     return load().lcs_verify_workspace_bytes(B, n_q, Hq, ctypes.byref(d), max_prefix_len)
 
 
+def row_ld(n: int) -> int:
+    """Row stride (in floats) for fp32 logit or score rows of n positions: n rounded up to
+    64, plus 32.  Rows then start 128 bytes past a multiple of 256 bytes apart, which
+    spreads the verify kernel's concurrent row writes over the HBM channels; a
+    power-of-two stride makes them collide."""
+    return (max(n, 1) + 63) // 64 * 64 + 32
+
+
 def verify_attn(kv: PagedKV, q: torch.Tensor, prefix_len: torch.Tensor, max_prefix_len: int,
                 scale: float, collect_rows: Tuple[int, int], tree_mask: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
