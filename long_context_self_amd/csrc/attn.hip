@@ -539,48 +539,12 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int pid, int r, int
     a.lse[(size_t)(b * a.n_q + i) * a.Hq + h] = (Ls > 0.f) ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
 }
 
-// Split-order merge of splits [s0, s0 + n) of q-row r (n <= 128): running max M (log2
-// units), sum Ls and the unnormalised output columns of this lane.  One wave.
-template <int D>
-__device__ __forceinline__ void merge_range(const float* base, size_t pstride, int r, int s0, int n, int lane,
-                                            float& M, float& Ls, float (&acc)[D / 64]) {
-  constexpr int CPL = D / 64;
-  const float* mcol = base + (size_t)kMaxRowsPerWG * D + r;
-  const float* ocol = base + (size_t)r * D + CPL * lane;
-  float mv[2], lv[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int sp = lane + 64 * u;
-    mv[u] = -INFINITY;
-    lv[u] = 0.f;
-    if (sp < n) {
-      const size_t o = (size_t)(s0 + sp) * pstride;
-      mv[u] = mcol[o];
-      lv[u] = mcol[o + kMaxRowsPerWG];
-    }
-  }
-  M = fmaxf(mv[0], mv[1]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  const float Ms = (M == -INFINITY) ? 0.f : M;
-  float wv[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) wv[u] = __builtin_amdgcn_exp2f(mv[u] - Ms);
-  Ls = wv[0] * lv[0] + wv[1] * lv[1];
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off);
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-#pragma unroll 8
-  for (int sp = 0; sp < n; ++sp) {
-    const float w = lane_f(sp < 64 ? wv[0] : wv[1], sp & 63);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] += w * ocol[(size_t)(s0 + sp) * pstride + c];
-  }
-}
-
-// NSA: merge each branch's splits, then out = sum over branches of gate * branch output;
-// lse [B][n_q][Hq][3] holds each branch's log-sum-exp (-inf for a branch that saw nothing).
+// NSA: merge each branch's splits in split order, then out = sum over branches of gate *
+// branch output; lse [B][n_q][Hq][3] holds each branch's log-sum-exp (-inf for a branch
+// that saw nothing).  The launch's splits are the compression, selection and window
+// branches' in that order.  One pass: lane s loads the (m, l) of split s and every lane
+// its columns of all splits (the first kChunk at once), as in merge_row, and each split
+// adds into its own branch's accumulator.
 template <int D>
 __device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int pid, int r, int lane) {
   constexpr int CPL = D / 64;
@@ -588,8 +552,82 @@ __device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int pid, int r,
   const int bg = pid / a.n_rc;
   const int g = bg % a.Hkv;
   const int b = bg / a.Hkv;
+  const int ns = a.n_split;                     // 3 .. kMaxSplits
+  const int e0 = a.ns0, e1 = a.ns0 + a.ns1;     // first selection split, first window split
   const size_t pstride = (size_t)kMaxRowsPerWG * (D + 2);
-  const float* base = a.part + (size_t)pid * a.n_split * pstride;
+  const float* base = a.part + (size_t)pid * ns * pstride;
+  const float* mcol = base + (size_t)kMaxRowsPerWG * D + r;
+  const float* ocol = base + (size_t)r * D + CPL * lane;
+  float cur[kChunk][CPL], nxt[kChunk][CPL];
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) cur[u][c] = ocol[(size_t)min(u, ns - 1) * pstride + c];
+  float mv[2], lv[2];
+  int bv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int sp = lane + 64 * u;
+    const size_t o = (size_t)min(sp, ns - 1) * pstride;
+    mv[u] = mcol[o];
+    lv[u] = mcol[o + kMaxRowsPerWG];
+    bv[u] = (sp >= e1) ? 2 : (sp >= e0 ? 1 : 0);
+    if (sp >= ns) { mv[u] = -INFINITY; lv[u] = 0.f; }
+  }
+  float M[3], Ls[3], wv[2];
+#pragma unroll
+  for (int br = 0; br < 3; ++br) {
+    float x = fmaxf(bv[0] == br ? mv[0] : -INFINITY, bv[1] == br ? mv[1] : -INFINITY);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    M[br] = x;
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const float Mb = (bv[u] == 0) ? M[0] : (bv[u] == 1 ? M[1] : M[2]);
+    wv[u] = __builtin_amdgcn_exp2f(mv[u] - ((Mb == -INFINITY) ? 0.f : Mb));
+  }
+#pragma unroll
+  for (int br = 0; br < 3; ++br) {
+    // butterfly sum: every lane ends with the same, run-to-run fixed value
+    float x = (bv[0] == br ? wv[0] * lv[0] : 0.f) + (bv[1] == br ? wv[1] * lv[1] : 0.f);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    Ls[br] = x;
+  }
+  float acc[3][CPL];
+#pragma unroll
+  for (int br = 0; br < 3; ++br)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[br][c] = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += kChunk) {
+    const bool more = c0 + kChunk < ns;
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) nxt[u][c] = ocol[(size_t)min(c0 + kChunk + u, ns - 1) * pstride + c];
+    }
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int sp = c0 + u;
+      if (sp >= ns) break;
+      const float w = lane_f(sp < 64 ? wv[0] : wv[1], sp & 63);
+      const int br = (sp >= e1) ? 2 : (sp >= e0 ? 1 : 0);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        if (br == 0) acc[0][c] += w * cur[u][c];
+        else if (br == 1) acc[1][c] += w * cur[u][c];
+        else acc[2][c] += w * cur[u][c];
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) cur[u][c] = nxt[u][c];
+    }
+  }
   const int rr = rc * kMaxRowsPerWG + r;
   const int i = rr / a.G;
   const int h = g * a.G + (rr - i * a.G);
@@ -597,17 +635,14 @@ __device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int pid, int r,
   float res[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) res[c] = 0.f;
-  const int s0[3] = {0, a.ns0, a.ns0 + a.ns1};
-  const int ns[3] = {a.ns0, a.ns1, a.ns2};
 #pragma unroll
   for (int br = 0; br < 3; ++br) {
-    float M, Ls, acc[CPL];
-    merge_range<D>(base, pstride, r, s0[br], ns[br], lane, M, Ls, acc);
     const float gate = a.gates[qh * 3 + br];
-    const float f = (Ls > 0.f) ? gate / Ls : 0.f;
+    const float f = (Ls[br] > 0.f) ? gate / Ls[br] : 0.f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) res[c] += f * acc[c];
-    if (lane == 0 && a.lse != nullptr) a.lse[qh * 3 + br] = (Ls > 0.f) ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+    for (int c = 0; c < CPL; ++c) res[c] += f * acc[br][c];
+    if (lane == 0 && a.lse != nullptr)
+      a.lse[qh * 3 + br] = (Ls[br] > 0.f) ? (M[br] + __log2f(Ls[br])) * kLn2 : -INFINITY;
   }
   float* op = a.out + qh * D + CPL * lane;
 #pragma unroll
