@@ -1289,34 +1289,57 @@ __global__ void __launch_bounds__(256) compress_kernel(AttnArgs a, const int32_t
                                                        uint16_t* vc) {
   constexpr int CH = D / 8;           // 16-byte chunks per row
   constexpr int RPW = 256 / CH;       // compressed rows per workgroup
+  constexpr int kPgCap = 512;         // block-table entries staged in LDS per workgroup
+  constexpr int kBatch = 8;           // tokens whose K and V loads go out together
+  __shared__ int32_t s_pg[kPgCap];
   const int g = blockIdx.y, b = blockIdx.z;
-  const int i = blockIdx.x * RPW + (int)threadIdx.x / CH;
+  const int i_base = blockIdx.x * RPW;
+  const int i = i_base + (int)threadIdx.x / CH;
   const int c = (int)threadIdx.x % CH;
-  if (i >= a.max_cmp) return;
+  if (i_base >= a.max_cmp) return;
   const int P = 1 << a.lg_page;
   const int L = min(max(prefix_len[b], 0), a.max_prefix_len);
   const int n = (L < a.cmp_len) ? 0 : min((L - a.cmp_len) / a.cmp_stride + 1, a.max_cmp);
+  const int32_t* bt = a.bt + (size_t)b * a.max_pages;
+  // the block-table entries of the workgroup's token span go to LDS in one round trip,
+  // so that every token's K and V loads can go out without waiting on its page
+  const int i_last = min(i_base + RPW, n) - 1;
+  const int pg0 = (i_base * a.cmp_stride) >> a.lg_page;
+  const int npg = (i_last >= i_base) ? ((i_last * a.cmp_stride + a.cmp_len - 1) >> a.lg_page) - pg0 + 1 : 0;
+  const bool staged = npg <= kPgCap;
+  if (staged)
+    for (int e = threadIdx.x; e < npg; e += 256) s_pg[e] = bt[pg0 + e];
+  __syncthreads();
   u32x4 ko = u32x4{0, 0, 0, 0}, vo = u32x4{0, 0, 0, 0};
   if (i < n) {
     float ks[8], vs[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) ks[e] = vs[e] = 0.f;
     const int p0 = i * a.cmp_stride;
-    const int32_t* bt = a.bt + (size_t)b * a.max_pages;
-#pragma unroll 4
-    for (int t = 0; t < a.cmp_len; ++t) {
-      const int p = p0 + t;
-      const int page = bt[p >> a.lg_page];
-      if ((unsigned)page >= (unsigned)a.num_pages) continue;   // outside the cache: skipped
-      const size_t row = ((size_t)(page * a.Hkv + g) << a.lg_page) | (size_t)(p & (P - 1));
-      const u32x4 kk = *reinterpret_cast<const u32x4*>(a.k + row * D + 8 * c);
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(a.v + row * D + 8 * c);
+    for (int t0 = 0; t0 < a.cmp_len; t0 += kBatch) {
+      u32x4 kk[kBatch], vv[kBatch];
+      bool ok[kBatch];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        ks[2 * w] += bf16_to_f32(kk[w] & 0xffffu);
-        ks[2 * w + 1] += bf16_to_f32(kk[w] >> 16);
-        vs[2 * w] += bf16_to_f32(vv[w] & 0xffffu);
-        vs[2 * w + 1] += bf16_to_f32(vv[w] >> 16);
+      for (int u = 0; u < kBatch; ++u) {
+        const int p = p0 + t0 + u;
+        int page = -1;
+        if (t0 + u < a.cmp_len) page = staged ? s_pg[(p >> a.lg_page) - pg0] : bt[p >> a.lg_page];
+        ok[u] = (unsigned)page < (unsigned)a.num_pages;   // outside the cache: skipped
+        // a skipped token loads row 0 (always in bounds) and is not added
+        const size_t row = ok[u] ? (((size_t)(page * a.Hkv + g) << a.lg_page) | (size_t)(p & (P - 1))) : 0;
+        kk[u] = *reinterpret_cast<const u32x4*>(a.k + row * D + 8 * c);
+        vv[u] = *reinterpret_cast<const u32x4*>(a.v + row * D + 8 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (!ok[u]) continue;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          ks[2 * w] += bf16_to_f32(kk[u][w] & 0xffffu);
+          ks[2 * w + 1] += bf16_to_f32(kk[u][w] >> 16);
+          vs[2 * w] += bf16_to_f32(vv[u][w] & 0xffffu);
+          vs[2 * w + 1] += bf16_to_f32(vv[u][w] >> 16);
+        }
       }
     }
     const float inv = 1.f / (float)a.cmp_len;     // a power of two: exact
@@ -1326,6 +1349,7 @@ __global__ void __launch_bounds__(256) compress_kernel(AttnArgs a, const int32_t
       vo[w] = pack_bf16(vs[2 * w] * inv, vs[2 * w + 1] * inv);
     }
   }
+  if (i >= a.max_cmp) return;
   const size_t o = ((size_t)(b * a.Hkv + g) * a.max_cmp + i) * D + 8 * c;
   *reinterpret_cast<u32x4*>(kc + o) = ko;
   *reinterpret_cast<u32x4*>(vc + o) = vo;
