@@ -109,13 +109,19 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lptr_t)p);
 }
-// 16 bytes per lane from src into LDS at dst + 16 * lane (dst wave-uniform).  K/V rows
-// are read once per call, so the load carries the non-temporal hint: measured on the
-// 128K x 8 step, verify 950 -> 913 us and a draft step 35.6 -> 32.5 us, with the
-// collected logit rows (streaming stores) and the selector unchanged.
+// 16 bytes per lane from src into LDS at dst + 16 * lane (dst wave-uniform).  NT: the
+// K/V rows are read once per call, so the load carries the non-temporal hint (measured
+// on the 128K x 8 step: verify 950 -> 913 us, a draft step 35.6 -> 32.5 us).  Launches
+// whose row chunks re-read the same K/V (more than 48 q-rows per KV group) load without
+// it, so that the re-reads hit the caches.
+template <bool NT>
 __device__ __forceinline__ void dma16(const void* src, void* dst) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds_addr(dst))
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds_addr(dst))
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr(dst))
+                 : "memory", "m0");
 }
 // 4 bytes per lane from src into LDS at dst + 4 * lane (dst wave-uniform).
 __device__ __forceinline__ void dma4(const void* src, void* dst) {
@@ -393,7 +399,7 @@ __device__ __forceinline__ void meta_stage_c(const AttnArgs& a, const SeqInfo& s
 // it fetches global chunk p ^ (token % RCH), so that the later MFMA-layout reads
 // (16 lanes, one chunk index each, 16 different rows) fall on different banks.
 // Tile tt occupies blocks [tt*16/(64/RCH), ...) of 1 KB; V: token t -> block KDMA+t.
-template <int D>
+template <int D, bool NT>
 __device__ __forceinline__ void step_dma(const uint16_t* kb, const uint16_t* vb, const int32_t* rows, char* slot,
                                          int lane, int x, int j) {
   constexpr int RCH = D / 8;          // 16-byte chunks per row
@@ -406,14 +412,14 @@ __device__ __forceinline__ void step_dma(const uint16_t* kb, const uint16_t* vb,
     for (int i = 0; i < IPT; ++i) {
       const int tok = 16 * tt + RPI * i + rq;
       const int c = p ^ (tok % RCH);
-      dma16(kb + (size_t)max(rows[tok], 0) * D + 8 * c, slot + (tt * IPT + i) * 1024);
+      dma16<NT>(kb + (size_t)max(rows[tok], 0) * D + 8 * c, slot + (tt * IPT + i) * 1024);
     }
   const int4 rv0 = *reinterpret_cast<const int4*>(rows + 4 * j);
   const int4 rv1 = *reinterpret_cast<const int4*>(rows + 16 + 4 * j);
   const int rv[8] = {rv0.x, rv0.y, rv0.z, rv0.w, rv1.x, rv1.y, rv1.z, rv1.w};
   const int dx = 8 * (x & (D / 8 - 1));   // d = 64: lanes x >= 8 repeat x - 8 (rows unused)
 #pragma unroll
-  for (int t = 0; t < 8; ++t) dma16(vb + (size_t)max(rv[t], 0) * D + dx, slot + (2 * IPT + t) * 1024);
+  for (int t = 0; t < 8; ++t) dma16<NT>(vb + (size_t)max(rv[t], 0) * D + dx, slot + (2 * IPT + t) * 1024);
 }
 
 // The same DMAs one at a time, so that a refill can be spread through the compute of
@@ -434,16 +440,16 @@ __device__ __forceinline__ void dma_rows(const int32_t* rows, int lane, int j, i
   sr[G::NK + 0] = rv0.x; sr[G::NK + 1] = rv0.y; sr[G::NK + 2] = rv0.z; sr[G::NK + 3] = rv0.w;
   sr[G::NK + 4] = rv1.x; sr[G::NK + 5] = rv1.y; sr[G::NK + 6] = rv1.z; sr[G::NK + 7] = rv1.w;
 }
-template <int D, int n>
+template <int D, int n, bool NT>
 __device__ __forceinline__ void dma_piece(const uint16_t* kb, const uint16_t* vb, const int (&sr)[DmaGeom<D>::N],
                                           char* slot, int lane, int x) {
   using G = DmaGeom<D>;
   if (n < G::NK) {
     const int tok = 16 * (n / G::IPT) + G::RPI * (n % G::IPT) + lane / G::RCH;
     const int c = (lane % G::RCH) ^ (tok % G::RCH);
-    dma16(kb + (size_t)max(sr[n], 0) * D + 8 * c, slot + n * 1024);
+    dma16<NT>(kb + (size_t)max(sr[n], 0) * D + 8 * c, slot + n * 1024);
   } else {
-    dma16(vb + (size_t)max(sr[n], 0) * D + 8 * (x & (D / 8 - 1)), slot + n * 1024);
+    dma16<NT>(vb + (size_t)max(sr[n], 0) * D + 8 * (x & (D / 8 - 1)), slot + n * 1024);
   }
 }
 
@@ -662,7 +668,7 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
 
 // SC: dense verify that writes per-KV-head partial scores of the two collected rows
 // instead of their logits (the selector's per-head sum, done here, 2G times fewer bytes)
-template <int D, int QT, int MODE, bool SC = false>
+template <int D, int QT, int MODE, bool SC = false, bool NT = true>
 __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   constexpr int KS = D / 32;                  // k-steps of the QK^T product
   constexpr int NDMA = DmaGeom<D>::N;         // 16-byte DMAs per lane per step
@@ -796,8 +802,8 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   if ((MODE != MODE_LIST_SHARED || a.phys) && w0 < w1) {
     meta_stage_c<MODE>(a, si, g, w0, w1, colmask, lane, wm, 0);
     wait_lgkm0();
-    step_dma<D>(kb, vb, wm.row[0], ring, lane, x, j);
-    if (w0 + 1 < w1) step_dma<D>(kb, vb, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
+    step_dma<D, NT>(kb, vb, wm.row[0], ring, lane, x, j);
+    if (w0 + 1 < w1) step_dma<D, NT>(kb, vb, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
   }
   // Q in LDS.  An LDS-only barrier: __syncthreads would also wait for those DMAs.
   wait_lgkm0();
@@ -826,8 +832,8 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
       wait_vm<0>();
       meta_stage_c<MODE>(a, si, g, w0, w1, colmask, lane, wm, 0);
       wait_lgkm0();
-      step_dma<D>(kb, vb, wm.row[0], ring, lane, x, j);
-      if (w0 + 1 < w1) step_dma<D>(kb, vb, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
+      step_dma<D, NT>(kb, vb, wm.row[0], ring, lane, x, j);
+      if (w0 + 1 < w1) step_dma<D, NT>(kb, vb, wm.row[0] + kStepTokens, ring + kSlot, lane, x, j);
     }
     // Software pipeline.  Iteration s waits for slot s and moves it to registers, issues
     // the metadata stage, runs S(s) on the matrix core, stores S(s)'s collected logits,
@@ -1005,7 +1011,7 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
       pv([&](auto ec) {
         constexpr int e = decltype(ec)::value;
         static_for<e * NDMA / 8, (e + 1) * NDMA / 8>([&](auto nc) {
-          if (FAST || dma_due) dma_piece<D, decltype(nc)::value>(kb, vb, sr, slot, lane, x);
+          if (FAST || dma_due) dma_piece<D, decltype(nc)::value, NT>(kb, vb, sr, slot, lane, x);
         });
       });
       bool grow_any = false;
@@ -1372,7 +1378,10 @@ hipError_t launch_main_mode(const AttnPlan& p, const AttnArgs& a, hipStream_t st
   if (!launched) switch (p.QT) {
     case 1: hipLaunchKernelGGL((attn_kernel<D, 1, MODE>), grid, dim3(256), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((attn_kernel<D, 2, MODE>), grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((attn_kernel<D, 3, MODE>), grid, dim3(256), 0, stream, a); break;
+    default:   // several row chunks re-read the same K/V: cached loads
+      if (p.n_rc > 1) hipLaunchKernelGGL((attn_kernel<D, 3, MODE, false, false>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((attn_kernel<D, 3, MODE>), grid, dim3(256), 0, stream, a);
+      break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (MODE != MODE_NSA && p.n_split == 1)) return e;
