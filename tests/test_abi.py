@@ -231,3 +231,14 @@ def test_scores_host_errors():
     assert ss(ld=99) == lcs.LCS_E_SHAPE
     assert ss(mode=9) == lcs.LCS_E_ARG
     assert ss(B=0) == lcs.LCS_OK
+
+
+def test_row_ld_avoids_power_of_two_strides():
+    """lcs.row_ld: at least n, a multiple of 4 (16-byte rows for the fast write path),
+    and 32 floats past a multiple of 64, so no row stride is a power of two."""
+    from long_context_self_amd import lcs
+    for n in (1, 5, 63, 64, 65, 4096, 32768, 65536, 131072, 131073):
+        ld = lcs.row_ld(n)
+        assert ld >= n and ld % 4 == 0 and ld % 64 == 32
+        assert ld & (ld - 1) != 0
+        assert ld - n < 96
