@@ -182,3 +182,31 @@ def test_empty_batch_and_errors():
     assert e.value.status == lcs.LCS_E_ARG
     # B = 0 is a no-op
     lcs.verify_attn(dkv, q[:0], pl, cfg.L, 0.125, (0, cfg.n_q - 1))
+
+
+@pytest.mark.parametrize("mode", ["shared", "per_kv_head"])
+def test_padded_row_stride_staged_rows_and_select(mode):
+    # logit rows at the stride lcs.row_ld gives (32 floats past a multiple of 64): the
+    # staged 512-byte row runs land at that stride, and select reading the padded rows
+    # picks exactly what it picks from the same rows packed at stride L
+    torch, lcs = require_gpu()
+    cfg = synth.CONFIGS["llama8b_32k"].with_(L=3000, B=2)
+    lens = [3000, 2960]
+    kv = synth.make_paged_kv(cfg, seed=5, lens=lens)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=5)
+    maxL = max(lens)
+    ld = lcs.row_ld(maxL)
+    assert ld % 64 == 32 and ld > maxL
+    check(cfg, kv, q, ld_extra=ld - maxL)
+    _, logits, _ = run_verify(cfg, kv, q, ld_extra=ld - maxL)
+    pl = i32_dev(kv.prefix_len, torch)
+    padded = torch.from_numpy(np.nan_to_num(logits, nan=0.0)).cuda()
+    packed = padded[..., :maxL].contiguous()
+    i1, c1 = lcs.select_topk(padded, pl, maxL, cfg.Hkv, mode, 256, 4, 64)
+    i2, c2 = lcs.select_topk(packed, pl, maxL, cfg.Hkv, mode, 256, 4, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    n = c1.cpu().numpy()
+    a, b = i1.cpu().numpy(), i2.cpu().numpy()
+    for s in np.ndindex(*n.shape):
+        assert np.array_equal(a[s][:n[s]], b[s][:n[s]])
