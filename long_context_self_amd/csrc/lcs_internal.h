@@ -168,11 +168,13 @@ struct SelArgs {
 
 struct SelPlan {
   int32_t n_sets, item_cap, n_chunks, n_pos_chunks;
+  int32_t fin_threads;   // threads of a finish workgroup (256 or 1024)
   size_t keys_bytes, hist_bytes, cc_bytes, cand_bytes, ca_bytes, thr_bytes, total_bytes;
 };
 
+// cus: compute units of the device (0: the MI355X's 256); only the launch shape depends on it
 SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t max_len,
-                    int32_t block_size);
+                    int32_t block_size, int32_t cus = 0);
 
 hipError_t select_launch(const SelPlan& plan, SelArgs args, void* workspace, hipStream_t stream);
 

@@ -345,17 +345,21 @@ __device__ __forceinline__ int32_t emit_id(const SelArgs& a, int b, int it) {
 }
 
 constexpr int kFinLDS = 8192;      // candidates a workgroup holds in LDS
-constexpr int kFinThreads = 1024;  // threads of a finish workgroup
-constexpr int kFinIPT = kItemChunk / kFinThreads;   // consecutive items per thread in finish
-constexpr int kFinBPT = 2048 / kFinThreads;         // radix bins per thread in a pass
 
 // Boundary and output of one 4096-item chunk (one workgroup per chunk and set).  Every
 // chunk's workgroup finds the exact boundary composite itself: the radix passes over
 // the first-digit bin's candidates cost less than one more launch.  It then places its
 // kept items after the sink window, the kept items of the chunks before it (their items
 // above the bin, counted by collect, and their candidates at or above the boundary) and
-// the kept items before it in this chunk.
-__global__ void __launch_bounds__(kFinThreads) finish_kernel(SelArgs a) {
+// the kept items before it in this chunk.  FT threads: 1024 when the chunks of all sets
+// fit in one round of the CUs, else 256 (fewer waves make the radix passes' barriers
+// cheaper when several workgroups share a CU; measured: 64K x 4 per-KV-head sets 52.7 ->
+// 50.2 us, while 128K x 8 and 32K are faster with 1024).
+template <int FT>
+__global__ void __launch_bounds__(FT) finish_kernel(SelArgs a) {
+  constexpr int kFinThreads = FT;
+  constexpr int kFinIPT = kItemChunk / FT;   // consecutive items per thread
+  constexpr int kFinBPT = 2048 / FT;         // radix bins per thread in a pass
   const int set = blockIdx.y;
   const int b = set / a.n_sets;
   const Win w = window(a, b);
@@ -508,7 +512,7 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(SelArgs a) {
 }  // namespace
 
 SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t max_len,
-                    int32_t block_size) {
+                    int32_t block_size, int32_t cus) {
   SelPlan p{};
   p.n_sets = (mode == LCS_SEL_SHARED) ? 1 : Hkv;
   const size_t NS = (size_t)B * p.n_sets;
@@ -518,6 +522,7 @@ SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t ma
   p.item_cap = (int32_t)align_up((size_t)items, 16);
   p.n_chunks = (int32_t)((items + kItemChunk - 1) / kItemChunk);
   p.n_pos_chunks = (int32_t)(((long long)(max_len > 0 ? max_len : 1) + kScorePos - 1) / kScorePos);
+  p.fin_threads = ((long long)p.n_chunks * (long long)NS > (cus > 0 ? cus : kDefaultCUs)) ? 256 : 1024;
   p.keys_bytes = align_up(NS * p.item_cap * 4, 256);
   p.hist_bytes = align_up(NS * kHistBins * 4, 256);
   p.cc_bytes = align_up(NS * 4, 256);
@@ -555,7 +560,10 @@ hipError_t select_launch(const SelPlan& p, SelArgs a, void* workspace, hipStream
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(collect_kernel, dim3(p.n_chunks, NS), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(finish_kernel, dim3(p.n_chunks, NS), dim3(kFinThreads), 0, stream, a);
+  if (p.fin_threads == 256)
+    hipLaunchKernelGGL(finish_kernel<256>, dim3(p.n_chunks, NS), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(finish_kernel<1024>, dim3(p.n_chunks, NS), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
