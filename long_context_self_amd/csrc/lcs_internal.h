@@ -164,10 +164,11 @@ struct SelArgs {
   uint32_t* chunk_above; // [NS][n_chunks]
   uint64_t* thr;         // [NS][2]
   int32_t item_cap, n_chunks, n_pos_chunks;
+  int32_t score_iters;   // 512-position chunks one score workgroup covers (1 in block mode)
 };
 
 struct SelPlan {
-  int32_t n_sets, item_cap, n_chunks, n_pos_chunks;
+  int32_t n_sets, item_cap, n_chunks, n_pos_chunks, score_iters;
   int32_t fin_threads;   // threads of a finish workgroup (256 or 1024)
   size_t keys_bytes, hist_bytes, cc_bytes, cand_bytes, ca_bytes, thr_bytes, total_bytes;
 };

@@ -20,7 +20,9 @@
 //  * score_kernel streams the two logit rows of every head once (the only HBM-
 //    sized read), writes an order-preserving uint32 key per item, and builds a
 //    4096-bin histogram of the top 12 key bits in LDS, flushed with one global
-//    atomic per non-empty bin.
+//    atomic per non-empty bin.  A workgroup covers one to eight 512-position chunks,
+//    as many as still leave four workgroups per CU, so that large calls clear and
+//    flush fewer histograms.
 //  * collect_kernel finds the bin that holds the k-th item, counts the items above
 //    it per 4096-item chunk and appends the bin's items as 44-bit composites
 //    (20 low key bits, then the complemented index) to a candidate list; each
@@ -169,8 +171,11 @@ __global__ void __launch_bounds__(256) score_kernel(SelArgs a) {
   const int s = set - b * a.n_sets;
   const Win w = window(a, b);
   if (w.all || a.top_k == 0) return;
-  const int p0 = blockIdx.x * kScorePos;
-  if (p0 >= w.L) return;
+  // a workgroup covers score_iters consecutive kScorePos-position chunks (one in block
+  // mode) and flushes its histogram once
+  const int iters = (a.mode == LCS_SEL_BLOCK) ? 1 : a.score_iters;
+  const int pbase = blockIdx.x * iters * kScorePos;
+  if (pbase >= w.L) return;
   const int tid = threadIdx.x;
   const int h0 = (a.mode == LCS_SEL_SHARED) ? 0 : s * a.G;
   const int nh = (a.mode == LCS_SEL_SHARED) ? a.Hq : a.G;
@@ -183,52 +188,56 @@ __global__ void __launch_bounds__(256) score_kernel(SelArgs a) {
     for (int i = tid; i < kScorePos / 4; i += 256) bm[i] = 0;
   __syncthreads();
 
-  const int p = p0 + 2 * tid;          // this thread's two positions
-  float acc0 = 0.f, acc1 = 0.f;
-  const int nr = NR2 ? 2 : a.n_rows;
-  const float* base = a.logits + (size_t)b * a.Hq * nr * a.ld;
-  if (a.vec4 && p + 1 < w.L) {
+  uint32_t* keys = a.keys + (size_t)set * a.item_cap;
+  for (int it = 0; it < iters; ++it) {
+    const int p0 = pbase + it * kScorePos;
+    if (p0 >= w.L) break;
+    const int p = p0 + 2 * tid;          // this thread's two positions
+    float acc0 = 0.f, acc1 = 0.f;
+    const int nr = NR2 ? 2 : a.n_rows;
+    const float* base = a.logits + (size_t)b * a.Hq * nr * a.ld;
+    if (a.vec4 && p + 1 < w.L) {
 #pragma unroll 8
-    for (int hh = 0; hh < nh; ++hh) {
-      float t0, t1;
-      head_score<KIND, NR2, true>(a, base + (size_t)(h0 + hh) * nr * a.ld + p, b, h0 + hh, t0, t1);
-      acc0 = acc0 + t0;
-      acc1 = acc1 + t1;
-    }
-  } else if (p < w.L) {
-    for (int hh = 0; hh < nh; ++hh) {
-      const float* hb = base + (size_t)(h0 + hh) * nr * a.ld + p;
-      float t0, t1, u0, u1;
-      head_score<KIND, NR2, false>(a, hb, b, h0 + hh, t0, t1);
-      acc0 = acc0 + t0;
-      if (p + 1 < w.L) {
-        head_score<KIND, NR2, false>(a, hb + 1, b, h0 + hh, u0, u1);
-        acc1 = acc1 + u0;
+      for (int hh = 0; hh < nh; ++hh) {
+        float t0, t1;
+        head_score<KIND, NR2, true>(a, base + (size_t)(h0 + hh) * nr * a.ld + p, b, h0 + hh, t0, t1);
+        acc0 = acc0 + t0;
+        acc1 = acc1 + t1;
+      }
+    } else if (p < w.L) {
+      for (int hh = 0; hh < nh; ++hh) {
+        const float* hb = base + (size_t)(h0 + hh) * nr * a.ld + p;
+        float t0, t1, u0, u1;
+        head_score<KIND, NR2, false>(a, hb, b, h0 + hh, t0, t1);
+        acc0 = acc0 + t0;
+        if (p + 1 < w.L) {
+          head_score<KIND, NR2, false>(a, hb + 1, b, h0 + hh, u0, u1);
+          acc1 = acc1 + u0;
+        }
       }
     }
-  }
-  const uint32_t k0 = f2key(acc0), k1 = f2key(acc1);
-  uint32_t* keys = a.keys + (size_t)set * a.item_cap;
-  if (a.mode != LCS_SEL_BLOCK) {
-    if (p + 1 < w.L) {
-      *reinterpret_cast<uint2*>(keys + p) = make_uint2(k0, k1);
-    } else if (p < w.L) {
-      keys[p] = k0;
+    const uint32_t k0 = f2key(acc0), k1 = f2key(acc1);
+    if (a.mode != LCS_SEL_BLOCK) {
+      if (p + 1 < w.L) {
+        *reinterpret_cast<uint2*>(keys + p) = make_uint2(k0, k1);
+      } else if (p < w.L) {
+        keys[p] = k0;
+      }
+      if (p >= w.lo && p < w.hi) atomicAdd(&lh[k0 >> 20], 1u);
+      if (p + 1 >= w.lo && p + 1 < w.hi) atomicAdd(&lh[k1 >> 20], 1u);
+    } else if (!a.block_lse) {
+      if (p < w.L) atomicMax(&bm[(2 * tid) >> a.lg_bs], k0);
+      if (p + 1 < w.L) atomicMax(&bm[(2 * tid + 1) >> a.lg_bs], k1);
+    } else {
+      sg[2 * tid] = acc0;
+      sg[2 * tid + 1] = acc1;
     }
-    if (p >= w.lo && p < w.hi) atomicAdd(&lh[k0 >> 20], 1u);
-    if (p + 1 >= w.lo && p + 1 < w.hi) atomicAdd(&lh[k1 >> 20], 1u);
-  } else if (!a.block_lse) {
-    if (p < w.L) atomicMax(&bm[(2 * tid) >> a.lg_bs], k0);
-    if (p + 1 < w.L) atomicMax(&bm[(2 * tid + 1) >> a.lg_bs], k1);
-  } else {
-    sg[2 * tid] = acc0;
-    sg[2 * tid + 1] = acc1;
   }
   __syncthreads();
   if (a.mode == LCS_SEL_BLOCK) {
     const int bs = 1 << a.lg_bs;
     const int nbc = kScorePos >> a.lg_bs;
-    const int c0 = p0 >> a.lg_bs;
+    const int c0 = pbase >> a.lg_bs;
     for (int cl = tid; cl < nbc; cl += 256) {
       const int c = c0 + cl;
       if (c < w.n) {
@@ -345,6 +354,8 @@ __device__ __forceinline__ int32_t emit_id(const SelArgs& a, int b, int it) {
 }
 
 constexpr int kFinLDS = 8192;      // candidates a workgroup holds in LDS
+constexpr int kMaxScoreIters = 8;  // most kScorePos chunks one score workgroup covers
+constexpr long long kScoreWGsPerCU = 4;   // score workgroups per CU to keep
 
 // Boundary and output of one 4096-item chunk (one workgroup per chunk and set).  Every
 // chunk's workgroup finds the exact boundary composite itself: the radix passes over
@@ -521,7 +532,16 @@ SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t ma
   if (items < 1) items = 1;
   p.item_cap = (int32_t)align_up((size_t)items, 16);
   p.n_chunks = (int32_t)((items + kItemChunk - 1) / kItemChunk);
-  p.n_pos_chunks = (int32_t)(((long long)(max_len > 0 ? max_len : 1) + kScorePos - 1) / kScorePos);
+  // score workgroups: several chunks each while that still leaves kScoreWGsPerCU
+  // workgroups per CU (fewer histogram clears and flushes)
+  const long long pos_chunks = ((long long)(max_len > 0 ? max_len : 1) + kScorePos - 1) / kScorePos;
+  const long long ncu = cus > 0 ? cus : kDefaultCUs;
+  p.score_iters = 1;
+  if (mode != LCS_SEL_BLOCK)
+    while (p.score_iters < kMaxScoreIters &&
+           pos_chunks * (long long)NS / (2 * p.score_iters) >= kScoreWGsPerCU * ncu)
+      p.score_iters *= 2;
+  p.n_pos_chunks = (int32_t)((pos_chunks + p.score_iters - 1) / p.score_iters);
   p.fin_threads = ((long long)p.n_chunks * (long long)NS > (cus > 0 ? cus : kDefaultCUs)) ? 256 : 1024;
   p.keys_bytes = align_up(NS * p.item_cap * 4, 256);
   p.hist_bytes = align_up(NS * kHistBins * 4, 256);
@@ -546,6 +566,7 @@ hipError_t select_launch(const SelPlan& p, SelArgs a, void* workspace, hipStream
   a.item_cap = p.item_cap;
   a.n_chunks = p.n_chunks;
   a.n_pos_chunks = p.n_pos_chunks;
+  a.score_iters = p.score_iters;
   const int NS = a.B * p.n_sets;
   hipLaunchKernelGGL(zero_kernel, dim3(min(1024, (NS * kHistBins + 255) / 256)), dim3(256), 0, stream, a, NS);
   hipError_t e = hipGetLastError();
