@@ -133,3 +133,44 @@ def test_partial_scores_bit_exact(case):
         L = int(case.kv.prefix_len[b])
         want = osel.partial_scores_f32(case.logits, b, L, cfg.Hq, cfg.Hkv)
         assert np.array_equal(case.scores[b, :, :L].view(np.uint32), want.view(np.uint32)), f"b {b}"
+
+
+def test_long_tree_two_row_chunks_sampled():
+    """128K prefix, 16 verifier rows (64 q-rows per KV group: two row chunks, whose launch
+    loads K/V with caching so that the chunks' re-reads hit), logit rows at the padded
+    stride: sampled rows of both chunks and both collected rows against the oracle."""
+    torch, lcs = require_gpu()
+    cfg = synth.CONFIGS["stress_128k"].with_(B=2, n_q=16)
+    kv = synth.make_paged_kv(cfg, seed=7)
+    q = synth.make_queries(cfg, kv, cfg.n_q, seed=7)
+    dkv = kv_dev(kv, torch, lcs)
+    B, L = cfg.B, cfg.L
+    ld = lcs.row_ld(L)
+    out = torch.full((B, cfg.n_q, cfg.Hq, cfg.d), float("nan"), device="cuda")
+    logits = torch.full((B, cfg.Hq, 2, ld), float("nan"), device="cuda")
+    lse = torch.full((B, cfg.n_q, cfg.Hq), float("nan"), device="cuda")
+    lcs.verify_attn(dkv, bf16_dev(q, torch), i32_dev(kv.prefix_len, torch), L, scale_for(cfg.d),
+                    (0, cfg.n_q - 1), out=out, logits=logits, lse=lse)
+    torch.cuda.synchronize()
+    out, logits, lse = out.cpu().numpy(), logits.cpu().numpy(), lse.cpu().numpy()
+    del dkv
+    torch.cuda.empty_cache()
+    assert np.isfinite(out).all()
+    sc = scale_for(cfg.d)
+    qf = oa.bf16_to_f64(q)
+    rng = np.random.default_rng(4)
+    for i in (0, 5, 11, 12, 15, int(rng.integers(cfg.n_q))):   # rows 0-11: chunk 0, 12-15: chunk 1
+        b, h = int(rng.integers(B)), int(rng.integers(cfg.Hq))
+        g, Lb = h // cfg.G, int(kv.prefix_len[b])
+        pos = np.arange(Lb + i + 1)
+        K = oa.paged_rows(kv.k, kv.block_table, b, g, pos, cfg.page_size)
+        V = oa.paged_rows(kv.v, kv.block_table, b, g, pos, cfg.page_size)
+        o, _, l = oa.attention_one(qf[b, i, h], K, V, sc)
+        assert np.max(np.abs(out[b, i, h] - o)) <= OUT_TOL, f"row {i}"
+        assert abs(lse[b, i, h] - l) <= 1e-3
+    for c, i in ((0, 0), (1, cfg.n_q - 1)):
+        b, h = int(rng.integers(B)), int(rng.integers(cfg.Hq))
+        Lb = int(kv.prefix_len[b])
+        K = oa.paged_rows(kv.k, kv.block_table, b, h // cfg.G, np.arange(Lb), cfg.page_size)
+        assert logit_rel_err(logits[b, h, c, :Lb], sc * (K @ qf[b, i, h])) <= LOGIT_TOL
+        assert np.isnan(logits[b, h, c, Lb:]).all()
