@@ -1485,26 +1485,43 @@ AttnPlan attn_plan_nsa(int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t 
                           ((long long)window + kStepTokens - 1) / kStepTokens + tail_steps};
   long long pairs = (long long)B * Hkv * p.n_rc;
   if (pairs < 1) pairs = 1;
-  // one round of workgroups over the CUs, shared by the branches in proportion to their
-  // step bounds; every branch gets at least one split, and a split streams enough KV
-  // that its partial stays a small share of what it reads
+  // One round of workgroups over the CUs, shared by the branches so that the branch
+  // with the most steps per wave has as few as possible (each split adds kWaves waves).
+  // The selection branch streams the rows' block union, whose size only the device
+  // knows: between one row's cap blocks (every row shares them) and n_q * cap (none
+  // shared).  Its estimate is the geometric mean of those bounds, which keeps the worst
+  // relative misestimate smallest.  The call is latency-bound, so no split minimum:
+  // every branch gets at least one split, and at most one per kWaves steps of its bound.
   const long long ncu = cus > 0 ? cus : kDefaultCUs;
   long long total = ncu / pairs;
   if (total < 3) total = 3;
-  const long long partial_bytes = (long long)rows_wg * (d + 2) * 4;
-  const long long step_bytes = (long long)kStepTokens * 2 * d * 2;
-  long long min_steps = (partial_bytes * 25 + step_bytes - 1) / step_bytes;
-  if (min_steps < kWaves) min_steps = kWaves;
-  const long long sumT = T[0] + T[1] + T[2];
+  const long long t1_lo = (long long)cap * (page_size / kStepTokens) + tail_steps;
+  double est[3] = {(double)T[0], (double)T[1], (double)T[2]};
+  if (t1_lo > 0 && T[1] > t1_lo) est[1] = sqrt((double)t1_lo * (double)T[1]);
+  long long ns[3], cap_ns[3];
+  for (int c = 0; c < 3; ++c) {
+    ns[c] = 1;
+    cap_ns[c] = (T[c] + kWaves - 1) / kWaves;
+    if (cap_ns[c] > kMaxSplits / 3) cap_ns[c] = kMaxSplits / 3;
+    if (cap_ns[c] < 1) cap_ns[c] = 1;
+  }
+  for (long long used = 3; used < total; ++used) {
+    int best = -1;
+    double worst = 0.0;
+    for (int c = 0; c < 3; ++c) {
+      const double per = est[c] / (double)ns[c];
+      if (ns[c] < cap_ns[c] && per > worst) {
+        worst = per;
+        best = c;
+      }
+    }
+    if (best < 0) break;
+    ++ns[best];
+  }
   int n = 0;
   for (int c = 0; c < 3; ++c) {
-    long long ns = (sumT > 0) ? total * T[c] / sumT : 1;
-    const long long ns_cap = (T[c] + min_steps - 1) / min_steps;
-    if (ns > ns_cap) ns = ns_cap;
-    if (ns > kMaxSplits / 3) ns = kMaxSplits / 3;
-    if (ns < 1) ns = 1;
-    p.ns_br[c] = (int32_t)ns;
-    n += (int32_t)ns;
+    p.ns_br[c] = (int32_t)ns[c];
+    n += (int32_t)ns[c];
   }
   p.n_split = n;
   p.T_max = (int32_t)(T[0] > T[1] ? (T[0] > T[2] ? T[0] : T[2]) : (T[1] > T[2] ? T[1] : T[2]));
