@@ -221,6 +221,12 @@ lcs_status lcs_verify_attn_scores(const lcs_paged_kv* kv, const void* q, int32_t
  *  logits       fp32 [B][Hq][2][logits_ld] as written by lcs_verify_attn.
  *  block_size   BLOCK mode only: power of two in [4, 512]; ignored otherwise.
  *  workspace    at least lcs_select_workspace_bytes(...) bytes, no initialisation.
+ *               A call leaves its histograms clean and marks them with the call's
+ *               layout, so that the next call on the same workspace with the same
+ *               layout skips clearing them; a workspace with other contents (first
+ *               use, another layout, other data) fails the mark or the item count
+ *               and the call rebuilds the histograms from its keys.  Calls that share
+ *               a workspace must not overlap.
  * Limits: max_prefix_len < 2^24.
  * ------------------------------------------------------------------------- */
 size_t lcs_select_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, lcs_set_mode mode,

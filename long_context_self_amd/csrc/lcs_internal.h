@@ -163,6 +163,8 @@ struct SelArgs {
   uint64_t* cand;        // [NS][item_cap]
   uint32_t* chunk_above; // [NS][n_chunks]
   uint64_t* thr;         // [NS][2]
+  uint64_t* marker;      // histograms left clean by the last call of this layout
+  uint64_t marker_value; // the value that says so for this call's layout
   int32_t item_cap, n_chunks, n_pos_chunks;
   int32_t score_iters;   // 512-position chunks one score workgroup covers (1 in block mode)
 };
@@ -170,7 +172,7 @@ struct SelArgs {
 struct SelPlan {
   int32_t n_sets, item_cap, n_chunks, n_pos_chunks, score_iters;
   int32_t fin_threads;   // threads of a finish workgroup (256 or 1024)
-  size_t keys_bytes, hist_bytes, cc_bytes, cand_bytes, ca_bytes, thr_bytes, total_bytes;
+  size_t keys_bytes, hist_bytes, cc_bytes, cand_bytes, ca_bytes, thr_bytes, mk_bytes, total_bytes;
 };
 
 // cus: compute units of the device (0: the MI355X's 256); only the launch shape depends on it

@@ -23,6 +23,9 @@
 //    atomic per non-empty bin.  A workgroup covers one to eight 512-position chunks,
 //    as many as still leave four workgroups per CU, so that large calls clear and
 //    flush fewer histograms.
+//  * No clearing pass: the previous call's finish_kernel left the histograms clean and
+//    wrote a marker for its layout; collect trusts them only if the marker matches and
+//    the counts add up to the pool, and rebuilds them from the keys otherwise.
 //  * collect_kernel finds the bin that holds the k-th item, counts the items above
 //    it per 4096-item chunk and appends the bin's items as 44-bit composites
 //    (20 low key bits, then the complemented index) to a candidate list; each
@@ -122,11 +125,6 @@ __device__ __forceinline__ void load16(const uint32_t* keys, int i0, uint32_t (&
   }
 }
 
-__global__ void zero_kernel(SelArgs a, int NS) {
-  const int n = NS * kHistBins;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) a.hist[i] = 0;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < NS; i += gridDim.x * blockDim.x) a.cand_count[i] = 0;
-}
 
 // Score of one head's rows at positions p, p + 1 (both < L when BOTH), into t0, t1.
 // NR2: exactly two rows (the Collect-2-Query layout), summed as one pair.
@@ -171,6 +169,7 @@ __global__ void __launch_bounds__(256) score_kernel(SelArgs a) {
   const int s = set - b * a.n_sets;
   const Win w = window(a, b);
   if (w.all || a.top_k == 0) return;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.cand_count[set] = 0;   // collect appends after this launch
   // a workgroup covers score_iters consecutive kScorePos-position chunks (one in block
   // mode) and flushes its histogram once
   const int iters = (a.mode == LCS_SEL_BLOCK) ? 1 : a.score_iters;
@@ -264,9 +263,9 @@ __global__ void __launch_bounds__(256) score_kernel(SelArgs a) {
 }
 
 // Threshold bin of a set from its histogram: the bin holding the k-th largest item.
-__device__ void find_bin(const SelArgs& a, int set, uint32_t* s_wave, int* sh_bin, uint32_t* sh_above) {
+__device__ uint32_t find_bin(const SelArgs& a, const uint32_t* h, uint32_t* s_wave, int* sh_bin,
+                             uint32_t* sh_above) {
   const int tid = threadIdx.x;
-  const uint32_t* h = a.hist + (size_t)set * kHistBins;
   uint32_t hv[16];
   uint32_t c = 0;
 #pragma unroll
@@ -290,6 +289,7 @@ __device__ void find_bin(const SelArgs& a, int set, uint32_t* s_wave, int* sh_bi
     }
   }
   __syncthreads();
+  return total;
 }
 
 __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
@@ -312,7 +312,24 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
   uint32_t k[kIPT], flags = 0, n_above = 0;
   if (mine) load16(a.keys + (size_t)set * a.item_cap, i0, k);
   __syncthreads();
-  find_bin(a, set, s_wave, &sh_bin, &sh_above);
+  // The global histogram is valid when the last call of this layout left it clean (its
+  // finish pass zeroed it and wrote the marker) and it counts exactly the pool's items.
+  // Otherwise (a fresh or reused workspace) every workgroup rebuilds the set's histogram
+  // from the keys in LDS; the finish pass then leaves it clean for the next call.
+  const uint32_t h_total = find_bin(a, a.hist + (size_t)set * kHistBins, s_wave, &sh_bin, &sh_above);
+  if (*a.marker != a.marker_value || h_total != (uint32_t)(w.hi - w.lo)) {
+    __shared__ uint32_t lhist[kHistBins];
+    for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0;
+    if (tid == 0) {
+      sh_bin = 0;
+      sh_above = 0;
+    }
+    __syncthreads();
+    const uint32_t* keys = a.keys + (size_t)set * a.item_cap;
+    for (int it = w.lo + tid; it < w.hi; it += 256) atomicAdd(&lhist[keys[it] >> 20], 1u);
+    __syncthreads();
+    find_bin(a, lhist, s_wave, &sh_bin, &sh_above);
+  }
   const int bin = sh_bin;
   if (blockIdx.x == 0 && tid == 0) {
     a.thr[(size_t)set * 2 + 0] = (uint64_t)bin;
@@ -377,6 +394,13 @@ __global__ void __launch_bounds__(FT) finish_kernel(SelArgs a) {
   const int tid = threadIdx.x;
   const int c0 = blockIdx.x * kItemChunk;          // first item of this chunk
   int32_t* out = a.indices + (size_t)set * a.cap;
+  // the histograms were read by collect: leave them clean for the next call of this
+  // layout, which then needs no clearing pass (the marker says they are clean)
+  if (blockIdx.x == 0) {
+    uint32_t* gh = a.hist + (size_t)set * kHistBins;
+    for (int i = tid; i < kHistBins; i += kFinThreads) gh[i] = 0u;
+    if (set == 0 && tid == 0) *a.marker = a.marker_value;
+  }
   if (w.all) {
     for (int it = c0 + tid; it < min(w.n, c0 + kItemChunk); it += kFinThreads)
       if (it < a.cap) out[it] = emit_id(a, b, it);
@@ -549,8 +573,9 @@ SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t ma
   p.cand_bytes = align_up(NS * p.item_cap * 8, 256);
   p.ca_bytes = align_up(NS * p.n_chunks * 4, 256);
   p.thr_bytes = align_up(NS * 2 * 8, 256);
+  p.mk_bytes = 256;
   p.total_bytes = p.keys_bytes + p.hist_bytes + p.cc_bytes + p.cand_bytes + p.ca_bytes +
-                  p.thr_bytes;
+                  p.thr_bytes + p.mk_bytes;
   return p;
 }
 
@@ -561,16 +586,18 @@ hipError_t select_launch(const SelPlan& p, SelArgs a, void* workspace, hipStream
   a.cand_count = reinterpret_cast<uint32_t*>(ws); ws += p.cc_bytes;
   a.cand = reinterpret_cast<uint64_t*>(ws); ws += p.cand_bytes;
   a.chunk_above = reinterpret_cast<uint32_t*>(ws); ws += p.ca_bytes;
-  a.thr = reinterpret_cast<uint64_t*>(ws);
+  a.thr = reinterpret_cast<uint64_t*>(ws); ws += p.thr_bytes;
+  a.marker = reinterpret_cast<uint64_t*>(ws);
   a.n_sets = p.n_sets;
   a.item_cap = p.item_cap;
   a.n_chunks = p.n_chunks;
   a.n_pos_chunks = p.n_pos_chunks;
   a.score_iters = p.score_iters;
   const int NS = a.B * p.n_sets;
-  hipLaunchKernelGGL(zero_kernel, dim3(min(1024, (NS * kHistBins + 255) / 256)), dim3(256), 0, stream, a, NS);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // layout-specific, so that a workspace last used with another layout is not trusted
+  a.marker_value = 0x9E3779B97F4A7C15ull ^ ((uint64_t)NS << 40) ^ ((uint64_t)p.item_cap << 8) ^
+                   (uint64_t)p.n_chunks;
+  hipError_t e;
   const dim3 sgrid(p.n_pos_chunks, NS);
   if (a.kind == SCORE_SOFTMAX_WT)
     hipLaunchKernelGGL((score_kernel<SCORE_SOFTMAX_WT, false>), sgrid, dim3(256), 0, stream, a);

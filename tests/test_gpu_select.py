@@ -223,3 +223,28 @@ def test_window_sizes_at_int32_max_keep_everything(mode, bs, which):
         for s in range(len(res[b])):
             assert res[b][s].tolist() == list(range(n_items))
     assert_exact(idx, cnt, res)
+
+
+@pytest.mark.parametrize("mode,bs", [("shared", 0), ("per_kv_head", 0), ("block", 64)])
+def test_workspace_reuse_garbage_and_layout_changes(mode, bs):
+    """One workspace through a sequence of calls: first filled with random bytes (the
+    histograms are then rebuilt from the keys), then reused with the same layout (the
+    histograms the last call left clean are trusted), then with another layout and back.
+    Every call equals the CPU rule bit for bit."""
+    torch, lcs = require_gpu()
+    rng = np.random.default_rng(21)
+    Hq, Hkv = 8, 2
+    shapes = [(2, 9000), (2, 9000), (3, 5000), (2, 9000)]
+    need = max(lcs.select_workspace_bytes(B, Hq, Hkv, mode, L, bs) for B, L in shapes)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda", generator=g)
+    for B, L in shapes:
+        lens = np.array([L - 37 * b for b in range(B)], dtype=np.int32)
+        lg_np = rng.standard_normal((B, Hq, 2, L)).astype(np.float32)
+        lg = torch.from_numpy(lg_np).cuda()
+        top_k = 40 if mode == "block" else 700
+        idx, cnt = lcs.select_topk(lg, i32_dev(lens, torch), L, Hkv, mode, top_k, 4, 64, block_size=bs,
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        assert_exact(idx.cpu().numpy(), cnt.cpu().numpy(), cpu_rule(lg_np, lens, Hkv, mode, top_k, 4, 64, bs))
