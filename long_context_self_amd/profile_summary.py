@@ -15,7 +15,10 @@
 plain device-to-device copy of known size in the same run (the runtime's copy kernel;
 the last dispatch of it at least a quarter the size of the largest, since the per-layer
 KV replicas made before the calibration copy are copies too),
-and sums the named kernels' dispatches into HBM bytes per call.  The JSON carries a
+and sums the named kernels' dispatches into HBM bytes per call.  Each kernel's figure is
+the median over its dispatches, so that a one-time first-call path (a workspace that
+is not yet initialised, a cold cache) does not stand for the steady per-call traffic;
+the mean and the maximum are kept beside it.  The JSON carries a
 hash of the kernel sources so that a later source change makes it stale.  Inputs are
 either rocprofv3's CSV files or its default SQLite database (`*_results.db`).
 """
@@ -28,6 +31,7 @@ import json
 import os
 import re
 import sqlite3
+import statistics
 import sys
 from collections import defaultdict
 
@@ -68,18 +72,21 @@ def stats_rows(path: str):
     for name, d in sqlite3.connect(path).execute("select name, duration from kernels"):
         durs[name].append(float(d))
     grand = sum(sum(v) for v in durs.values()) or 1.0
-    return [{"Name": k, "Calls": str(len(v)), "AverageNs": sum(v) / len(v), "MinNs": min(v), "MaxNs": max(v),
-             "TotalDurationNs": sum(v), "Percentage": 100.0 * sum(v) / grand} for k, v in durs.items()]
+    return [{"Name": k, "Calls": str(len(v)), "AverageNs": sum(v) / len(v), "MedianNs": statistics.median(v),
+             "MinNs": min(v), "MaxNs": max(v), "TotalDurationNs": sum(v), "Percentage": 100.0 * sum(v) / grand}
+            for k, v in durs.items()]
 
 
 def stats(args) -> None:
     rows = stats_rows(args.csv)
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     out = [f"# {args.title}", "", "Command (run from the repository root):", "", "```", args.command, "```", "",
-           "| kernel | calls | avg us | min us | max us | total us | % |", "|---|---:|---:|---:|---:|---:|---:|"]
+           "| kernel | calls | avg us | median us | min us | max us | total us | % |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|"]
     for r in rows:
-        out.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f | %.2f |" % (
-            short_name(r["Name"])[:70], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+        med = "%.2f" % (float(r["MedianNs"]) / 1e3) if r.get("MedianNs") is not None else "—"
+        out.append("| `%s` | %s | %.2f | %s | %.2f | %.2f | %.1f | %.2f |" % (
+            short_name(r["Name"])[:70], r["Calls"], float(r["AverageNs"]) / 1e3, med, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e3, float(r["Percentage"])))
     if args.note:
         out += ["", args.note]
@@ -121,12 +128,14 @@ def traffic(args) -> None:
             if k not in vals:
                 sys.exit(f"kernel {k!r} has no {counter} values in {path}; have {sorted(vals)}")
             v = vals[k]
-            avg_kib = sum(v) / len(v)
+            med_kib = statistics.median(v)
             ent = res["kernels"].setdefault(k, {})
-            ent[f"{counter}_kib_avg"] = round(avg_kib, 1)
+            ent[f"{counter}_kib_median"] = round(med_kib, 1)
+            ent[f"{counter}_kib_mean"] = round(sum(v) / len(v), 1)
+            ent[f"{counter}_kib_max"] = round(max(v), 1)
             ent[f"{counter}_dispatches"] = len(v)
-            ent[f"{counter}_bytes_scaled"] = round(avg_kib * 1024.0 * factor)
-            total += avg_kib * 1024.0 * factor
+            ent[f"{counter}_bytes_scaled"] = round(med_kib * 1024.0 * factor)
+            total += med_kib * 1024.0 * factor
     res["hbm_bytes_per_launch"] = round(total)
     if args.algorithmic_bytes:
         res["algorithmic_bytes_per_launch"] = args.algorithmic_bytes
@@ -137,9 +146,10 @@ def traffic(args) -> None:
 
 
 def counters(args) -> None:
-    """Per-dispatch averages of every counter in one or more --pmc databases for the named
-    kernels, with the derived MFMA busy fraction, MFMA bf16 flops and LDS bank-conflict
-    rate where their inputs were collected."""
+    """Per-dispatch medians of every counter in one or more --pmc databases for the named
+    kernels (the median, as in `traffic`, so a one-time first-call path does not stand for
+    the steady call), with the derived MFMA busy fraction, MFMA bf16 flops and LDS
+    bank-conflict rate where their inputs were collected."""
     per = defaultdict(dict)
     for path in args.db:
         rows = sqlite3.connect(path).execute("select kernel_name, counter_name, value from counters_collection")
@@ -148,10 +158,10 @@ def counters(args) -> None:
             acc[(short_name(name), cn)].append(float(v))
         for (k, cn), v in acc.items():
             if k in args.kernel:
-                per[k][cn] = sum(v) / len(v)
+                per[k][cn] = statistics.median(v)
     out = ["# " + args.title, "", "Commands (run from the repository root):", ""]
     out += ["```"] + list(args.command) + ["```", ""]
-    out += ["| kernel | counter | per dispatch |", "|---|---|---:|"]
+    out += ["| kernel | counter | per dispatch (median) |", "|---|---|---:|"]
     for k in args.kernel:
         for cn in sorted(per.get(k, {})):
             out.append(f"| `{k}` | {cn} | {per[k][cn]:.4g} |")
