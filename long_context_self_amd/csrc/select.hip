@@ -305,19 +305,23 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
     sh_bin = 0;
     sh_above = 0;
   }
+  // the marker is read first, so that its check after the scan costs no round trip
+  // (as a relaxed atomic load, which the compiler does not sink past the barriers to its use)
+  const uint64_t marker = __hip_atomic_load(a.marker, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // this thread's kIPT consecutive keys do not depend on the bin: they load while the
   // histogram is scanned
   const int i0 = blockIdx.x * kItemChunk + kIPT * tid;
   const bool mine = i0 < w.hi && i0 + kIPT > w.lo;
   uint32_t k[kIPT], flags = 0, n_above = 0;
-  if (mine) load16(a.keys + (size_t)set * a.item_cap, i0, k);
+  const uint32_t* keys = a.keys + (size_t)set * a.item_cap;
+  if (mine) load16(keys, i0, k);
   __syncthreads();
   // The global histogram is valid when the last call of this layout left it clean (its
   // finish pass zeroed it and wrote the marker) and it counts exactly the pool's items.
   // Otherwise (a fresh or reused workspace) every workgroup rebuilds the set's histogram
   // from the keys in LDS; the finish pass then leaves it clean for the next call.
   const uint32_t h_total = find_bin(a, a.hist + (size_t)set * kHistBins, s_wave, &sh_bin, &sh_above);
-  if (*a.marker != a.marker_value || h_total != (uint32_t)(w.hi - w.lo)) {
+  if (marker != a.marker_value || h_total != (uint32_t)(w.hi - w.lo)) {
     __shared__ uint32_t lhist[kHistBins];
     for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0;
     if (tid == 0) {
@@ -325,8 +329,26 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
       sh_above = 0;
     }
     __syncthreads();
-    const uint32_t* keys = a.keys + (size_t)set * a.item_cap;
-    for (int it = w.lo + tid; it < w.hi; it += 256) atomicAdd(&lhist[keys[it] >> 20], 1u);
+    // the pool's keys in 16-byte groups, kRebuildLoads groups in flight per thread; a
+    // group ends at or below item_cap (a multiple of 16 and at least the item count).
+    // Groups past the pool load the last group again (unconditional loads stay in
+    // flight together) and count nothing.
+    constexpr int kRebuildLoads = 8;
+    const int q0 = w.lo >> 2, q1 = (w.hi + 3) >> 2;
+    for (int q = q0 + tid; q < q1; q += kRebuildLoads * 256) {
+      uint4 x[kRebuildLoads];
+#pragma unroll
+      for (int u = 0; u < kRebuildLoads; ++u)
+        x[u] = *reinterpret_cast<const uint4*>(keys + 4 * min(q + 256 * u, q1 - 1));
+#pragma unroll
+      for (int u = 0; u < kRebuildLoads; ++u) {
+        const int it = 4 * (q + 256 * u);     // past the pool when the group was clamped
+        const uint32_t kv[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (it + e >= w.lo && it + e < w.hi) atomicAdd(&lhist[kv[e] >> 20], 1u);
+      }
+    }
     __syncthreads();
     find_bin(a, lhist, s_wave, &sh_bin, &sh_above);
   }
@@ -430,17 +452,44 @@ __global__ void __launch_bounds__(FT) finish_kernel(SelArgs a) {
       kk[4 * v + 3] = q.w;
     }
   }
+  // Loaded with the keys, before anything that depends on them: the earlier chunks'
+  // above-bin counts, and the first kSpec * FT candidates (read before their count is
+  // known; entries past the count are left unused), so that the candidates' count and
+  // the chunks' offsets add no round trip of their own.
+  constexpr int kSpec = 1024 / FT;
+  const uint64_t* gcand = a.cand + (size_t)set * a.item_cap;
+  const uint32_t* cabove = a.chunk_above + (size_t)set * a.n_chunks;
+  uint32_t part = 0;
+  uint64_t spec[kSpec], thr_bin = 0, thr_above = 0;
+  int n_cand = 0;
+  if (K > 0) {
+#pragma unroll
+    for (int u = 0; u < kSpec; ++u) {
+      const int e = tid + u * kFinThreads;
+      spec[u] = (e < a.item_cap) ? gcand[e] : 0ull;
+    }
+    thr_bin = a.thr[(size_t)set * 2 + 0];
+    thr_above = a.thr[(size_t)set * 2 + 1];
+    n_cand = (int)a.cand_count[set];
+    if (tid < (int)blockIdx.x) part = cabove[tid];
+    for (int c = tid + kFinThreads; c < (int)blockIdx.x; c += kFinThreads) part += cabove[c];
+  }
   int bin = 0;
   uint64_t cstar = ~0ull;
   uint32_t base = (uint32_t)w.lo;
   if (K > 0) {
-    bin = (int)a.thr[(size_t)set * 2 + 0];
-    const uint32_t above = (uint32_t)a.thr[(size_t)set * 2 + 1];
-    const int n_c = min((int)a.cand_count[set], a.item_cap);
-    const uint64_t* gcand = a.cand + (size_t)set * a.item_cap;
+    bin = (int)thr_bin;
+    const uint32_t above = (uint32_t)thr_above;
+    const int n_c = min(n_cand, a.item_cap);
     const bool in_lds = n_c <= kFinLDS;
-    if (in_lds)
-      for (int e = tid; e < n_c; e += kFinThreads) lc[e] = gcand[e];
+    if (in_lds) {
+#pragma unroll
+      for (int u = 0; u < kSpec; ++u) {
+        const int e = tid + u * kFinThreads;
+        if (e < n_c) lc[e] = spec[u];
+      }
+      for (int e = tid + kSpec * kFinThreads; e < n_c; e += kFinThreads) lc[e] = gcand[e];
+    }
     const uint64_t* cand = in_lds ? lc : gcand;
     if (tid == 0) {
       sh_prefix = 0;
@@ -500,9 +549,8 @@ __global__ void __launch_bounds__(FT) finish_kernel(SelArgs a) {
       __syncthreads();
       cstar = sh_one;
     }
-    // kept items of the chunks before this one
-    uint32_t part = 0;
-    for (int c = tid; c < (int)blockIdx.x; c += kFinThreads) part += a.chunk_above[(size_t)set * a.n_chunks + c];
+    // kept items of the chunks before this one: their items above the bin (part, loaded
+    // above) and their candidates at or above the boundary
     for (int e = tid; e < n_c; e += kFinThreads) {
       const uint64_t cv = cand[e];
       const int item = (int)(kItemMask - (uint32_t)(cv & kItemMask));
