@@ -248,3 +248,43 @@ def test_workspace_reuse_garbage_and_layout_changes(mode, bs):
                                    workspace=ws)
         torch.cuda.synchronize()
         assert_exact(idx.cpu().numpy(), cnt.cpu().numpy(), cpu_rule(lg_np, lens, Hkv, mode, top_k, 4, 64, bs))
+
+
+def _boundary_bin_logits(rng, B, L, Hq, n_c, n_high, n_sink, n_recent):
+    """Logits whose set scores put n_high items above one first-digit bin and exactly
+    n_c tied items in it (every head's two rows hold the same value v, so every score
+    is the same sum of v), the rest below it."""
+    lens = np.array([L - 37 * b for b in range(B)], dtype=np.int32)
+    v = np.full((B, L), 0.001, dtype=np.float32)
+    for b in range(B):
+        pool = rng.permutation(np.arange(n_sink, lens[b] - n_recent))
+        assert pool.size > n_high + n_c
+        v[b, pool[:n_high]] = (100.0 + rng.random(n_high)).astype(np.float32)
+        v[b, pool[n_high:n_high + n_c]] = 1.0
+    lg = np.ascontiguousarray(np.broadcast_to(v[:, None, None, :], (B, Hq, 2, L)), dtype=np.float32)
+    return lg, lens
+
+
+@pytest.mark.parametrize("mode", ["shared", "per_kv_head"])
+@pytest.mark.parametrize("n_c", [1023, 1024, 1025, 3000, 8192, 8193])
+def test_boundary_bin_sizes_around_prefetch_and_lds(mode, n_c):
+    """The boundary bin holds exactly n_c tied items: around the 1024 candidates the
+    finish pass loads before it knows their count, and around the 8192 it holds in LDS
+    (one more are read from memory in every radix pass).  200 of them are kept, the
+    smaller indices first, as the CPU rule keeps them (finish with 1024 threads)."""
+    rng = np.random.default_rng(100 + n_c)
+    K, n_high = 2048, 1848
+    lg, lens = _boundary_bin_logits(rng, 1, 40000, 4, n_c, n_high, 4, 64)
+    idx, cnt = gpu_select(lg, lens, 2, mode, K, 4, 64)
+    assert_exact(idx, cnt, cpu_rule(lg, lens, 2, mode, K, 4, 64))
+
+
+@pytest.mark.parametrize("n_c", [1025, 8193])
+def test_boundary_bin_sizes_finish_256_threads(n_c):
+    """The same at 360000-item sets over three sequences, where the finish pass runs
+    256-thread workgroups (four prefetched candidates per thread)."""
+    rng = np.random.default_rng(200 + n_c)
+    K, n_high = 2048, 1848
+    lg, lens = _boundary_bin_logits(rng, 3, 360000, 4, n_c, n_high, 4, 64)
+    idx, cnt = gpu_select(lg, lens, 2, "shared", K, 4, 64)
+    assert_exact(idx, cnt, cpu_rule(lg, lens, 2, "shared", K, 4, 64))
