@@ -359,7 +359,7 @@ def kernel_table(cfg, m):
 
 # the kernels behind each call, as rocprofv3 names them
 CALL_KERNELS = {"verify": "attn_kernel (dense verify) + combine_kernel",
-                "select": "zero_kernel + score_kernel + collect_kernel + finish_kernel",
+                "select": "score_kernel + collect_kernel + finish_kernel",
                 "draft_step": "attn_kernel (shared token list) + combine_kernel"}
 
 
