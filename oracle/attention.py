@@ -23,7 +23,7 @@ lse = m + log(sum exp(s - m)).
 """
 from __future__ import annotations
 
-from typing import Optional, Sequence, Tuple
+from typing import Optional, Sequence
 
 import numpy as np
 
