@@ -56,8 +56,19 @@ def build(name):
     scores = torch.full((B, cfg.Hkv, L), float("nan"), device="cuda")
     lcs.verify_attn_scores(c.dkv, bf16_dev(c.q, torch), pl, L, scale_for(cfg.d), cfg.collect_rows,
                            scores=scores)
+    # the physical-slot hand-off on the same logits (the bench's physical_hand_off variant)
+    pidx = torch.full((B, n_sets, S), -1, dtype=torch.int32, device="cuda")
+    pcnt = torch.zeros((B, n_sets), dtype=torch.int32, device="cuda")
+    lcs.select_topk_physical(logits, pl, L, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, c.dkv,
+                             cap=S, indices=pidx, counts=pcnt)
+    pdout = torch.full((B, 1, cfg.Hq, cfg.d), float("nan"), device="cuda")
+    pdlse = torch.full((B, 1, cfg.Hq), float("nan"), device="cuda")
+    lcs.sparse_draft_attn_physical(c.dkv, bf16_dev(c.qd, torch), cfg.mode, pidx, pcnt, pl, i32_dev(tl, torch),
+                                   cfg.n_q + cfg.n_draft, scale_for(cfg.d), out=pdout, lse=pdlse)
     torch.cuda.synchronize()
     c.scores = scores.cpu().numpy()
+    c.pidx, c.pcnt = pidx.cpu().numpy(), pcnt.cpu().numpy()
+    c.pdout, c.pdlse = pdout.cpu().numpy(), pdlse.cpu().numpy()
     c.out, c.logits, c.lse = out.cpu().numpy(), logits.cpu().numpy(), lse.cpu().numpy()
     c.idx, c.cnt, c.tl = idx.cpu().numpy(), cnt.cpu().numpy(), tl
     c.dout, c.dlse = dout.cpu().numpy(), dlse.cpu().numpy()
@@ -174,3 +185,20 @@ def test_long_tree_two_row_chunks_sampled():
         K = oa.paged_rows(kv.k, kv.block_table, b, h // cfg.G, np.arange(Lb), cfg.page_size)
         assert logit_rel_err(logits[b, h, c, :Lb], sc * (K @ qf[b, i, h])) <= LOGIT_TOL
         assert np.isnan(logits[b, h, c, Lb:]).all()
+
+
+def test_physical_hand_off_full(case):
+    """Select's physical slots are its logical selection mapped through the block table
+    (slot = page << log2(page size) | offset), and the draft over them equals the draft
+    over the positions bit for bit, at the full workload."""
+    cfg, kv = case.cfg, case.kv
+    lg = int(cfg.page_size).bit_length() - 1
+    assert np.array_equal(case.pcnt, case.cnt)
+    for b in range(cfg.B):
+        for s in range(case.cnt.shape[1]):
+            n = int(case.cnt[b, s])
+            pos = case.idx[b, s, :n].astype(np.int64)
+            want = (kv.block_table[b, pos >> lg].astype(np.int64) << lg) | (pos & (cfg.page_size - 1))
+            assert np.array_equal(case.pidx[b, s, :n].astype(np.int64), want), f"b {b} set {s}"
+    assert np.array_equal(case.pdout.view(np.uint32), case.dout.view(np.uint32))
+    assert np.array_equal(case.pdlse.view(np.uint32), case.dlse.view(np.uint32))
