@@ -171,7 +171,7 @@ struct SelArgs {
 
 struct SelPlan {
   int32_t n_sets, item_cap, n_chunks, n_pos_chunks, score_iters;
-  int32_t fin_threads;   // threads of a finish workgroup (256 or 1024)
+  int32_t fin_threads;   // threads of a finish workgroup (256, 512 or 1024)
   size_t keys_bytes, hist_bytes, cc_bytes, cand_bytes, ca_bytes, thr_bytes, mk_bytes, total_bytes;
 };
 

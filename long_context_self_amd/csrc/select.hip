@@ -402,9 +402,11 @@ constexpr long long kScoreWGsPerCU = 4;   // score workgroups per CU to keep
 // kept items after the sink window, the kept items of the chunks before it (their items
 // above the bin, counted by collect, and their candidates at or above the boundary) and
 // the kept items before it in this chunk.  FT threads: 1024 when the chunks of all sets
-// fit in one round of the CUs, else 256 (fewer waves make the radix passes' barriers
-// cheaper when several workgroups share a CU; measured: 64K x 4 per-KV-head sets 52.7 ->
-// 50.2 us, while 128K x 8 and 32K are faster with 1024).
+// fit in one round of the CUs, 512 when they fit with two workgroups per CU (the LDS
+// holds two), else 256: fewer waves make the radix passes' barriers cheaper when several
+// workgroups share a CU, more threads take fewer items each (measured at 64K x 4
+// per-KV-head sets, 512 workgroups: select 52.7 us with 1024, 50.2 with 256, and with
+// 512 threads 44.7 -> 42.8 us on the current passes; 128K x 8 and 32K run 1024).
 template <int FT>
 __global__ void __launch_bounds__(FT) finish_kernel(SelArgs a) {
   constexpr int kFinThreads = FT;
@@ -614,7 +616,10 @@ SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t ma
            pos_chunks * (long long)NS / (2 * p.score_iters) >= kScoreWGsPerCU * ncu)
       p.score_iters *= 2;
   p.n_pos_chunks = (int32_t)((pos_chunks + p.score_iters - 1) / p.score_iters);
-  p.fin_threads = ((long long)p.n_chunks * (long long)NS > (cus > 0 ? cus : kDefaultCUs)) ? 256 : 1024;
+  {
+    const long long wg = (long long)p.n_chunks * (long long)NS, nc = cus > 0 ? cus : kDefaultCUs;
+    p.fin_threads = wg <= nc ? 1024 : (wg <= 2 * nc ? 512 : 256);
+  }
   p.keys_bytes = align_up(NS * p.item_cap * 4, 256);
   p.hist_bytes = align_up(NS * kHistBins * 4, 256);
   p.cc_bytes = align_up(NS * 4, 256);
@@ -658,6 +663,8 @@ hipError_t select_launch(const SelPlan& p, SelArgs a, void* workspace, hipStream
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.fin_threads == 256)
     hipLaunchKernelGGL(finish_kernel<256>, dim3(p.n_chunks, NS), dim3(256), 0, stream, a);
+  else if (p.fin_threads == 512)
+    hipLaunchKernelGGL(finish_kernel<512>, dim3(p.n_chunks, NS), dim3(512), 0, stream, a);
   else
     hipLaunchKernelGGL(finish_kernel<1024>, dim3(p.n_chunks, NS), dim3(1024), 0, stream, a);
   return hipGetLastError();

@@ -279,12 +279,14 @@ def test_boundary_bin_sizes_around_prefetch_and_lds(mode, n_c):
     assert_exact(idx, cnt, cpu_rule(lg, lens, 2, mode, K, 4, 64))
 
 
+@pytest.mark.parametrize("B", [3, 7])
 @pytest.mark.parametrize("n_c", [1025, 8193])
-def test_boundary_bin_sizes_finish_256_threads(n_c):
-    """The same at 360000-item sets over three sequences, where the finish pass runs
-    256-thread workgroups (four prefetched candidates per thread)."""
-    rng = np.random.default_rng(200 + n_c)
+def test_boundary_bin_sizes_smaller_finish_workgroups(B, n_c):
+    """The same at 360000-item sets (88 chunks each): over three sequences the finish pass
+    runs 512-thread workgroups (264 of them, two per CU; two prefetched candidates per
+    thread), over seven 256-thread ones (616; four per thread)."""
+    rng = np.random.default_rng(200 + n_c + B)
     K, n_high = 2048, 1848
-    lg, lens = _boundary_bin_logits(rng, 3, 360000, 4, n_c, n_high, 4, 64)
+    lg, lens = _boundary_bin_logits(rng, B, 360000, 4, n_c, n_high, 4, 64)
     idx, cnt = gpu_select(lg, lens, 2, "shared", K, 4, 64)
     assert_exact(idx, cnt, cpu_rule(lg, lens, 2, "shared", K, 4, 64))
