@@ -29,7 +29,8 @@
 //  * collect_kernel finds the bin that holds the k-th item, counts the items above
 //    it per 4096-item chunk and appends the bin's items as 44-bit composites
 //    (20 low key bits, then the complemented index) to a candidate list; each
-//    thread owns 16 consecutive items, and one scan places a workgroup's appends.
+//    thread owns 4 to 16 consecutive items (1024 to 256 threads, as many as the
+//    chunks' workgroups leave per CU), and one scan places a workgroup's appends.
 //  * finish_kernel (one workgroup per chunk) loads the candidates into LDS and
 //    radix-selects the exact boundary composite in up to four 11-bit passes,
 //    stopping once the chosen digit holds a single candidate.  Every chunk does this
@@ -110,13 +111,12 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave
   return pre + x - v;
 }
 
-constexpr int kIPT = kItemChunk / 256;   // consecutive items per thread in collect / emit
-
-// the 16 keys of items [i0, i0 + 16); i0 is a multiple of 16 below item_cap, which is a
-// multiple of 16, so the four 16-byte loads stay inside the set's key array
-__device__ __forceinline__ void load16(const uint32_t* keys, int i0, uint32_t (&k)[kIPT]) {
+// the N keys of items [i0, i0 + N) (N = 4, 8 or 16); i0 is a multiple of N below
+// item_cap, which is a multiple of 16, so the 16-byte loads stay inside the set's keys
+template <int N>
+__device__ __forceinline__ void load_keys(const uint32_t* keys, int i0, uint32_t (&k)[N]) {
 #pragma unroll
-  for (int v = 0; v < kIPT / 4; ++v) {
+  for (int v = 0; v < N / 4; ++v) {
     const uint4 x = *reinterpret_cast<const uint4*>(keys + i0 + 4 * v);
     k[4 * v] = x.x;
     k[4 * v + 1] = x.y;
@@ -263,25 +263,28 @@ __global__ void __launch_bounds__(256) score_kernel(SelArgs a) {
 }
 
 // Threshold bin of a set from its histogram: the bin holding the k-th largest item.
+// CT threads, each owning kHistBins / CT consecutive bins.
+template <int CT>
 __device__ uint32_t find_bin(const SelArgs& a, const uint32_t* h, uint32_t* s_wave, int* sh_bin,
                              uint32_t* sh_above) {
+  constexpr int BPT = kHistBins / CT;
   const int tid = threadIdx.x;
-  uint32_t hv[16];
+  uint32_t hv[BPT];
   uint32_t c = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    hv[e] = h[16 * tid + e];
+  for (int e = 0; e < BPT; ++e) {
+    hv[e] = h[BPT * tid + e];
     c += hv[e];
   }
   uint32_t total;
-  const uint32_t excl = block_excl_scan<256>(c, s_wave, total);
+  const uint32_t excl = block_excl_scan<CT>(c, s_wave, total);
   const uint32_t K = (uint32_t)a.top_k;
   const uint32_t above_t = total - excl - c;       // items in bins above this thread's range
   if (above_t < K && above_t + c >= K) {
     uint32_t cum = above_t;
-    for (int e = 15; e >= 0; --e) {
+    for (int e = BPT - 1; e >= 0; --e) {
       if (cum + hv[e] >= K) {
-        *sh_bin = 16 * tid + e;
+        *sh_bin = BPT * tid + e;
         *sh_above = cum;
         break;
       }
@@ -292,13 +295,16 @@ __device__ uint32_t find_bin(const SelArgs& a, const uint32_t* h, uint32_t* s_wa
   return total;
 }
 
-__global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
+// CT threads (1024, 512 or 256, as the finish pass), each owning kItemChunk / CT items
+template <int CT>
+__global__ void __launch_bounds__(CT) collect_kernel(SelArgs a) {
+  constexpr int kIPT = kItemChunk / CT;
   const int set = blockIdx.y;
   const int b = set / a.n_sets;
   const Win w = window(a, b);
   if (w.all || a.top_k == 0) return;
   const int tid = threadIdx.x;
-  __shared__ uint32_t s_wave[4];
+  __shared__ uint32_t s_wave[CT / 64];
   __shared__ int sh_bin;
   __shared__ uint32_t sh_above, lqbase;
   if (tid == 0) {
@@ -314,16 +320,16 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
   const bool mine = i0 < w.hi && i0 + kIPT > w.lo;
   uint32_t k[kIPT], flags = 0, n_above = 0;
   const uint32_t* keys = a.keys + (size_t)set * a.item_cap;
-  if (mine) load16(keys, i0, k);
+  if (mine) load_keys<kIPT>(keys, i0, k);
   __syncthreads();
   // The global histogram is valid when the last call of this layout left it clean (its
   // finish pass zeroed it and wrote the marker) and it counts exactly the pool's items.
   // Otherwise (a fresh or reused workspace) every workgroup rebuilds the set's histogram
   // from the keys in LDS; the finish pass then leaves it clean for the next call.
-  const uint32_t h_total = find_bin(a, a.hist + (size_t)set * kHistBins, s_wave, &sh_bin, &sh_above);
+  const uint32_t h_total = find_bin<CT>(a, a.hist + (size_t)set * kHistBins, s_wave, &sh_bin, &sh_above);
   if (marker != a.marker_value || h_total != (uint32_t)(w.hi - w.lo)) {
     __shared__ uint32_t lhist[kHistBins];
-    for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0;
+    for (int i = tid; i < kHistBins; i += CT) lhist[i] = 0;
     if (tid == 0) {
       sh_bin = 0;
       sh_above = 0;
@@ -335,14 +341,14 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
     // flight together) and count nothing.
     constexpr int kRebuildLoads = 8;
     const int q0 = w.lo >> 2, q1 = (w.hi + 3) >> 2;
-    for (int q = q0 + tid; q < q1; q += kRebuildLoads * 256) {
+    for (int q = q0 + tid; q < q1; q += kRebuildLoads * CT) {
       uint4 x[kRebuildLoads];
 #pragma unroll
       for (int u = 0; u < kRebuildLoads; ++u)
-        x[u] = *reinterpret_cast<const uint4*>(keys + 4 * min(q + 256 * u, q1 - 1));
+        x[u] = *reinterpret_cast<const uint4*>(keys + 4 * min(q + CT * u, q1 - 1));
 #pragma unroll
       for (int u = 0; u < kRebuildLoads; ++u) {
-        const int it = 4 * (q + 256 * u);     // past the pool when the group was clamped
+        const int it = 4 * (q + CT * u);      // past the pool when the group was clamped
         const uint32_t kv[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -350,7 +356,7 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
       }
     }
     __syncthreads();
-    find_bin(a, lhist, s_wave, &sh_bin, &sh_above);
+    find_bin<CT>(a, lhist, s_wave, &sh_bin, &sh_above);
   }
   const int bin = sh_bin;
   if (blockIdx.x == 0 && tid == 0) {
@@ -369,7 +375,7 @@ __global__ void __launch_bounds__(256) collect_kernel(SelArgs a) {
   }
   // one scan of (above << 16 | candidates); both are at most kItemChunk per workgroup
   uint32_t total;
-  const uint32_t excl = block_excl_scan<256>((n_above << 16) | __builtin_popcount(flags), s_wave, total);
+  const uint32_t excl = block_excl_scan<CT>((n_above << 16) | __builtin_popcount(flags), s_wave, total);
   if (tid == 0) {
     lqbase = (total & 0xFFFFu) ? atomicAdd(&a.cand_count[set], total & 0xFFFFu) : 0u;
     a.chunk_above[(size_t)set * a.n_chunks + blockIdx.x] = total >> 16;
@@ -659,7 +665,12 @@ hipError_t select_launch(const SelPlan& p, SelArgs a, void* workspace, hipStream
   else
     hipLaunchKernelGGL((score_kernel<SCORE_LOGIT_SUM, false>), sgrid, dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(collect_kernel, dim3(p.n_chunks, NS), dim3(256), 0, stream, a);
+  if (p.fin_threads == 256)
+    hipLaunchKernelGGL(collect_kernel<256>, dim3(p.n_chunks, NS), dim3(256), 0, stream, a);
+  else if (p.fin_threads == 512)
+    hipLaunchKernelGGL(collect_kernel<512>, dim3(p.n_chunks, NS), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL(collect_kernel<1024>, dim3(p.n_chunks, NS), dim3(1024), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.fin_threads == 256)
     hipLaunchKernelGGL(finish_kernel<256>, dim3(p.n_chunks, NS), dim3(256), 0, stream, a);
