@@ -202,3 +202,26 @@ def test_physical_hand_off_full(case):
             assert np.array_equal(case.pidx[b, s, :n].astype(np.int64), want), f"b {b} set {s}"
     assert np.array_equal(case.pdout.view(np.uint32), case.dout.view(np.uint32))
     assert np.array_equal(case.pdlse.view(np.uint32), case.dlse.view(np.uint32))
+
+
+def test_select_from_partial_scores_full(case):
+    """Select from the fused per-KV-head partial scores at the full workload (the launch
+    that sums one row per KV head, several 512-position chunks per workgroup) equals the
+    CPU rule on those scores bit for bit; with per-KV-head sets it also equals the
+    selection from the logit rows."""
+    torch, lcs = require_gpu()
+    cfg = case.cfg
+    S = cfg.n_sink + cfg.top_k + cfg.n_recent
+    sc = torch.from_numpy(np.ascontiguousarray(case.scores)).cuda()
+    pl = i32_dev(case.kv.prefix_len, torch)
+    idx, cnt = lcs.select_topk_scores(sc, pl, cfg.L, cfg.mode, cfg.top_k, cfg.n_sink, cfg.n_recent, cap=S,
+                                      Hq=cfg.Hq)
+    torch.cuda.synchronize()
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    ref = osel.select(case.scores[:, :, None, :], case.kv.prefix_len, cfg.Hkv, cfg.mode, cfg.top_k, cfg.n_sink,
+                      cfg.n_recent, precision="f32")
+    for b in range(cfg.B):
+        for s, r in enumerate(ref[b]):
+            assert gc[b, s] == r.size and np.array_equal(gi[b, s, :r.size], r), f"b {b} set {s}"
+    if cfg.mode == "per_kv_head":
+        assert np.array_equal(gc, case.cnt) and np.array_equal(gi, case.idx)
