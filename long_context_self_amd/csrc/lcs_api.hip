@@ -316,8 +316,9 @@ lcs_status select_impl(const float* logits, int64_t logits_ld, int32_t n_rows, i
   }
   if (need > items) need = items;
   if (cap < need) return fail(LCS_E_SHAPE, "cap %d < %lld entries the selection can produce", cap, need);
+  const int32_t reads = (mode == LCS_SET_SHARED ? Hq : Hq / Hkv) * n_rows;   // values per position
   const lcs::SelPlan plan = lcs::select_plan(B, Hq, Hkv, (int32_t)mode, max_prefix_len, block_size,
-                                             lcs::device_cus());
+                                             lcs::device_cus(), reads);
   if (workspace == nullptr || workspace_bytes < plan.total_bytes)
     return fail(LCS_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, plan.total_bytes);
   lcs::SelArgs a{};

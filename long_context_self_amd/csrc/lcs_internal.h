@@ -175,9 +175,10 @@ struct SelPlan {
   size_t keys_bytes, hist_bytes, cc_bytes, cand_bytes, ca_bytes, thr_bytes, mk_bytes, total_bytes;
 };
 
-// cus: compute units of the device (0: the MI355X's 256); only the launch shape depends on it
+// cus: compute units of the device (0: the MI355X's 256); reads: score values read per
+// position (heads of a set x rows; 0: many).  Only the launch shape depends on either.
 SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t max_len,
-                    int32_t block_size, int32_t cus = 0);
+                    int32_t block_size, int32_t cus = 0, int32_t reads = 0);
 
 hipError_t select_launch(const SelPlan& plan, SelArgs args, void* workspace, hipStream_t stream);
 

@@ -450,6 +450,7 @@ __device__ __forceinline__ int32_t emit_id(const SelArgs& a, int b, int it) {
 constexpr int kFinLDS = 8192;      // candidates a workgroup holds in LDS
 constexpr int kMaxScoreIters = 8;  // most kScorePos chunks one score workgroup covers
 constexpr long long kScoreWGsPerCU = 4;   // score workgroups per CU to keep
+constexpr int kManyReads = 16;             // values read per position that need all four
 
 // Boundary and output of one 4096-item chunk (one workgroup per chunk and set).  Every
 // chunk's workgroup finds the exact boundary composite itself: the radix passes over
@@ -652,7 +653,7 @@ __global__ void __launch_bounds__(FT) finish_kernel(SelArgs a) {
 }  // namespace
 
 SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t max_len,
-                    int32_t block_size, int32_t cus) {
+                    int32_t block_size, int32_t cus, int32_t reads) {
   SelPlan p{};
   p.n_sets = (mode == LCS_SEL_SHARED) ? 1 : Hkv;
   const size_t NS = (size_t)B * p.n_sets;
@@ -662,13 +663,17 @@ SelPlan select_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t mode, int32_t ma
   p.item_cap = (int32_t)align_up((size_t)items, 16);
   p.n_chunks = (int32_t)((items + kItemChunk - 1) / kItemChunk);
   // score workgroups: several chunks each while that still leaves kScoreWGsPerCU
-  // workgroups per CU (fewer histogram clears and flushes)
+  // workgroups per CU (fewer histogram clears and flushes); a set whose positions read
+  // few values (partial scores, small groups) keeps half as many, each covering more
+  // chunks (measured: partial scores at 64K x 4, 28.1 -> 26.7 us; at 128K x 8, 28.2 ->
+  // 27.4 us; two logit rows of 32 heads at 128K x 8 need the four: 64.2 against 65.4)
   const long long pos_chunks = ((long long)(max_len > 0 ? max_len : 1) + kScorePos - 1) / kScorePos;
   const long long ncu = cus > 0 ? cus : kDefaultCUs;
   p.score_iters = 1;
   if (mode != LCS_SEL_BLOCK)
     while (p.score_iters < kMaxScoreIters &&
-           pos_chunks * (long long)NS / (2 * p.score_iters) >= kScoreWGsPerCU * ncu)
+           pos_chunks * (long long)NS / (2 * p.score_iters) >=
+               (reads > 0 && reads < kManyReads ? kScoreWGsPerCU / 2 : kScoreWGsPerCU) * ncu)
       p.score_iters *= 2;
   p.n_pos_chunks = (int32_t)((pos_chunks + p.score_iters - 1) / p.score_iters);
   {
