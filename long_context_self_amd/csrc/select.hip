@@ -86,6 +86,14 @@ __device__ __forceinline__ Win window(const SelArgs& a, int b) {
   return w;
 }
 
+// A value that no kernel of the call writes while this one runs, read through the
+// constant address space: a scalar load (one per wave, through the scalar cache) where a
+// global read of one address by every thread would send every wave's request to it.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // Block-wide exclusive prefix sum over NT threads (NT a multiple of 64).
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
@@ -526,9 +534,9 @@ __global__ void __launch_bounds__(FT) finish_kernel(SelArgs a) {
       const int e = tid + u * kFinThreads;
       spec[u] = (e < a.item_cap) ? gcand[e] : 0ull;
     }
-    thr_bin = a.thr[(size_t)set * 2 + 0];
-    thr_above = a.thr[(size_t)set * 2 + 1];
-    n_cand = (int)a.cand_count[set];
+    thr_bin = ld_uniform(a.thr + (size_t)set * 2 + 0);
+    thr_above = ld_uniform(a.thr + (size_t)set * 2 + 1);
+    n_cand = (int)ld_uniform(a.cand_count + set);
     if (tid < (int)blockIdx.x) part = cabove[tid];
     for (int c = tid + kFinThreads; c < (int)blockIdx.x; c += kFinThreads) part += cabove[c];
   }
