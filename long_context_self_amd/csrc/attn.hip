@@ -498,17 +498,13 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int pid, int r, int
     lv[u] = mcol[o + kMaxRowsPerWG];
     if (sp >= ns) { mv[u] = -INFINITY; lv[u] = 0.f; }
   }
-  float M = fmaxf(mv[0], mv[1]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float M = wave_max_f32(fmaxf(mv[0], mv[1]));
   const float Ms = (M == -INFINITY) ? 0.f : M;
   float wv[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) wv[u] = __builtin_amdgcn_exp2f(mv[u] - Ms);
   // butterfly sum: every lane ends with the same, run-to-run fixed value
-  float Ls = wv[0] * lv[0] + wv[1] * lv[1];
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off);
+  const float Ls = wave_sum_f32(wv[0] * lv[0] + wv[1] * lv[1]);
   float acc[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
@@ -583,10 +579,7 @@ __device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int pid, int r,
   float M[3], Ls[3], wv[2];
 #pragma unroll
   for (int br = 0; br < 3; ++br) {
-    float x = fmaxf(bv[0] == br ? mv[0] : -INFINITY, bv[1] == br ? mv[1] : -INFINITY);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    M[br] = x;
+    M[br] = wave_max_f32(fmaxf(bv[0] == br ? mv[0] : -INFINITY, bv[1] == br ? mv[1] : -INFINITY));
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -596,10 +589,7 @@ __device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int pid, int r,
 #pragma unroll
   for (int br = 0; br < 3; ++br) {
     // butterfly sum: every lane ends with the same, run-to-run fixed value
-    float x = (bv[0] == br ? wv[0] * lv[0] : 0.f) + (bv[1] == br ? wv[1] * lv[1] : 0.f);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    Ls[br] = x;
+    Ls[br] = wave_sum_f32((bv[0] == br ? wv[0] * lv[0] : 0.f) + (bv[1] == br ? wv[1] * lv[1] : 0.f));
   }
   float acc[3][CPL];
 #pragma unroll
@@ -928,8 +918,7 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
       smask |= 1u << (cslot[qt] * a.G + hh);
       if (a.cdup) smask |= 1u << ((cslot[qt] + 1) * a.G + hh);
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) smask |= __shfl_xor(smask, off);
+    smask = wave_or_u32(smask);
     auto stage_logits = [&](int st) {
       if (st > st_last) return;
       const int col = (st - st_first) * kStepTokens + 4 * j;
@@ -1128,10 +1117,7 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
 
   // full row sums (fixed order)
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    l[qt] += __shfl_xor(l[qt], 16);
-    l[qt] += __shfl_xor(l[qt], 32);
-  }
+  for (int qt = 0; qt < QT; ++qt) l[qt] = sum_x16_x32(l[qt]);
 
   // ---- merge the 4 waves' states through LDS.  Every wave publishes (m, l, O); then
   //      wave w merges dims {8i + 2w, 8i + 2w + 1} of every row, in wave order 0..3.
@@ -1250,18 +1236,13 @@ __global__ void __launch_bounds__(256) block_union_kernel(AttnArgs a) {
     }
     __syncthreads();
     // ascending compaction: thread t owns ids [16t, 16t + 16) of the chunk; an exclusive
-    // scan of the per-thread counts (wave shuffles, then the four wave totals)
+    // scan of the per-thread counts (wave scan, then the four wave totals)
     uint32_t c = 0;
     for (int e = 0; e < 16; ++e) {
       const int id = 16 * tid + e;
       c += (id < span) && ((mlo[id] | mhi[id]) != 0);
     }
-    uint32_t x = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_incl_scan(c);
     if (lane == 63) wsum[w] = x;
     __syncthreads();
     uint32_t pre = 0, chunk_total = 0;

@@ -184,4 +184,71 @@ hipError_t select_launch(const SelPlan& plan, SelArgs args, void* workspace, hip
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// ---------------------------------------------------------------------------
+// Wave primitives (64 lanes, every lane active).  None goes through LDS: a shuffle
+// through LDS waits for the LDS return at each of its steps.
+// ---------------------------------------------------------------------------
+// Inclusive prefix sum.  Within each 16-lane row, four DPP row shifts (a lane whose
+// source lies before its row's start adds 0); then each row adds the totals of the rows
+// below it, read with readlane.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  x += (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+  return (uint32_t)x;
+}
+
+// Butterfly all-reduce over lane xor 32, 16, 8, 4, 2, 1, in that order.  The gfx950
+// half and row swaps (v_permlane32_swap, v_permlane16_swap) return both members of the
+// lane xor 32 (xor 16) pair, so op(first, second) combines a lane with its partner.
+// Each step combines the same pair of values as the xor-shuffle butterfly, so with a
+// commutative op every lane ends with the same value, bit for bit the shuffle
+// butterfly's.  Lane
+// xor 8 is row_ror:8 (rotating a 16-lane row by 8); lane xor 4 is row_ror:4 once lanes
+// r and r ^ 8 hold the same value, which the xor-8 step leaves; xor 2 and xor 1 are
+// quad permutations.
+template <typename Op>
+__device__ __forceinline__ float wave_bfly_f32(float v, Op op) {
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));
+  v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));
+  v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false)));
+  v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false)));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  return wave_bfly_f32(v, [](float a, float b) { return a + b; });
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  return wave_bfly_f32(v, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
+  const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = s32[0] | s32[1];
+  const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = s16[0] | s16[1];
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false);
+  return v;
+}
+// lane + lane ^ 16, then + lane ^ 32 (the xor-shuffle pair sums in that order)
+__device__ __forceinline__ float sum_x16_x32(float v) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
 }  // namespace lcs

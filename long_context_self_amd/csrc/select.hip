@@ -94,24 +94,6 @@ __device__ __forceinline__ T ld_uniform(const T* p) {
   return *(const __attribute__((address_space(4))) T*)p;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave (every lane active).  Within each
-// 16-lane row, four DPP row shifts (a lane whose source lies before its row's start adds
-// 0); then each row adds the totals of the rows below it, read with readlane.  No LDS
-// round trip: a shuffle through LDS waits on the LDS return at each of its six steps.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  int x = (int)v;
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
-  const int r0 = __builtin_amdgcn_readlane(x, 15);
-  const int r1 = __builtin_amdgcn_readlane(x, 31);
-  const int r2 = __builtin_amdgcn_readlane(x, 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  x += (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
-  return (uint32_t)x;
-}
-
 // Block-wide exclusive prefix sum over NT threads (NT a multiple of 64).
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
