@@ -415,14 +415,14 @@ __global__ void __launch_bounds__(CT) collect_kernel(SelArgs a) {
     a.thr[(size_t)set * 2 + 0] = (uint64_t)bin;
     a.thr[(size_t)set * 2 + 1] = (uint64_t)sh_above;
   }
-  // count the items above the bin, flag the bin's
+  // count the items above the bin, flag the bin's (branch-free, as in the finish pass)
   if (mine) {
 #pragma unroll
     for (int e = 0; e < kIPT; ++e) {
-      if (i0 + e < w.lo || i0 + e >= w.hi) continue;
-      const int dg = (int)(k[e] >> 20);
-      n_above += dg > bin;
-      if (dg == bin) flags |= 1u << e;
+      const bool in = (i0 + e >= w.lo) & (i0 + e < w.hi);
+      const uint32_t dg = k[e] >> 20;
+      n_above += (uint32_t)(in & (dg > (uint32_t)bin));
+      flags |= (uint32_t)(in & (dg == (uint32_t)bin)) << e;
     }
   }
   // one scan of (above << 16 | candidates); both are at most kItemChunk per workgroup
@@ -436,11 +436,11 @@ __global__ void __launch_bounds__(CT) collect_kernel(SelArgs a) {
   uint64_t* cand = a.cand + (size_t)set * a.item_cap;
   uint32_t pos = lqbase + (excl & 0xFFFFu);
 #pragma unroll
-  for (int e = 0; e < kIPT; ++e)
-    if (flags & (1u << e)) {
-      if (pos < (uint32_t)a.item_cap) cand[pos] = composite(k[e], i0 + e);
-      ++pos;
-    }
+  for (int e = 0; e < kIPT; ++e) {
+    const uint32_t f = (flags >> e) & 1u;
+    if (f && pos < (uint32_t)a.item_cap) cand[pos] = composite(k[e], i0 + e);
+    pos += f;
+  }
 }
 
 // The id written for item it of sequence b: the position, or its physical slot.
@@ -621,34 +621,36 @@ __global__ void __launch_bounds__(FT) finish_kernel(SelArgs a) {
     block_excl_scan<kFinThreads>(part, s_wave, before);
     base += before;
   }
+  // Both loops below are branch-free up to the store: this code runs once per workgroup,
+  // and every taken branch of a one-shot path costs an instruction fetch.
   uint32_t flags = 0, cnt = 0;
   if (K > 0) {
 #pragma unroll
     for (int e = 0; e < kFinIPT; ++e) {
       const int it = t0 + e;
-      if (it < w.lo || it >= w.hi) continue;
-      const int dg = (int)(kk[e] >> 20);
-      if (dg > bin || (dg == bin && composite(kk[e], it) >= cstar)) {
-        flags |= 1u << e;
-        ++cnt;
-      }
+      const uint32_t dg = kk[e] >> 20;
+      // kept: in the pool, and above the boundary composite
+      const bool keep = (it >= w.lo) & (it < w.hi) &
+                        ((dg > (uint32_t)bin) | ((dg == (uint32_t)bin) & (composite(kk[e], it) >= cstar)));
+      flags |= (uint32_t)keep << e;
+      cnt += (uint32_t)keep;
     }
   }
   uint32_t total;
   uint32_t pos = base + block_excl_scan<kFinThreads>(cnt, s_wave, total);
+  // output slot of each item (-1: none): a sink item keeps its position, a recent item
+  // follows the K kept pool items, and kept pool items take consecutive slots
+  const int rbase = w.lo + K - w.hi;
 #pragma unroll
   for (int e = 0; e < kFinIPT; ++e) {
     const int it = t0 + e;
-    if (it >= w.n) continue;
-    if (it < w.lo) {
-      if (it < a.cap) out[it] = emit_id(a, b, it);
-    } else if (it >= w.hi) {
-      const int o = w.lo + K + (it - w.hi);
-      if (o < a.cap) out[o] = emit_id(a, b, it);
-    } else if (flags & (1u << e)) {
-      if ((int)pos < a.cap) out[pos] = emit_id(a, b, it);
-      ++pos;
-    }
+    const uint32_t kept = (flags >> e) & 1u;
+    int o = kept ? (int)pos : -1;
+    o = (it < w.lo) ? it : o;
+    o = (it >= w.hi) ? rbase + it : o;
+    o = (it < w.n) ? o : -1;
+    pos += kept;
+    if (o >= 0 && o < a.cap) out[o] = emit_id(a, b, it);
   }
   if (blockIdx.x == 0 && tid == 0) a.counts[set] = min(w.lo + K + (w.n - w.hi), a.cap);
 }
