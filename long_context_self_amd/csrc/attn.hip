@@ -454,10 +454,11 @@ __device__ __forceinline__ void dma_piece(const uint16_t* kb, const uint16_t* vb
 }
 
 // Merge split-K partials in split order.  One wave per q-row.  Lane s loads the
-// (m, l) of split s while every lane also loads its columns of the first kChunk
-// splits; later chunks are loaded one chunk ahead of their use, so the common case
-// (n_split <= kChunk) costs one memory round trip.  Split weights reach the column
-// loop through readlane.
+// (m, l) of split s while every lane also loads its columns of the first KC splits
+// (KC = 8, 16 or 32: the least that covers n_split, so that a call with few splits
+// issues few column loads); later chunks are loaded one chunk ahead of their use, so
+// the common case (n_split <= 32) costs one memory round trip.  Split weights reach
+// the column loop through readlane.
 // q-rows (one wave each) per combine workgroup: few rows per workgroup spread a call's
 // rows over more CUs, which shortens the launch's one round trip (measured: a draft
 // step's combine 0.75 us faster with one row than with four, verify's 0.6 us with two)
@@ -471,7 +472,7 @@ __device__ __forceinline__ float lane_f(float v, int l) {
 
 // Merge the split-K partials of q-row r of pair pid (= (b*Hkv + g)*n_rc + rc) in split
 // order and write its output row and lse.  One wave.
-template <int D>
+template <int D, int KC>
 __device__ __forceinline__ void merge_row(const AttnArgs& a, int pid, int r, int lane) {
   const int rc = pid % a.n_rc;
   const int bg = pid / a.n_rc;
@@ -484,9 +485,9 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int pid, int r, int
   const float* mcol = base + (size_t)kMaxRowsPerWG * D + r;
   constexpr int CPL = D / 64;                   // columns per lane (2 or 1)
   const float* ocol = base + (size_t)r * D + CPL * lane;
-  float cur[kChunk][CPL], nxt[kChunk][CPL];
+  float cur[KC][CPL], nxt[KC][CPL];
 #pragma unroll
-  for (int u = 0; u < kChunk; ++u)
+  for (int u = 0; u < KC; ++u)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) cur[u][c] = ocol[(size_t)min(u, ns - 1) * pstride + c];
   float mv[2], lv[2];
@@ -508,16 +509,16 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int pid, int r, int
   float acc[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-  for (int c0 = 0; c0 < ns; c0 += kChunk) {
-    const bool more = c0 + kChunk < ns;
+  for (int c0 = 0; c0 < ns; c0 += KC) {
+    const bool more = c0 + KC < ns;
     if (more) {
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u)
+      for (int u = 0; u < KC; ++u)
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) nxt[u][c] = ocol[(size_t)min(c0 + kChunk + u, ns - 1) * pstride + c];
+        for (int c = 0; c < CPL; ++c) nxt[u][c] = ocol[(size_t)min(c0 + KC + u, ns - 1) * pstride + c];
     }
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
+    for (int u = 0; u < KC; ++u) {
       const int sp = c0 + u;
       const float w = (sp < ns) ? lane_f(sp < 64 ? wv[0] : wv[1], sp & 63) : 0.f;
 #pragma unroll
@@ -525,7 +526,7 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int pid, int r, int
     }
     if (more) {
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u)
+      for (int u = 0; u < KC; ++u)
 #pragma unroll
         for (int c = 0; c < CPL; ++c) cur[u][c] = nxt[u][c];
     }
@@ -653,7 +654,9 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   const int r = blockIdx.y * combine_rows<MODE>() + (threadIdx.x >> 6);
   if (r >= nrows) return;
   if constexpr (MODE == MODE_NSA) merge_row_nsa<D>(a, pid, r, threadIdx.x & 63);
-  else merge_row<D>(a, pid, r, threadIdx.x & 63);
+  else if (a.n_split <= 8) merge_row<D, 8>(a, pid, r, threadIdx.x & 63);
+  else if (a.n_split <= 16) merge_row<D, 16>(a, pid, r, threadIdx.x & 63);
+  else merge_row<D, kChunk>(a, pid, r, threadIdx.x & 63);
 }
 
 // SC: dense verify that writes per-KV-head partial scores of the two collected rows
