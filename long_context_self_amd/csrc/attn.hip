@@ -546,9 +546,9 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int pid, int r, int
 // branch output; lse [B][n_q][Hq][3] holds each branch's log-sum-exp (-inf for a branch
 // that saw nothing).  The launch's splits are the compression, selection and window
 // branches' in that order.  One pass: lane s loads the (m, l) of split s and every lane
-// its columns of all splits (the first kChunk at once), as in merge_row, and each split
+// its columns of all splits (the first KC at once), as in merge_row, and each split
 // adds into its own branch's accumulator.
-template <int D>
+template <int D, int KC>
 __device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int pid, int r, int lane) {
   constexpr int CPL = D / 64;
   const int rc = pid % a.n_rc;
@@ -561,9 +561,9 @@ __device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int pid, int r,
   const float* base = a.part + (size_t)pid * ns * pstride;
   const float* mcol = base + (size_t)kMaxRowsPerWG * D + r;
   const float* ocol = base + (size_t)r * D + CPL * lane;
-  float cur[kChunk][CPL], nxt[kChunk][CPL];
+  float cur[KC][CPL], nxt[KC][CPL];
 #pragma unroll
-  for (int u = 0; u < kChunk; ++u)
+  for (int u = 0; u < KC; ++u)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) cur[u][c] = ocol[(size_t)min(u, ns - 1) * pstride + c];
   float mv[2], lv[2];
@@ -597,16 +597,16 @@ __device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int pid, int r,
   for (int br = 0; br < 3; ++br)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[br][c] = 0.f;
-  for (int c0 = 0; c0 < ns; c0 += kChunk) {
-    const bool more = c0 + kChunk < ns;
+  for (int c0 = 0; c0 < ns; c0 += KC) {
+    const bool more = c0 + KC < ns;
     if (more) {
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u)
+      for (int u = 0; u < KC; ++u)
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) nxt[u][c] = ocol[(size_t)min(c0 + kChunk + u, ns - 1) * pstride + c];
+        for (int c = 0; c < CPL; ++c) nxt[u][c] = ocol[(size_t)min(c0 + KC + u, ns - 1) * pstride + c];
     }
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
+    for (int u = 0; u < KC; ++u) {
       const int sp = c0 + u;
       if (sp >= ns) break;
       const float w = lane_f(sp < 64 ? wv[0] : wv[1], sp & 63);
@@ -620,7 +620,7 @@ __device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int pid, int r,
     }
     if (more) {
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u)
+      for (int u = 0; u < KC; ++u)
 #pragma unroll
         for (int c = 0; c < CPL; ++c) cur[u][c] = nxt[u][c];
     }
@@ -653,8 +653,11 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
   const int nrows = min(kMaxRowsPerWG, a.rows - rc * kMaxRowsPerWG);
   const int r = blockIdx.y * combine_rows<MODE>() + (threadIdx.x >> 6);
   if (r >= nrows) return;
-  if constexpr (MODE == MODE_NSA) merge_row_nsa<D>(a, pid, r, threadIdx.x & 63);
-  else if (a.n_split <= 8) merge_row<D, 8>(a, pid, r, threadIdx.x & 63);
+  if constexpr (MODE == MODE_NSA) {
+    if (a.n_split <= 8) merge_row_nsa<D, 8>(a, pid, r, threadIdx.x & 63);
+    else if (a.n_split <= 16) merge_row_nsa<D, 16>(a, pid, r, threadIdx.x & 63);
+    else merge_row_nsa<D, kChunk>(a, pid, r, threadIdx.x & 63);
+  } else if (a.n_split <= 8) merge_row<D, 8>(a, pid, r, threadIdx.x & 63);
   else if (a.n_split <= 16) merge_row<D, 16>(a, pid, r, threadIdx.x & 63);
   else merge_row<D, kChunk>(a, pid, r, threadIdx.x & 63);
 }
