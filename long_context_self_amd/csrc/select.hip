@@ -309,9 +309,16 @@ __global__ void __launch_bounds__(256) score_kernel(SelArgs a) {
     }
     __syncthreads();
   }
+  // flush: every bin count of this thread is read from LDS first (one round trip), then
+  // the non-empty ones go out as atomics (a loop of read, wait, atomic waits 16 times)
   uint32_t* gh = a.hist + (size_t)set * kHistBins;
-  for (int i = tid; i < kHistBins; i += 256)
-    if (lh[i]) atomicAdd(&gh[i], lh[i]);
+  constexpr int kFlush = kHistBins / 256;
+  uint32_t hv[kFlush];
+#pragma unroll
+  for (int k = 0; k < kFlush; ++k) hv[k] = lh[tid + 256 * k];
+#pragma unroll
+  for (int k = 0; k < kFlush; ++k)
+    if (hv[k]) atomicAdd(&gh[tid + 256 * k], hv[k]);
 }
 
 // Threshold bin of a set from its histogram: the bin holding the k-th largest item.
