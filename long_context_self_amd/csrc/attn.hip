@@ -1129,13 +1129,14 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
   //      wave w merges dims {8i + 2w, 8i + 2w + 1} of every row, in wave order 0..3.
   __syncthreads();   // every wave is done with Q, its metadata and its ring
   {
+    // O tile e of a lane as one 16-byte store: floats [(qt * kPer + 4 e) * 64, + 256) hold
+    // the tile's four values of every lane, lane-major
     float* w = s_merge + (size_t)wave * QT * kPer * 64;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[(qt * kPer + e * 4 + i) * 64 + lane] = O[qt][e][i];
+        *reinterpret_cast<f32x4*>(w + (qt * kPer + e * 4) * 64 + 4 * lane) = O[qt][e];
       w[(qt * kPer + 32) * 64 + lane] = m[qt];
       w[(qt * kPer + 33) * 64 + lane] = l[qt];
     }
@@ -1161,9 +1162,11 @@ __global__ void __launch_bounds__(256, 1) attn_kernel(AttnArgs a) {
       const float sc = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Ms);
       L += sc * w[(qt * kPer + 33) * 64 + lane];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(w + (qt * kPer + (e0 + h) * 4) * 64 + 4 * lane);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) oo[qt][h][i] += sc * w[(qt * kPer + (e0 + h) * 4 + i) * 64 + lane];
+        for (int i = 0; i < 4; ++i) oo[qt][h][i] += sc * t[i];
+      }
     }
     mo[qt] = M;
     lo_[qt] = L;
