@@ -1,5 +1,8 @@
 """Full-size parity at the 64K (per-KV-head, B=4, 40/8 heads) and 128K (B=8) workloads,
-in the launch configurations the benchmark and the loop driver use.
+in the launch configurations the benchmark and the loop driver use, and for one 100K
+sequence of the 8B-shaped layer with a 20K-entry set: there verify splits each KV head
+96 ways, so the split-K merge loads its partials in three chunks, and the draft step
+merges 32 splits.
 
 The oracle cannot evaluate these calls whole, so it checks sampled outputs one by one:
 for a sampled (sequence, row, head) it gathers the visible K/V rows itself and runs
@@ -26,10 +29,14 @@ class Case:
     pass
 
 
+# a single long sequence: more verify splits than one chunk of the merge's loads holds
+LONG_SINGLE = synth.CONFIGS["llama8b_32k"].with_(name="llama8b_100k_b1", L=100000, top_k=20000)
+
+
 def build(name):
     torch, lcs = require_gpu()
     c = Case()
-    c.cfg = synth.CONFIGS[name]
+    c.cfg = LONG_SINGLE if name == LONG_SINGLE.name else synth.CONFIGS[name]
     c.kv = synth.make_paged_kv(c.cfg, seed=0)
     c.q = synth.make_queries(c.cfg, c.kv, c.cfg.n_q, seed=0)
     c.qd = synth.make_queries(c.cfg, c.kv, 1, seed=0, tag=100)
@@ -77,7 +84,7 @@ def build(name):
     return c
 
 
-@pytest.fixture(scope="module", params=["qwen14b_64k", "stress_128k"])
+@pytest.fixture(scope="module", params=["qwen14b_64k", "stress_128k", LONG_SINGLE.name])
 def case(request):
     return build(request.param)
 
