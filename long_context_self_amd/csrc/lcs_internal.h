@@ -208,12 +208,12 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 // Butterfly all-reduce over lane xor 32, 16, 8, 4, 2, 1, in that order.  The gfx950
 // half and row swaps (v_permlane32_swap, v_permlane16_swap) return both members of the
 // lane xor 32 (xor 16) pair, so op(first, second) combines a lane with its partner.
-// Each step combines the same pair of values as the xor-shuffle butterfly, so with a
-// commutative op every lane ends with the same value, bit for bit the shuffle
-// butterfly's.  Lane
-// xor 8 is row_ror:8 (rotating a 16-lane row by 8); lane xor 4 is row_ror:4 once lanes
-// r and r ^ 8 hold the same value, which the xor-8 step leaves; xor 2 and xor 1 are
-// quad permutations.
+// Lane xor 8 is row_ror:8 (rotating a 16-lane row by 8); lane xor 4 is row_ror:4 once
+// lanes r and r ^ 8 hold the same value, which the xor-8 step leaves; xor 2 and xor 1
+// are quad permutations.  Each step combines the same pair of values as the
+// xor-shuffle butterfly, so with an op that gives one result for either operand order
+// (a sum; a max, up to the sign of a zero) every lane ends with the same value, bit for
+// bit the shuffle butterfly's.
 template <typename Op>
 __device__ __forceinline__ float wave_bfly_f32(float v, Op op) {
   const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
